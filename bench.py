@@ -1,0 +1,353 @@
+"""Quest sparse-decode benchmark on one MI355X.
+
+Workload (default "bench128k"): one Qwen3-30B-A3B-class attention layer
+(32 q / 4 KV heads, head_dim 128, bf16), batch 8, 128000-token contexts in a
+paged cache (page 16), token budget 4096 (256 pages per KV head).  A step is
+the whole hot path for one new token per request: quest_append_kv (KV store +
+fused min/max refresh), quest_page_scores, quest_topk_pages and
+quest_sparse_decode (split-K attention + merge).  Inputs are seeded synthetic
+tensors already resident in HBM.
+
+Timing: W warm-up steps, then K timed steps.  Before each timed step an
+untimed write of a 2 GiB scratch buffer evicts the 256 MB Infinity Cache, so
+the metadata and KV are read from HBM as they would be between layers; HIP
+events on the library's stream bracket each step and each kernel.  value =
+batch * K / (sum of step times).  A warm number (back-to-back steps, no
+eviction) is reported separately and labelled as cache-assisted.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from kv_cache_decode_quest_amd import quest, workloads  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "sparse decode tokens/s + achieved HBM GB/s (% peak), batch 8 x 128k ctx"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+class BenchLayer:
+    """The layer's caller-owned buffers (the cache-manager role)."""
+
+    def __init__(self, w: workloads.Workload, capacity: int, device):
+        self.w, self.device = w, device
+        self.lay = workloads.make_layout(w, device, capacity)
+        self.L = quest.make_layout(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                   w.torch_dtype, self.lay.num_pool_pages, self.lay.max_pages)
+        self.k_cache, self.v_cache = workloads.empty_pool(w, self.lay, device)
+        self.kmeta = torch.zeros((self.lay.num_pool_pages, w.num_kv_heads, 2, w.head_dim),
+                                 dtype=w.torch_dtype, device=device)
+        self.pt = self.lay.page_table
+        self.ctx0 = self.lay.ctx0.clone()
+        k_new, v_new, cu, ctx_before = workloads.prefill_tokens(w, self.lay, device)
+        self.prefill = (k_new, v_new, cu)
+        quest.quest_append_kv(self.L, k_new, v_new, cu, ctx_before, int(self.ctx0.max()),
+                              self.pt, self.k_cache, self.v_cache, self.kmeta)
+        self.cu1 = torch.arange(w.batch + 1, dtype=torch.int32, device=device)
+
+
+def make_steps(w, n, device):
+    """Per-step inputs and the context arrays of each step (no host sync in
+    the timed loop)."""
+    steps = []
+    for s in range(n):
+        q, k_new, v_new = workloads.step_tokens(w, device, 0, s)
+        steps.append((q, k_new, v_new))
+    return steps
+
+
+def run_step(layer, bufs, s, inp, ctx_before, ctx_after, budgets, sm, events=None):
+    q, k_new, v_new = inp
+    L = layer.L
+    if events:
+        events[0].record()
+    quest.quest_append_kv(L, k_new, v_new, layer.cu1, ctx_before, 1, layer.pt, layer.k_cache,
+                          layer.v_cache, layer.kmeta)
+    if events:
+        events[1].record()
+    quest.quest_page_scores(L, q, layer.kmeta, layer.pt, ctx_after, bufs.scores)
+    if events:
+        events[2].record()
+    quest.quest_topk_pages(L, bufs.scores, ctx_after, budgets, bufs.max_k, bufs.sel_pages,
+                           bufs.num_sel)
+    if events:
+        events[3].record()
+    quest.quest_sparse_decode(L, q, layer.k_cache, layer.v_cache, layer.pt, ctx_after,
+                              bufs.sel_pages, bufs.num_sel, bufs.max_k, sm, bufs.out,
+                              bufs.workspace)
+    if events:
+        events[4].record()
+
+
+def step_bytes(w, ctx_after, sel, nsel):
+    """Algorithmic HBM bytes of one step: every live page's metadata row plus
+    the valid tokens of every selected page (K and V)."""
+    P, D, Hkv = w.page_size, w.head_dim, w.num_kv_heads
+    es = 2 if w.dtype == "bf16" else 4
+    ctx = ctx_after.cpu().to(torch.int64)
+    n = (ctx + P - 1) // P
+    meta = int(n.sum()) * Hkv * 2 * D * es
+    sel = sel.cpu().to(torch.int64)                         # [B][Hkv][max_k]
+    live = torch.arange(sel.shape[-1])[None, None, :] < nsel.cpu()[:, :, None]
+    valid = torch.clamp(ctx[:, None, None] - sel * P, min=0, max=P)
+    kv_tokens = int((valid * live).sum())
+    return meta, kv_tokens * 2 * D * es
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+SCORE_SOURCES = ["kv_cache_decode_quest_amd/csrc/page_scores.hip",
+                 "kv_cache_decode_quest_amd/csrc/quest_device.h"]
+
+
+def measured_traffic(kernel_bytes_per_launch):
+    """HBM traffic of the scoring kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "page_scores_bench128k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != source_hash(SCORE_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, layer_inputs, steps_inputs, n_req, n_steps):
+    """The fp64 oracle doing the same per-request decode work on the host."""
+    import numpy as np
+    import oracle
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+            else t.numpy()
+
+    lay, k_new, v_new, cu = layer_inputs
+    s = oracle.Shape(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                     lay.num_pool_pages, oracle.BF16 if w.dtype == "bf16" else oracle.F32)
+    kh, vh = workloads.empty_pool(w, lay, "cpu")
+    kh, vh = host(kh).copy(), host(vh).copy()
+    pt = lay.page_table.cpu().numpy()
+    cuh = cu.cpu().numpy()
+    kn, vn = host(k_new), host(v_new)
+    ctx0 = lay.ctx0.cpu().numpy()
+    log(f"cpu baseline: storing the prompt KV of {n_req} requests in the oracle's pool")
+    bounds = {}
+    for r in range(n_req):
+        a, b = int(cuh[r]), int(cuh[r + 1])
+        oracle.store_tokens(s, np.ascontiguousarray(kn[a:b]), np.ascontiguousarray(vn[a:b]), 0,
+                            pt[r], kh, vh)
+        bounds[r] = oracle.request_bounds(s, kh, pt[r], int(ctx0[r]))
+    sm = workloads.default_sm_scale(w)
+    log("cpu baseline: timing")
+    t0 = time.perf_counter()
+    done = 0
+    for st in range(n_steps):
+        q, kn1, vn1 = (host(x) for x in steps_inputs[st])
+        for r in range(n_req):
+            pos = int(ctx0[r]) + st
+            oracle.store_tokens(s, np.ascontiguousarray(kn1[r:r + 1]),
+                                np.ascontiguousarray(vn1[r:r + 1]), pos, pt[r], kh, vh)
+            ctx = pos + 1
+            j = pos // w.page_size
+            if j == bounds[r].shape[0]:
+                bounds[r] = np.concatenate([bounds[r], bounds[r][:1]], axis=0)
+            bounds[r][j] = oracle.page_bounds(s, kh, pt[r], ctx, j)
+            budget = int(workloads.budget_tokens(w, torch.tensor([ctx], dtype=torch.int32))[0])
+            oracle.decode_request(s, np.ascontiguousarray(q[r]), kh, vh, pt[r], ctx, budget, sm,
+                                  bounds=np.ascontiguousarray(bounds[r]))
+            done += 1
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_steps} decode steps x {n_req} of {w.batch} requests of the same "
+                      f"workload (store, page-bounds refresh, scores, top-k, attention per "
+                      f"request-step), fp64, single thread; {dt:.1f} s on {cpu}",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="bench128k", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--flush-mib", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--no-warm", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the Quest decode path here is built and timed "
+              "on a single MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    dev = torch.device("cuda:0")
+    quest.load()
+    w = workloads.WORKLOADS[args.workload]
+    if w.layers != 1:
+        print("bench.py times single-layer workloads", file=sys.stderr)
+        sys.exit(2)
+    K, W = args.steps, args.warmup
+    cap = max(K, W, 1)
+    log(f"workload {w.name}: batch {w.batch}, ctx {workloads.context_lengths(w).tolist()[:4]}..,"
+        f" building the cache")
+    layer = BenchLayer(w, cap, dev)
+    torch.cuda.synchronize()
+    log("cache built; drawing step inputs")
+    inputs = make_steps(w, max(K, W), dev)
+    ctx_b = [(layer.ctx0 + s).to(torch.int32) for s in range(cap)]
+    ctx_a = [(layer.ctx0 + s + 1).to(torch.int32) for s in range(cap)]
+    budgets = [workloads.budget_tokens(w, c).to(dev) for c in ctx_a]
+    max_k = max(1, max(int((b // w.page_size).max()) for b in budgets))
+    bufs = quest.alloc_decode_buffers(layer.L, w.batch, max_k, dev)
+    sm = workloads.default_sm_scale(w)
+    plan = quest.quest_sparse_decode_plan(layer.L, w.batch, max_k)
+    flush = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+
+    # snapshot the metadata rows the warm-up touches, restore them afterwards
+    P = w.page_size
+    touched = []
+    for r in range(w.batch):
+        c0 = int(layer.ctx0[r])
+        for j in range(c0 // P, (c0 + cap - 1) // P + 1):
+            touched.append(int(layer.pt[r, j]))
+    touched = torch.tensor(sorted(set(touched)), dtype=torch.int64, device=dev)
+    saved = layer.kmeta[touched].clone()
+
+    log(f"warm-up: {W} steps")
+    for s in range(W):
+        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+    torch.cuda.synchronize()
+    layer.kmeta[touched] = saved
+    torch.cuda.synchronize()
+
+    log(f"timed: {K} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    sels = torch.empty((K,) + tuple(bufs.sel_pages.shape), dtype=torch.int32, device=dev)
+    nsels = torch.empty((K,) + tuple(bufs.num_sel.shape), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(K):
+        flush.fill_(float(s))
+        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm, events[s])
+        sels[s].copy_(bufs.sel_pages)
+        nsels[s].copy_(bufs.num_sel)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_ms = [e[0].elapsed_time(e[4]) for e in events]
+    phase_ms = {name: [e[i].elapsed_time(e[i + 1]) for e in events]
+                for i, name in enumerate(["append", "scores", "topk", "decode"])}
+    total_s = sum(step_ms) / 1e3
+    value = w.batch * K / total_s
+
+    meta_b, kv_b = 0, 0
+    for s in range(K):
+        m, kv = step_bytes(w, ctx_a[s], sels[s], nsels[s])
+        meta_b += m
+        kv_b += kv
+    gbps = (meta_b + kv_b) / total_s / 1e9
+    score_us = sum(phase_ms["scores"]) / K * 1e3
+    score_bytes = meta_b / K
+    score_gbps = score_bytes / (score_us * 1e-6) / 1e9
+    decode_us = sum(phase_ms["decode"]) / K * 1e3
+    decode_gbps = (kv_b / K) / (decode_us * 1e-6) / 1e9
+    traffic = measured_traffic(score_bytes)
+
+    warm = None
+    if not args.no_warm:
+        # restore the metadata of the pages the timed steps touched, then run
+        # the same steps back to back without evicting the cache
+        layer.kmeta[touched] = saved
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for s in range(K):
+            run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+        ev[1].record()
+        torch.cuda.synchronize()
+        warm_s = ev[0].elapsed_time(ev[1]) / 1e3
+        warm = {"tokens_per_s": w.batch * K / warm_s, "ms_per_step": warm_s / K * 1e3,
+                "note": "back-to-back steps without cache eviction: part of the metadata "
+                        "is served from the Infinity Cache"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, (layer.lay,) + layer.prefill, inputs,
+                           min(args.cpu_requests, w.batch), min(args.cpu_steps, K))
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": sum(step_ms) / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch,
+                   "ctx": workloads.context_lengths(w).tolist()[0] if w.ctx_range is None
+                   else list(w.ctx_range),
+                   "page_size": w.page_size, "budget_tokens": w.budget_tokens,
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "decode_steps": K, "layers": 1},
+        "hbm_gbps": gbps,
+        "hbm_frac_peak": gbps / PEAK_HBM_GBPS,
+        "bytes_per_step": {"metadata": meta_b / K, "selected_kv": kv_b / K},
+        "roofline": {"kernel": "page_scores_mfma_kernel<128>", "bound": "hbm",
+                     "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": score_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": score_bytes,
+                     "avg_launch_us": score_us},
+        "kernels_us": {k: sum(v) / K * 1e3 for k, v in phase_ms.items()},
+        "decode_kernel": {"achieved_gbps": decode_gbps, "plan": plan},
+        "wall_s_timed_loop_incl_flush": t_wall,
+        "warm": warm,
+        "cpu_baseline": cpu,
+        "host": platform.node(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * quest.h -- C ABI of libquest.so: Quest query-aware sparse decode attention
+ * over a paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method.  Quest (Tang et al., "Quest: Query-Aware Sparsity for Efficient
+ * Long-Context LLM Inference", ICML 2024) keeps, per KV page, the elementwise
+ * minimum and maximum of the page's keys.  At each decode step the current
+ * query gives every page an upper bound on q.k over that min/max box, the
+ * best pages within a token budget are selected per KV head, and attention
+ * runs over those pages only.
+ *
+ * Where the pages put it.  The Sparse-vLLM skill page "add-sparse-method"
+ * (Placement Rules 2-4, Decision Rules) places persistent per-page metadata in
+ * the method's cache manager, refreshes it through on_kv_stored after KV is
+ * written, and builds the decode-time view from the current layer's q through
+ * build_decode_view.  The SparseEngine digest ("SparseEngine: Sparse-First
+ * Inference Engine", Method key points) registers Quest's query-relevant page
+ * selection as a lifecycle hook, lets each method's cache manager own KV
+ * representation, physical layout, position mapping and metadata, and hands
+ * the backend an explicit-KV attention view.  The four entry points below are
+ * those steps:
+ *     quest_append_kv      on_kv_stored: KV store + fused min/max refresh
+ *     quest_page_scores    build_decode_view, part 1: per-page bounds from q
+ *     quest_topk_pages     build_decode_view, part 2: top-k within the budget
+ *     quest_sparse_decode  attention over the selected explicit-KV view
+ *
+ * Conventions shared by every entry point
+ *  - All buffers are device memory owned by the caller (the cache manager
+ *    role).  The library allocates nothing, keeps no pointer after a call
+ *    returns and holds no state between calls.  The layout struct is read
+ *    during the call only.
+ *  - Every call is asynchronous: it validates its arguments on the host,
+ *    enqueues kernels on `stream` (a hipStream_t passed as void*, NULL for the
+ *    null stream) and returns.  It never synchronises, allocates or copies
+ *    device memory to the host, so a sequence of calls may be captured into a
+ *    hipGraph.
+ *  - Return value: QUEST_OK (0) or a negative quest_status.  Validation runs
+ *    before any HIP call; on a validation error nothing is launched.  A launch
+ *    failure reported by HIP returns QUEST_ERR_HIP.  Nothing is printed, no
+ *    exception crosses the ABI, the library never aborts.
+ *  - batch == 0 is valid and launches nothing.
+ *  - Device-side preconditions, not checked on the host (the data lives on the
+ *    device): page-table entries of live pages lie in [0, num_pool_pages);
+ *    ctx_lens[r] <= max_pages_per_seq * page_size; budgets >= 0.  Kernels skip
+ *    any page id outside the pool and any index outside a row instead of
+ *    touching memory out of bounds; results for such inputs are unspecified.
+ *  - Numbers: q, K, V, the page metadata and the output share one element type
+ *    (fp32, or bf16 with round-to-nearest-even on every bf16 write).  Scores,
+ *    softmax statistics and accumulators are fp32.
+ */
+#ifndef QUEST_H
+#define QUEST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QUEST_ABI_VERSION 1
+
+typedef enum {
+  QUEST_OK = 0,
+  QUEST_ERR_NULL = -1,        /* a required pointer is NULL */
+  QUEST_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+  QUEST_ERR_UNSUPPORTED = -3, /* valid but not built: dtype, D, P, G */
+  QUEST_ERR_WORKSPACE = -4,   /* workspace missing or too small */
+  QUEST_ERR_ABI = -5,         /* layout.abi_version != QUEST_ABI_VERSION */
+  QUEST_ERR_HIP = -6          /* the HIP runtime rejected a launch */
+} quest_status;
+
+typedef enum { QUEST_F32 = 0, QUEST_BF16 = 1 } quest_dtype;
+
+/* How a KV head's page score combines the scores of the q heads that share
+ * it (grouped-query attention).  MAX keeps the score an upper bound of q.k for
+ * every q head of the group; SUM bounds the group-summed logit. */
+typedef enum { QUEST_REDUCE_MAX = 0, QUEST_REDUCE_SUM = 1 } quest_group_reduce;
+
+/* Shape of one attention layer's paged cache.
+ *   num_q_heads (Hq) and num_kv_heads (Hkv): Hq % Hkv == 0, G = Hq/Hkv <= 16;
+ *     q head h reads KV head h / G.
+ *   head_dim (D): 64 or 128.   page_size (P): 16 or 32 tokens.
+ *   dtype: quest_dtype of q, K, V, metadata and output.
+ *   num_pool_pages: physical pages in the pool shared by all requests.
+ *   max_pages_per_seq: row stride of the page table and of the score array. */
+typedef struct {
+  int32_t abi_version;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t dtype;
+  int64_t num_pool_pages;
+  int32_t max_pages_per_seq;
+  int32_t reserved;           /* set to 0 */
+} quest_layout;
+
+/* Device layouts (row-major, contiguous):
+ *   k_cache    [num_pool_pages][Hkv][P][D]   token-major pages
+ *   v_cache    [num_pool_pages][Hkv][D][P]   dim-major pages (each channel's
+ *                                            P values are contiguous)
+ *   kmeta      [num_pool_pages][Hkv][2][D]   [..][0][d] = min, [..][1][d] = max
+ *   page_table int32 [batch][max_pages_per_seq]: logical page j of request r
+ *              -> physical page; position p lives in logical page p / P at slot
+ *              p % P.  Only entries j < ceil(ctx/P) are read.
+ *   ctx_lens   int32 [batch]: valid tokens of each request.
+ *   q, out     [batch][Hq][D]
+ *   scores     fp32 [batch][Hkv][max_pages_per_seq]
+ *   budget_tokens int32 [batch]
+ *   sel_pages  int32 [batch][Hkv][max_k]; num_sel int32 [batch][Hkv] */
+
+/* Returns QUEST_ABI_VERSION of the loaded library. */
+int quest_abi_version(void);
+
+/* Static, human-readable name of a quest_status value. */
+const char *quest_status_string(int status);
+
+/* on_kv_stored (Sparse-vLLM "add-sparse-method", Placement Rules 3): stores
+ * new tokens and refreshes the page metadata in one pass.
+ *   k_new, v_new  [T][Hkv][D]; request r owns rows cu_new[r] .. cu_new[r+1]-1
+ *                 (cu_new int32 [batch+1], device, non-decreasing, cu_new[0]=0)
+ *   ctx_before    int32 [batch], device: tokens request r held before; its new
+ *                 tokens take positions ctx_before[r], ctx_before[r]+1, ...
+ *   max_new_per_seq  host hint, >= 0: the largest per-request token count; it
+ *                 sizes the grid only (every token is stored whatever it is).
+ * K and V go to their slots.  For every touched page and KV head, the metadata
+ * becomes the elementwise min/max of the new tokens when the first new token
+ * sits at the page's slot 0 (a fresh page: nothing stale from a previous owner
+ * survives), and otherwise of the stored metadata and the new tokens.  Min and
+ * max are exact (no rounding).  A request's pages must not be shared with
+ * another request's new tokens in the same call. */
+int quest_append_kv(const quest_layout *layout, int32_t batch,
+                    const void *k_new, const void *v_new,
+                    const int32_t *cu_new, const int32_t *ctx_before,
+                    int32_t max_new_per_seq, const int32_t *page_table,
+                    void *k_cache, void *v_cache, void *kmeta, void *stream);
+
+/* build_decode_view, part 1 (Placement Rules 4; SparseEngine digest, Method
+ * key points, query-relevant page selection): for every request r, KV head g
+ * and logical page j < ceil(ctx_lens[r]/P),
+ *   U[h][j] = sum_d max(q[r][h][d]*min[j][g][d], q[r][h][d]*max[j][g][d])
+ * for each q head h of group g (q unscaled), and
+ *   scores[r][g][j] = max_h U[h][j]   (group_reduce MAX) or sum_h (SUM).
+ * Products of bf16 values are exact in fp32; sums are fp32 in an unspecified
+ * order.  Entries j >= ceil(ctx/P) are not written. */
+int quest_page_scores(const quest_layout *layout, int32_t batch,
+                      const void *q, const void *kmeta,
+                      const int32_t *page_table, const int32_t *ctx_lens,
+                      int32_t group_reduce, float *scores, void *stream);
+
+/* build_decode_view, part 2: k_r = min(max_k, clamp(floor(budget_tokens[r] /
+ * P), 1, n_r)) pages per (request, KV head), n_r = ceil(ctx_lens[r]/P);
+ * k_r = 0 when ctx_lens[r] == 0.  The k_r pages with the largest scores are
+ * selected; equal scores go to the lower logical page (-0.0 equals +0.0).
+ * sel_pages[r][g][0..k_r-1] receives their logical ids in ascending order,
+ * the rest of the row -1; num_sel[r][g] = k_r.  Selection is exact: any
+ * correct top-k of the given scores returns the same ids. */
+int quest_topk_pages(const quest_layout *layout, int32_t batch,
+                     const float *scores, const int32_t *ctx_lens,
+                     const int32_t *budget_tokens, int32_t max_k,
+                     int32_t *sel_pages, int32_t *num_sel, void *stream);
+
+/* Workspace bytes quest_sparse_decode needs for this batch and max_k (0 for
+ * batch 0).  A pure function of its arguments; never calls HIP. */
+size_t quest_sparse_decode_workspace_bytes(const quest_layout *layout,
+                                           int32_t batch, int32_t max_k);
+
+/* Attention over the explicit-KV view (SparseEngine digest, Method key
+ * points, AttentionView): for q head h of request r, with g = h / G,
+ *   out[r][h] = sum_t softmax_t(sm_scale * q[r][h].k_t) v_t
+ * over the valid tokens t (< ctx_lens[r]) of the pages sel_pages[r][g][0 ..
+ * num_sel[r][g]-1].  A head with no token in its view outputs zeros.
+ * Split-K: pages are spread over work-groups, each keeps a running max, sum
+ * and fp32 accumulator, and a second kernel merges the partials.  The bf16
+ * path rounds softmax weights to bf16 for the matrix-core P*V product.
+ * workspace: device memory of at least quest_sparse_decode_workspace_bytes;
+ * contents on entry do not matter. */
+int quest_sparse_decode(const quest_layout *layout, int32_t batch,
+                        const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *page_table, const int32_t *ctx_lens,
+                        const int32_t *sel_pages, const int32_t *num_sel,
+                        int32_t max_k, float sm_scale, void *out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Launch plan quest_sparse_decode uses (for reports): number of KV splits per
+ * (request, KV head) and pages per split.  Never calls HIP. */
+int quest_sparse_decode_plan(const quest_layout *layout, int32_t batch,
+                             int32_t max_k, int32_t *num_splits,
+                             int32_t *pages_per_split);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUEST_H */

@@ -1,0 +1,198 @@
+// page_scores.hip -- build_decode_view, part 1: Quest page upper bounds.
+//
+// For request r, KV head g, logical page j and each q head h of g's group:
+//     U[h][j] = sum_d max(q_hd * min_jd, q_hd * max_jd)
+// (Quest's bound on q.k over the page's min/max box; SparseEngine digest,
+// Method key points: query-relevant page selection through the decode-time q).
+// The KV head's score is the max (or sum) of U over its G q heads.
+//
+// bf16 path (matrix cores).  With q+ = max(q, 0) and q- = min(q, 0),
+//     max(q*a, q*b) = q+ * b + q- * a     whenever a <= b,
+// so U = [q- | q+] . [min | max]: a dot product of length 2D against the
+// page's metadata row, which is stored exactly in that order ([min][D] then
+// [max][D]).  A 16-page tile of one KV head is then a skinny GEMM
+//     C[16 heads][16 pages] = A[16 heads][2D] * B[2D][16 pages]
+// run as 2D/32 v_mfma_f32_16x16x32_bf16 steps.  Heads past G are zero rows.
+// Every product of two bf16 values is exact in fp32 and the zero halves add
+// exact zeros, so the only rounding is the fp32 accumulation.  The kernel is
+// bound by streaming the metadata (512 B per page and KV head at D = 128);
+// the matrix cores only remove the per-element select/multiply work that
+// would otherwise load the vector ALUs at HBM speed.
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 on a 64-lane wave: lane l holds
+// row (l % 16) of A and column (l % 16) of B, each for the eight K slots of
+// group l / 16; the 16x16 fp32 result gives lane l column l % 16, rows
+// 4*(l/16) .. 4*(l/16)+3.  Both operands use the same (group, element) -> k
+// assignment, so the sum over k is exact whatever order the unit uses inside.
+#include "quest_device.h"
+#include "quest_launch.h"
+
+namespace quest {
+
+constexpr int kScoreTilesPerWave = 4;
+constexpr int kScoreWaves = 4;
+constexpr int kScorePagesPerBlock = kScoreWaves * kScoreTilesPerWave * 16;
+
+// Splits 16 B of bf16 q values into their negative and positive parts,
+// halfword by halfword, by the sign bit (-0 goes to the negative part, where
+// it still contributes an exact zero).
+__device__ __forceinline__ void split_signs(uint4 w, uint4 &neg, uint4 &pos) {
+  uint32_t in[4] = {w.x, w.y, w.z, w.w}, n[4], p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = ((in[i] & 0x80008000u) >> 15) * 0xffffu;
+    n[i] = in[i] & m;
+    p[i] = in[i] & ~m;
+  }
+  neg = make_uint4(n[0], n[1], n[2], n[3]);
+  pos = make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) {
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void page_scores_mfma_kernel(
+    int Hkv, int G, int64_t pool, int P, int max_pages, int reduce,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kmeta,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
+    float *__restrict__ scores) {
+  constexpr int kChunks = 2 * D / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;          // head row of A, page column of B
+  const int grp = lane >> 4;          // K-slot group
+  const int g = blockIdx.x % Hkv;
+  const int block = blockIdx.x / Hkv;
+  const int r = blockIdx.y;
+  const int n = pages_in(ctx_lens[r], P, max_pages);
+  const int base = block * kScorePagesPerBlock;
+  if (base >= n) return;
+
+  // A operand: [q- | q+] of head `col` of the group (zero rows past G).
+  bf16x8 a[kChunks];
+  {
+    const uint16_t *qh = q + ((int64_t)r * Hkv * G + (int64_t)g * G + col) * D;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int k0 = c * 32 + grp * 8;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (col < G) w = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
+      uint4 neg, pos;
+      split_signs(w, neg, pos);
+      a[c] = as_bf16x8(k0 < D ? neg : pos);
+    }
+  }
+
+  const int32_t *pt = page_table + (int64_t)r * max_pages;
+  float *out = scores + ((int64_t)r * Hkv + g) * max_pages;
+
+  // Physical page of this lane's column in each of the wave's tiles.
+  int page[kScoreTilesPerWave];
+  int64_t row[kScoreTilesPerWave];
+#pragma unroll
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+    page[t] = base + (t * kScoreWaves + wave) * 16 + col;
+    int64_t phys = -1;
+    if (page[t] < n) {
+      phys = pt[page[t]];
+      if (phys >= pool) phys = -1;
+    }
+    row[t] = phys < 0 ? -1 : (phys * Hkv + g) * (2 * D);
+  }
+
+  uint4 b[2][kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    b[0][c] = row[0] >= 0 ? *(const uint4 *)(kmeta + row[0] + c * 32 + grp * 8)
+                          : make_uint4(0, 0, 0, 0);
+
+#pragma unroll
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < kScoreTilesPerWave) {
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c)
+        b[cur ^ 1][c] = row[t + 1] >= 0
+                            ? *(const uint4 *)(kmeta + row[t + 1] + c * 32 + grp * 8)
+                            : make_uint4(0, 0, 0, 0);
+    }
+    if (base + (t * kScoreWaves + wave) * 16 >= n) continue;   // whole tile empty
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], as_bf16x8(b[cur][c]), acc, 0, 0, 0);
+    // lane holds page `col`, heads 4*grp .. 4*grp+3: combine the group.
+    float v = reduce == 0 ? -__builtin_huge_valf() : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * grp + i < G) v = reduce == 0 ? fmaxf(v, acc[i]) : v + acc[i];
+    }
+    const float o16 = __shfl_xor(v, 16, kWave);
+    v = reduce == 0 ? fmaxf(v, o16) : v + o16;
+    const float o32 = __shfl_xor(v, 32, kWave);
+    v = reduce == 0 ? fmaxf(v, o32) : v + o32;
+    if (grp == 0 && page[t] < n) out[page[t]] = v;
+  }
+}
+
+// fp32 path: one thread per page, the group's q in LDS.  Each term takes the
+// product on the side the sign of q selects; rounding is monotonic, so this
+// is the larger of the two rounded products.
+__global__ __launch_bounds__(256) void page_scores_valu_kernel(
+    int Hkv, int G, int D, int64_t pool, int P, int max_pages, int reduce,
+    const float *__restrict__ q, const float *__restrict__ kmeta,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
+    float *__restrict__ scores) {
+  extern __shared__ float q_lds[];     // [G][D]
+  const int g = blockIdx.y, r = blockIdx.z;
+  const float *qg = q + ((int64_t)r * Hkv * G + (int64_t)g * G) * D;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_lds[i] = qg[i];
+  __syncthreads();
+  const int n = pages_in(ctx_lens[r], P, max_pages);
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int64_t phys = page_table[(int64_t)r * max_pages + j];
+  if (phys < 0 || phys >= pool) return;
+  const float *lo = kmeta + (phys * Hkv + g) * 2 * D;
+  const float *hi = lo + D;
+  float v = reduce == 0 ? -__builtin_huge_valf() : 0.f;
+  for (int h = 0; h < G; ++h) {
+    float u = 0.f;
+    for (int d = 0; d < D; ++d) {
+      const float qd = q_lds[h * D + d];
+      u += qd >= 0.f ? qd * hi[d] : qd * lo[d];
+    }
+    v = reduce == 0 ? fmaxf(v, u) : v + u;
+  }
+  scores[((int64_t)r * Hkv + g) * max_pages + j] = v;
+}
+
+hipError_t launch_page_scores(const Dims &dm, int batch, const void *q,
+                              const void *kmeta, const int32_t *page_table,
+                              const int32_t *ctx_lens, int reduce,
+                              float *scores, hipStream_t stream) {
+  if (dm.dtype == 1) {
+    const int blocks = (dm.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
+    dim3 grid((unsigned)(blocks * dm.Hkv), (unsigned)batch);
+    dim3 block(64 * kScoreWaves);
+    if (dm.D == 128)
+      hipLaunchKernelGGL(page_scores_mfma_kernel<128>, grid, block, 0, stream, dm.Hkv, dm.G,
+                         dm.pool, dm.P, dm.max_pages, reduce, (const uint16_t *)q,
+                         (const uint16_t *)kmeta, page_table, ctx_lens, scores);
+    else
+      hipLaunchKernelGGL(page_scores_mfma_kernel<64>, grid, block, 0, stream, dm.Hkv, dm.G,
+                         dm.pool, dm.P, dm.max_pages, reduce, (const uint16_t *)q,
+                         (const uint16_t *)kmeta, page_table, ctx_lens, scores);
+  } else {
+    dim3 grid((unsigned)((dm.max_pages + 255) / 256), (unsigned)dm.Hkv, (unsigned)batch);
+    hipLaunchKernelGGL(page_scores_valu_kernel, grid, dim3(256),
+                       (size_t)dm.G * dm.D * sizeof(float), stream, dm.Hkv, dm.G, dm.D,
+                       dm.pool, dm.P, dm.max_pages, reduce, (const float *)q,
+                       (const float *)kmeta, page_table, ctx_lens, scores);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace quest

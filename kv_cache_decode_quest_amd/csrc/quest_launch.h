@@ -1,0 +1,50 @@
+// quest_launch.h -- internal interface between the C ABI (quest_abi.cpp) and
+// the kernel files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace quest {
+
+struct Dims {
+  int Hq, Hkv, G, D, P;
+  int dtype;          // 0 fp32, 1 bf16
+  int64_t pool;       // physical pages
+  int max_pages;      // page-table row stride
+};
+
+hipError_t launch_append(const Dims &dm, int batch, const void *k_new,
+                         const void *v_new, const int32_t *cu_new,
+                         const int32_t *ctx_before, int max_new,
+                         const int32_t *page_table, void *k_cache,
+                         void *v_cache, void *kmeta, hipStream_t stream);
+
+hipError_t launch_page_scores(const Dims &dm, int batch, const void *q,
+                              const void *kmeta, const int32_t *page_table,
+                              const int32_t *ctx_lens, int reduce,
+                              float *scores, hipStream_t stream);
+
+hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
+                       const int32_t *ctx_lens, const int32_t *budget_tokens,
+                       int max_k, int32_t *sel_pages, int32_t *num_sel,
+                       hipStream_t stream);
+
+struct DecodePlan {
+  int n_split;          // splits per (request, KV head)
+  int pages_per_split;  // selected pages one work-group attends
+};
+
+// Pure host arithmetic; no HIP call.
+DecodePlan decode_plan(const Dims &dm, int batch, int max_k);
+size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k);
+
+hipError_t launch_decode(const Dims &dm, int batch, const void *q,
+                         const void *k_cache, const void *v_cache,
+                         const int32_t *page_table, const int32_t *ctx_lens,
+                         const int32_t *sel_pages, const int32_t *num_sel,
+                         int max_k, float sm_scale, void *out,
+                         float *workspace, hipStream_t stream);
+
+}  // namespace quest

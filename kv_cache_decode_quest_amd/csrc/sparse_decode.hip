@@ -1,0 +1,452 @@
+// sparse_decode.hip -- attention over the selected pages (the explicit-KV
+// attention view of the SparseEngine digest, Method key points), as a split-K
+// paged flash-decode followed by a log-sum-exp merge.
+//
+// Work split.  A work-group owns one (request, KV head) row and one split of
+// that row's selected pages; its waves take the split's pages round-robin.
+// All G q heads of the KV head are processed together, so each K/V page is
+// read from HBM once per step.  Each wave keeps, per head, a running max m,
+// a running sum l and an fp32 accumulator acc[D] (online softmax, logits in
+// base 2: x = sm_scale * log2(e) * q.k); the waves of a work-group merge
+// through LDS and write one partial (acc, m, l) per head; merge_kernel then
+// combines the splits.
+//
+// bf16 path (matrix cores, one 64-lane wave per page at a time):
+//   S = K q^T   C[16 tokens][16 heads] += K[16 tokens][32 d] * q^T[32 d][16 heads]
+//               (v_mfma_f32_16x16x32_bf16, D/32 steps per 16-token tile; K
+//               pages are token-major, so each lane loads 16 contiguous bytes)
+//   O += P V    C[16 heads][16 d] += P[16 heads][16 tokens] * V[16 tokens][16 d]
+//               (v_mfma_f32_16x16x16_bf16, one step per 16-token tile and
+//               16-channel tile; V pages are dim-major, so each lane loads 4
+//               consecutive tokens of one channel as 8 contiguous bytes)
+// The result of the first product leaves lane l with head l % 16 and tokens
+// 4*(l/16)..+3, which is exactly the lane's A operand of the second product:
+// softmax weights never leave their registers.  Weights are rounded to bf16
+// for the second product, and the running sum l adds the rounded weights, so
+// the output stays a convex combination of V rows.  Heads past G are zero
+// columns of q^T.
+#include "quest_device.h"
+#include "quest_launch.h"
+
+namespace quest {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kTargetWaves = 2048;     // 8 waves per CU on 256 CUs
+constexpr float kLog2e = 1.4426950408889634f;
+
+DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
+  DecodePlan p{1, max_k > 0 ? max_k : 1};
+  const long rows = (long)batch * dm.Hkv;
+  if (rows <= 0 || max_k <= 0) return p;
+  long ppw = (rows * max_k + kTargetWaves - 1) / kTargetWaves;   // pages per wave
+  if (ppw < 1) ppw = 1;
+  if (ppw > 16) ppw = 16;
+  long pps = ppw * kDecodeWaves;
+  if (pps > max_k) pps = max_k;
+  p.pages_per_split = (int)pps;
+  p.n_split = (int)((max_k + pps - 1) / pps);
+  return p;
+}
+
+size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k) {
+  if (batch <= 0) return 0;
+  const DecodePlan p = decode_plan(dm, batch, max_k);
+  return (size_t)batch * dm.Hkv * p.n_split * dm.G * (dm.D + 2) * sizeof(float);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// bf16 matrix-core kernel
+// ---------------------------------------------------------------------------
+template <int D, int P>
+struct PageRegs {
+  static constexpr int TT = P / 16;     // 16-token tiles
+  static constexpr int KC = D / 32;     // 32-channel chunks of q.k
+  static constexpr int NT = D / 16;     // 16-channel tiles of P.V
+  uint4 k[TT][KC];
+  uint2 v[TT][NT];
+};
+
+template <int D, int P>
+__device__ __forceinline__ void load_page(PageRegs<D, P> &pr, const uint16_t *__restrict__ kp,
+                                         const uint16_t *__restrict__ vp, int col, int grp) {
+#pragma unroll
+  for (int tt = 0; tt < PageRegs<D, P>::TT; ++tt) {
+#pragma unroll
+    for (int c = 0; c < PageRegs<D, P>::KC; ++c)
+      pr.k[tt][c] = *(const uint4 *)(kp + (tt * 16 + col) * D + c * 32 + grp * 8);
+#pragma unroll
+    for (int nt = 0; nt < PageRegs<D, P>::NT; ++nt)
+      pr.v[tt][nt] = *(const uint2 *)(vp + (nt * 16 + col) * P + tt * 16 + grp * 4);
+  }
+}
+
+template <int D, int P>
+__global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
+    int Hkv, int G, int64_t pool, int max_pages, int max_k, int n_split, int pps,
+    float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
+    const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
+  using PR = PageRegs<D, P>;
+  __shared__ float lds_m[kDecodeWaves][16];
+  __shared__ float lds_l[kDecodeWaves][16];
+  __shared__ float lds_acc[kDecodeWaves][16][D];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x % n_split;
+  const int row = blockIdx.x / n_split;
+  const int r = row / Hkv, g = row - r * Hkv;
+  const int nsel = min(num_sel[row], max_k);
+  const int first = split * pps;
+  if (first >= nsel) return;                       // merge reads only live splits
+  const int last = min(nsel, first + pps);
+  const int ctx = ctx_lens[r];
+  const int n = pages_in(ctx, P, max_pages);
+  const int32_t *sel = sel_pages + (int64_t)row * max_k;
+  const int32_t *pt = page_table + (int64_t)r * max_pages;
+
+  // q^T operand: column `col` = head, K slots of group `grp` (zero past G).
+  bf16x8 qop[PR::KC];
+  {
+    const uint16_t *qh = q + ((int64_t)r * Hkv * G + (int64_t)g * G + col) * D;
+#pragma unroll
+    for (int c = 0; c < PR::KC; ++c) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (col < G) w = *(const uint4 *)(qh + c * 32 + grp * 8);
+      qop[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  f32x4 acc[PR::NT];
+#pragma unroll
+  for (int nt = 0; nt < PR::NT; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_huge_valf();     // running max of head `col` (base-2 logits)
+  float l = 0.f;                        // running sum of head `col`
+
+  const int64_t page_elems = (int64_t)P * D;
+  // Page i of this wave: logical page, physical page, valid tokens.
+  auto page_of = [&](int i, int64_t &phys, int &valid) {
+    const int j = sel[i];
+    phys = -1;
+    valid = 0;
+    if (j >= 0 && j < n) {
+      const int64_t ph = pt[j];
+      if (ph >= 0 && ph < pool) {
+        phys = ph;
+        valid = min(P, ctx - j * P);
+      }
+    }
+  };
+
+  int i = first + wave;
+  PR cur, nxt;
+  int64_t phys_c = -1, phys_n = -1;
+  int valid_c = 0, valid_n = 0;
+  if (i < last) {
+    page_of(i, phys_c, valid_c);
+    if (phys_c >= 0)
+      load_page<D, P>(cur, k_cache + (phys_c * Hkv + g) * page_elems,
+                      v_cache + (phys_c * Hkv + g) * page_elems, col, grp);
+  }
+  for (; i < last; i += kDecodeWaves) {
+    const int inext = i + kDecodeWaves;
+    if (inext < last) {
+      page_of(inext, phys_n, valid_n);
+      if (phys_n >= 0)
+        load_page<D, P>(nxt, k_cache + (phys_n * Hkv + g) * page_elems,
+                        v_cache + (phys_n * Hkv + g) * page_elems, col, grp);
+    }
+    if (phys_c >= 0) {
+      // A partial page's unwritten slots may hold anything (NaN included):
+      // zero their V values, since a zero weight times NaN is still NaN.
+      if (valid_c < P) {
+#pragma unroll
+        for (int tt = 0; tt < PR::TT; ++tt) {
+          const int t0 = tt * 16 + 4 * grp;
+          const uint32_t mx = (t0 + 0 < valid_c ? 0x0000ffffu : 0u) |
+                              (t0 + 1 < valid_c ? 0xffff0000u : 0u);
+          const uint32_t my = (t0 + 2 < valid_c ? 0x0000ffffu : 0u) |
+                              (t0 + 3 < valid_c ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int nt = 0; nt < PR::NT; ++nt) {
+            cur.v[tt][nt].x &= mx;
+            cur.v[tt][nt].y &= my;
+          }
+        }
+      }
+      // logits: lane holds head `col`, tokens tt*16 + 4*grp + e
+      f32x4 s[PR::TT];
+      float pmax = -__builtin_huge_valf();
+#pragma unroll
+      for (int tt = 0; tt < PR::TT; ++tt) {
+        f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < PR::KC; ++c)
+          c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, cur.k[tt][c]), qop[c], c4, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = tt * 16 + 4 * grp + e;
+          const float x = tok < valid_c ? c4[e] * scale2 : -__builtin_huge_valf();
+          s[tt][e] = x;
+          pmax = fmaxf(pmax, x);
+        }
+      }
+      pmax = wave_max_xor(pmax, 16);
+      pmax = wave_max_xor(pmax, 32);
+      const float m_new = fmaxf(m, pmax);
+      const float alpha = (m == -__builtin_huge_valf()) ? 0.f : exp2_fast(m - m_new);
+      float psum = 0.f;
+      s16x4 pop[PR::TT];
+#pragma unroll
+      for (int tt = 0; tt < PR::TT; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t b = f32_to_bf16_bits(exp2_fast(s[tt][e] - m_new));
+          psum += bf16_bits_to_f32(b);
+          pop[tt][e] = (short)b;
+        }
+      }
+      psum += __shfl_xor(psum, 16, kWave);
+      psum += __shfl_xor(psum, 32, kWave);
+      l = l * alpha + psum;
+      m = m_new;
+      // rescale: this lane's accumulator rows are heads 4*grp .. 4*grp+3
+      float a4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a4[e] = __shfl(alpha, 4 * grp + e, kWave);
+#pragma unroll
+      for (int nt = 0; nt < PR::NT; ++nt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[nt][e] *= a4[e];
+#pragma unroll
+        for (int tt = 0; tt < PR::TT; ++tt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              pop[tt], __builtin_bit_cast(s16x4, cur.v[tt][nt]), acc[nt], 0, 0, 0);
+      }
+    }
+    cur = nxt;
+    phys_c = phys_n;
+    valid_c = valid_n;
+    phys_n = -1;
+  }
+
+  // merge the waves of this work-group
+  if (grp == 0) {
+    lds_m[wave][col] = m;
+    lds_l[wave][col] = l;
+  }
+#pragma unroll
+  for (int nt = 0; nt < PR::NT; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lds_acc[wave][4 * grp + e][nt * 16 + col] = acc[nt][e];
+  __syncthreads();
+  float *base = partial + ((int64_t)row * n_split + split) * G * (D + 2);
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D, d = idx - h * D;
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, lds_m[w][h]);
+    float a = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float mw = lds_m[w][h];
+      const float f = (mw == -__builtin_huge_valf()) ? 0.f : exp2_fast(mw - M);
+      a += f * lds_acc[w][h][d];
+      L += f * lds_l[w][h];
+    }
+    float *ph = base + h * (D + 2);
+    ph[d] = a;
+    if (d == 0) {
+      ph[D] = M;
+      ph[D + 1] = L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (vector ALUs): one work-group walks its split's pages in order,
+// staging each K and V page in LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
+    int Hkv, int G, int D, int P, int64_t pool, int max_pages, int max_k, int n_split,
+    int pps, float scale2, const float *__restrict__ q, const float *__restrict__ k_cache,
+    const float *__restrict__ v_cache, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
+    const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
+  extern __shared__ float lds[];
+  float *q_s = lds;                 // [G][D]
+  float *k_s = q_s + G * D;         // [P][D]
+  float *v_s = k_s + P * D;         // [D][P]
+  float *p_s = v_s + P * D;         // [G][P]
+  float *m_s = p_s + G * P;         // [G]
+  float *l_s = m_s + G;             // [G]
+  float *a_s = l_s + G;             // [G] rescale factors
+
+  const int split = blockIdx.x % n_split;
+  const int row = blockIdx.x / n_split;
+  const int r = row / Hkv, g = row - r * Hkv;
+  const int nsel = min(num_sel[row], max_k);
+  const int first = split * pps;
+  if (first >= nsel) return;
+  const int last = min(nsel, first + pps);
+  const int ctx = ctx_lens[r];
+  const int n = pages_in(ctx, P, max_pages);
+  const int32_t *sel = sel_pages + (int64_t)row * max_k;
+  const int32_t *pt = page_table + (int64_t)r * max_pages;
+
+  const float *qg = q + ((int64_t)r * Hkv * G + (int64_t)g * G) * D;
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) q_s[x] = qg[x];
+  for (int h = threadIdx.x; h < G; h += blockDim.x) {
+    m_s[h] = -__builtin_huge_valf();
+    l_s[h] = 0.f;
+  }
+  float acc[8];                      // pairs (h, d) = threadIdx.x + 256 * e
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  __syncthreads();
+
+  for (int i = first; i < last; ++i) {
+    const int j = sel[i];
+    if (j < 0 || j >= n) continue;
+    const int64_t phys = pt[j];
+    if (phys < 0 || phys >= pool) continue;
+    const int valid = min(P, ctx - j * P);
+    const float *kp = k_cache + (phys * Hkv + g) * (int64_t)P * D;
+    const float *vp = v_cache + (phys * Hkv + g) * (int64_t)P * D;
+    for (int x = threadIdx.x; x < P * D; x += blockDim.x) {
+      k_s[x] = kp[x];
+      v_s[x] = vp[x];
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < G * P; x += blockDim.x) {
+      const int h = x / P, t = x - h * P;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot += q_s[h * D + d] * k_s[t * D + d];
+      p_s[x] = t < valid ? dot * scale2 : -__builtin_huge_valf();
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < G; h += blockDim.x) {
+      float pm = -__builtin_huge_valf();
+      for (int t = 0; t < P; ++t) pm = fmaxf(pm, p_s[h * P + t]);
+      const float m_old = m_s[h];
+      const float m_new = fmaxf(m_old, pm);
+      const float alpha = (m_old == -__builtin_huge_valf()) ? 0.f : exp2_fast(m_old - m_new);
+      float sum = 0.f;
+      for (int t = 0; t < P; ++t) {
+        const float w = exp2_fast(p_s[h * P + t] - m_new);
+        p_s[h * P + t] = w;
+        sum += w;
+      }
+      l_s[h] = l_s[h] * alpha + sum;
+      m_s[h] = m_new;
+      a_s[h] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int x = threadIdx.x + 256 * e;
+      if (x < G * D) {
+        const int h = x / D, d = x - h * D;
+        float a = acc[e] * a_s[h];
+        for (int t = 0; t < valid; ++t) a += p_s[h * P + t] * v_s[d * P + t];
+        acc[e] = a;
+      }
+    }
+    __syncthreads();
+  }
+  float *base = partial + ((int64_t)row * n_split + split) * G * (D + 2);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int x = threadIdx.x + 256 * e;
+    if (x < G * D) {
+      const int h = x / D, d = x - h * D;
+      base[h * (D + 2) + d] = acc[e];
+      if (d == 0) {
+        base[h * (D + 2) + D] = m_s[h];
+        base[h * (D + 2) + D + 1] = l_s[h];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge: out[r][h] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(128) void merge_kernel(int Hkv, int G, int D, int max_k,
+                                                    int n_split, int pps,
+                                                    const int32_t *__restrict__ num_sel,
+                                                    const float *__restrict__ partial,
+                                                    T *__restrict__ out) {
+  const int hq = blockIdx.x;                 // r * Hq + h
+  const int Hq = Hkv * G;
+  const int r = hq / Hq, h = hq - r * Hq;
+  const int g = h / G, hl = h - g * G;
+  const int row = r * Hkv + g;
+  const int nsel = min(num_sel[row], max_k);
+  const int live = nsel <= 0 ? 0 : (nsel + pps - 1) / pps;
+  const float *base = partial + (int64_t)row * n_split * G * (D + 2) + (int64_t)hl * (D + 2);
+  const int64_t stride = (int64_t)G * (D + 2);
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < live; ++s) M = fmaxf(M, base[s * stride + D]);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float a = 0.f, L = 0.f;
+    for (int s = 0; s < live; ++s) {
+      const float ms = base[s * stride + D];
+      const float f = (ms == -__builtin_huge_valf()) ? 0.f : exp2_fast(ms - M);
+      a += f * base[s * stride + d];
+      L += f * base[s * stride + D + 1];
+    }
+    Elem<T>::store(out, (int64_t)hq * D + d, L > 0.f ? a / L : 0.f);
+  }
+}
+
+hipError_t launch_decode(const Dims &dm, int batch, const void *q,
+                         const void *k_cache, const void *v_cache,
+                         const int32_t *page_table, const int32_t *ctx_lens,
+                         const int32_t *sel_pages, const int32_t *num_sel,
+                         int max_k, float sm_scale, void *out,
+                         float *workspace, hipStream_t stream) {
+  const DecodePlan plan = decode_plan(dm, batch, max_k);
+  const float scale2 = sm_scale * kLog2e;
+  const unsigned blocks = (unsigned)((long)batch * dm.Hkv * plan.n_split);
+  if (dm.dtype == 1) {
+#define QUEST_DECODE(DD, PP)                                                              \
+  hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP>), dim3(blocks), dim3(256), 0, stream, \
+                     dm.Hkv, dm.G, dm.pool, dm.max_pages, max_k, plan.n_split,            \
+                     plan.pages_per_split, scale2, (const uint16_t *)q,                   \
+                     (const uint16_t *)k_cache, (const uint16_t *)v_cache, page_table,    \
+                     ctx_lens, sel_pages, num_sel, workspace)
+    if (dm.D == 128 && dm.P == 16) QUEST_DECODE(128, 16);
+    else if (dm.D == 128 && dm.P == 32) QUEST_DECODE(128, 32);
+    else if (dm.D == 64 && dm.P == 16) QUEST_DECODE(64, 16);
+    else QUEST_DECODE(64, 32);
+#undef QUEST_DECODE
+  } else {
+    const size_t lds = sizeof(float) * ((size_t)dm.G * dm.D + 2 * (size_t)dm.P * dm.D +
+                                        (size_t)dm.G * dm.P + 3 * (size_t)dm.G);
+    hipLaunchKernelGGL(sparse_decode_valu_kernel, dim3(blocks), dim3(256), lds, stream,
+                       dm.Hkv, dm.G, dm.D, dm.P, dm.pool, dm.max_pages, max_k, plan.n_split,
+                       plan.pages_per_split, scale2, (const float *)q, (const float *)k_cache,
+                       (const float *)v_cache, page_table, ctx_lens, sel_pages, num_sel,
+                       workspace);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const unsigned mblocks = (unsigned)((long)batch * dm.Hkv * dm.G);
+  if (dm.dtype == 1)
+    hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.Hkv,
+                       dm.G, dm.D, max_k, plan.n_split, plan.pages_per_split, num_sel,
+                       workspace, (uint16_t *)out);
+  else
+    hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.Hkv,
+                       dm.G, dm.D, max_k, plan.n_split, plan.pages_per_split, num_sel,
+                       workspace, (float *)out);
+  return hipGetLastError();
+}
+
+}  // namespace quest

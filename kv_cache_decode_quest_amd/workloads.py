@@ -34,6 +34,7 @@ class Workload:
     dtype: str                      # "f32" or "bf16"
     ctx: int = 0                    # fixed context per request (if ctx_range is None)
     ctx_range: tuple | None = None  # inclusive uniform range for ragged batches
+    ctx_list: tuple | None = None   # explicit per-request lengths (edge cases)
     budget_tokens: int = 0          # fixed token budget per request ...
     budget_page_div: int = 0        # ... or max(1, n_pages // div) whole pages
     steps: int = 1                  # decode steps, one appended token per request each
@@ -117,6 +118,9 @@ class Layout:
 
 def context_lengths(w: Workload) -> torch.Tensor:
     """int32 [B] on the CPU: prompt lengths (seeded for ragged workloads)."""
+    if w.ctx_list is not None:
+        assert len(w.ctx_list) == w.batch
+        return torch.tensor(w.ctx_list, dtype=torch.int32)
     if w.ctx_range is None:
         return torch.full((w.batch,), w.ctx, dtype=torch.int32)
     lo, hi = w.ctx_range

@@ -1,0 +1,194 @@
+"""GPU-vs-oracle parity plumbing: builds one layer's paged cache on the GPU
+through the library and the same cache on the host through the oracle, runs
+decode steps on both, and compares.
+
+Tolerances (floating point; integers and page ids are compared exactly):
+  page metadata   exact (min/max involve no rounding)
+  page scores     |S_gpu - S_ref| <= 2 (D + 2) 2^-24 max_h sum_d |q_hd| max(|min_d|, |max_d|)
+                  (fp32 summation bound gamma_n, doubled for any rounding mode)
+  selections      bit-exact per row; a row whose differing pages all pair up
+                  with scores within 1e-5 relative is only flagged
+  outputs         max-abs <= 2e-2 and mean-abs <= 2e-3, and elementwise
+                  |err| <= 2^-8 |o| + 5e-4 (bf16) or 1e-5 (1 + |o|) (fp32)
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+from helpers import elem_of, to_f64, to_oracle
+from kv_cache_decode_quest_amd import quest, workloads
+
+U32 = 2.0 ** -24
+
+
+def log(msg):
+    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+class Layer:
+    """One attention layer's paged cache on the GPU (filled by quest_append_kv)
+    and, optionally, its host mirror for the oracle (filled by oracle.store)."""
+
+    def __init__(self, w: workloads.Workload, device, layer=0, capacity=None, host=True,
+                 kmeta_junk=7.0):
+        self.w, self.device, self.layer = w, device, layer
+        self.lay = workloads.make_layout(w, device, capacity)
+        self.L = quest.make_layout(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                   w.torch_dtype, self.lay.num_pool_pages, self.lay.max_pages)
+        self.k_cache, self.v_cache = workloads.empty_pool(w, self.lay, device)
+        self.kmeta = torch.full((self.lay.num_pool_pages, w.num_kv_heads, 2, w.head_dim),
+                                kmeta_junk, dtype=w.torch_dtype, device=device)
+        self.ctx = self.lay.ctx0.clone()
+        self.pt = self.lay.page_table
+        self.pt_host = self.pt.cpu().numpy()
+        k_new, v_new, cu, ctx_before = workloads.prefill_tokens(w, self.lay, device, layer)
+        max_new = int(self.ctx.max()) if self.ctx.numel() else 0
+        quest.quest_append_kv(self.L, k_new, v_new, cu, ctx_before, max_new, self.pt,
+                              self.k_cache, self.v_cache, self.kmeta)
+        self.shape = oracle.Shape(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                  self.lay.num_pool_pages, elem_of(w.torch_dtype))
+        self.host = None
+        if host:
+            kh, vh = workloads.empty_pool(w, self.lay, "cpu")
+            self.host = [to_oracle(kh).copy(), to_oracle(vh).copy()]
+            kn, vn, cuh = to_oracle(k_new), to_oracle(v_new), cu.cpu().numpy()
+            for r in range(w.batch):
+                a, b = int(cuh[r]), int(cuh[r + 1])
+                if b > a:
+                    oracle.store_tokens(self.shape, np.ascontiguousarray(kn[a:b]),
+                                        np.ascontiguousarray(vn[a:b]), 0, self.pt_host[r],
+                                        self.host[0], self.host[1])
+        torch.cuda.synchronize()
+
+    # ----- one decode step ---------------------------------------------------
+    def step_inputs(self, step):
+        return workloads.step_tokens(self.w, self.device, self.layer, step)
+
+    def append_step(self, k_new, v_new):
+        B = self.w.batch
+        cu = torch.arange(B + 1, dtype=torch.int32, device=self.device)
+        quest.quest_append_kv(self.L, k_new, v_new, cu, self.ctx, 1, self.pt, self.k_cache,
+                              self.v_cache, self.kmeta)
+        if self.host is not None:
+            kn, vn = to_oracle(k_new), to_oracle(v_new)
+            ctx = self.ctx.cpu().numpy()
+            for r in range(B):
+                oracle.store_tokens(self.shape, np.ascontiguousarray(kn[r:r + 1]),
+                                    np.ascontiguousarray(vn[r:r + 1]), int(ctx[r]),
+                                    self.pt_host[r], self.host[0], self.host[1])
+        self.ctx = self.ctx + 1
+
+    def budgets(self):
+        return workloads.budget_tokens(self.w, self.ctx).to(self.device)
+
+    def max_k(self):
+        b = self.budgets().cpu()
+        return max(1, int((b // self.w.page_size).max()))
+
+    def view(self, q, bufs, reduce="max"):
+        quest.quest_page_scores(self.L, q, self.kmeta, self.pt, self.ctx, bufs.scores, reduce)
+        quest.quest_topk_pages(self.L, bufs.scores, self.ctx, self.budgets(), bufs.max_k,
+                               bufs.sel_pages, bufs.num_sel)
+
+    def attend(self, q, bufs, sel=None, nsel=None, sm_scale=None):
+        sm = workloads.default_sm_scale(self.w) if sm_scale is None else sm_scale
+        quest.quest_sparse_decode(self.L, q, self.k_cache, self.v_cache, self.pt, self.ctx,
+                                  bufs.sel_pages if sel is None else sel,
+                                  bufs.num_sel if nsel is None else nsel, bufs.max_k, sm,
+                                  bufs.out, bufs.workspace)
+
+    def buffers(self, max_k=None):
+        return quest.alloc_decode_buffers(self.L, self.w.batch, max_k or self.max_k(),
+                                          self.device)
+
+    # ----- oracle side -------------------------------------------------------
+    def oracle_request(self, q, r, reduce="max", sm_scale=None):
+        sm = workloads.default_sm_scale(self.w) if sm_scale is None else sm_scale
+        qr = np.ascontiguousarray(to_oracle(q[r]))
+        ctx = int(self.ctx[r])
+        budget = int(self.budgets()[r])
+        return oracle.decode_request(self.shape, qr, self.host[0], self.host[1],
+                                     self.pt_host[r], ctx, budget, sm, reduce)
+
+
+# ----- comparisons -----------------------------------------------------------
+
+def check_pool_bytes(layer: Layer):
+    kg = to_oracle(layer.k_cache)
+    vg = to_oracle(layer.v_cache)
+    assert kg.tobytes() == layer.host[0].tobytes(), "K pool differs from the oracle's store"
+    assert vg.tobytes() == layer.host[1].tobytes(), "V pool differs from the oracle's store"
+
+
+def check_kmeta(layer: Layer, r, bounds, kmeta_host=None):
+    """GPU metadata of request r's live pages equals the oracle's from-scratch
+    min/max exactly (values; +0 and -0 compare equal)."""
+    km = to_f64(layer.kmeta) if kmeta_host is None else kmeta_host
+    n = bounds.shape[0]
+    phys = layer.pt_host[r][:n]
+    got = km[phys]                                  # [n][Hkv][2][D]
+    bad = np.argwhere(got != bounds)
+    assert bad.size == 0, f"request {r}: metadata differs at {bad[:5].tolist()}"
+
+
+def score_bound(q_r, bounds, G):
+    """Per (g, j) fp32 summation error bound of the page score."""
+    qa = np.abs(q_r)                                # [Hq][D]
+    mag = np.maximum(np.abs(bounds[:, :, 0, :]), np.abs(bounds[:, :, 1, :]))   # [n][Hkv][D]
+    Hq, D = q_r.shape
+    Hkv = Hq // G
+    per_head = np.einsum("hd,jhd->hj", qa, np.repeat(mag, G, axis=1))   # [Hq][n]
+    grp = per_head.reshape(Hkv, G, -1).max(axis=1)                      # [Hkv][n]
+    return 2.0 * (D + 2) * U32 * grp + 1e-30
+
+
+def check_scores(gpu_scores_r, ref_scores, q_r, bounds, G):
+    n = ref_scores.shape[1]
+    got = gpu_scores_r[:, :n]
+    err = np.abs(got - ref_scores)
+    tol = score_bound(q_r, bounds, G)
+    worst = (err / tol).max() if n else 0.0
+    assert np.all(err <= tol), f"scores outside the fp32 bound (worst ratio {worst:.3g})"
+    return worst
+
+
+def compare_selection(gpu_sel_row, gpu_nsel, ref_sel, ref_scores_row, rel=1e-5):
+    """Returns 'exact' or 'flagged'; raises on a real mismatch."""
+    k = len(ref_sel)
+    assert gpu_nsel == k, f"num_sel {gpu_nsel} != {k}"
+    assert np.all(gpu_sel_row[k:] == -1), "tail of the selection row is not -1"
+    g = gpu_sel_row[:k]
+    assert np.all(np.diff(g) > 0), "selection not strictly ascending"
+    if np.array_equal(g, ref_sel):
+        return "exact"
+    A = sorted(set(ref_sel.tolist()) - set(g.tolist()))
+    B = sorted(set(g.tolist()) - set(ref_sel.tolist()))
+    assert len(A) == len(B)
+    for a in A:
+        for b in B:
+            sa, sb = ref_scores_row[a], ref_scores_row[b]
+            assert abs(sa - sb) <= rel * max(abs(sa), abs(sb)), \
+                f"page {b} selected instead of {a}: scores {sb!r} vs {sa!r} are not a near-tie"
+    return "flagged"
+
+
+def check_out(got, ref, dtype, what="output"):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    if err.size == 0:
+        return 0.0
+    assert err.max() <= 2e-2, f"{what}: max-abs {err.max():.3g} > 2e-2"
+    assert err.mean() <= 2e-3, f"{what}: mean-abs {err.mean():.3g} > 2e-3"
+    if dtype == torch.bfloat16:
+        tol = 2.0 ** -8 * np.abs(ref) + 5e-4
+    else:
+        tol = 1e-5 * (1 + np.abs(ref))
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond the internal bar, max {err.max():.3g}"
+    return float(err.max())

@@ -1,0 +1,170 @@
+"""Host-side checks of libquest.so: it loads, exports every entry point the
+header declares, and rejects bad arguments before any HIP call.  Nothing here
+launches a kernel (the validation failures return before any launch, and
+batch-0 calls launch nothing)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_decode_quest_amd import quest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "quest.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ABI = 0, -1, -2, -3, -4, -5
+FAKE = ctypes.c_void_p(0x100000)          # aligned, never dereferenced on the host
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(quest_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return quest.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in quest.h but not exported"
+    assert sorted(quest.EXPORTS) == names
+
+
+def test_version_and_status_strings(lib):
+    assert quest.quest_abi_version() == 1
+    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ABI, -6):
+        assert quest.status_string(st) != "unknown status"
+    assert quest.status_string(-99) == "unknown status"
+
+
+def layout(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=4, head_dim=128, page_size=16, dtype=1,
+                num_pool_pages=1000, max_pages_per_seq=100)
+    base.update(kw)
+    abi = base.pop("abi_version", 1)
+    return quest.make_layout(base["num_q_heads"], base["num_kv_heads"], base["head_dim"],
+                             base["page_size"], base["dtype"], base["num_pool_pages"],
+                             base["max_pages_per_seq"], abi_version=abi)
+
+
+def scores_call(lib, L, batch=1, reduce=0, q=FAKE, kmeta=FAKE, out=FAKE):
+    return lib.quest_page_scores(ctypes.byref(L) if L is not None else None, batch, q, kmeta,
+                                 FAKE, FAKE, reduce, out, None)
+
+
+def decode_call(lib, L, batch=1, max_k=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, scale=0.1):
+    return lib.quest_sparse_decode(ctypes.byref(L), batch, q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, max_k, scale, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(abi_version=2), ERR_ABI),
+    (dict(num_q_heads=30), ERR_SHAPE),                 # 30 % 4 != 0
+    (dict(num_q_heads=0), ERR_SHAPE),
+    (dict(num_pool_pages=0), ERR_SHAPE),
+    (dict(max_pages_per_seq=0), ERR_SHAPE),
+    (dict(head_dim=96), ERR_UNSUPPORTED),
+    (dict(page_size=8), ERR_UNSUPPORTED),
+    (dict(dtype=7), ERR_UNSUPPORTED),
+    (dict(num_q_heads=68), ERR_UNSUPPORTED),           # G = 17 > 16
+])
+def test_layout_rejections(lib, kw, want):
+    L = layout(**kw)
+    assert scores_call(lib, L) == want
+    assert lib.quest_topk_pages(ctypes.byref(L), 1, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None) == want
+    assert decode_call(lib, L) == want
+    assert lib.quest_append_kv(ctypes.byref(L), 1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE,
+                               FAKE, None) == want
+
+
+def test_null_layout(lib):
+    assert lib.quest_page_scores(None, 1, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == ERR_NULL
+
+
+def test_batch_bounds_and_empty_batch(lib):
+    L = layout()
+    assert scores_call(lib, L, batch=-1) == ERR_SHAPE
+    assert scores_call(lib, L, batch=70000) == ERR_SHAPE
+    # batch 0: nothing to do, no pointer needed, nothing launched
+    assert lib.quest_page_scores(ctypes.byref(L), 0, None, None, None, None, 0, None, None) == OK
+    assert lib.quest_topk_pages(ctypes.byref(L), 0, None, None, None, 4, None, None, None) == OK
+    assert lib.quest_sparse_decode(ctypes.byref(L), 0, None, None, None, None, None, None, None,
+                                   4, 0.1, None, None, 0, None) == OK
+    assert lib.quest_append_kv(ctypes.byref(L), 0, None, None, None, None, 0, None, None, None,
+                               None, None) == OK
+    assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(L), 0, 4) == 0
+
+
+def test_null_pointers(lib):
+    L = layout()
+    assert scores_call(lib, L, q=None) == ERR_NULL
+    assert scores_call(lib, L, out=None) == ERR_NULL
+    assert lib.quest_topk_pages(ctypes.byref(L), 1, FAKE, None, FAKE, 8, FAKE, FAKE, None) == ERR_NULL
+    assert decode_call(lib, L, q=None) == ERR_NULL
+    assert lib.quest_append_kv(ctypes.byref(L), 1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE,
+                               None, None) == ERR_NULL
+
+
+def test_argument_rejections(lib):
+    L = layout()
+    assert scores_call(lib, L, reduce=2) == ERR_UNSUPPORTED
+    assert lib.quest_topk_pages(ctypes.byref(L), 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == ERR_SHAPE
+    assert decode_call(lib, L, max_k=0) == ERR_SHAPE
+    assert decode_call(lib, L, scale=float("nan")) == ERR_SHAPE
+    assert decode_call(lib, L, scale=float("inf")) == ERR_SHAPE
+    assert lib.quest_append_kv(ctypes.byref(L), 1, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE,
+                               FAKE, None) == ERR_SHAPE
+    # bf16 vector loads need 16-byte alignment
+    assert scores_call(lib, L, q=ctypes.c_void_p(0x100002)) == ERR_SHAPE
+    assert decode_call(lib, L, q=ctypes.c_void_p(0x100008)) == ERR_SHAPE
+
+
+def test_workspace_contract(lib):
+    L = layout()
+    need = lib.quest_sparse_decode_workspace_bytes(ctypes.byref(L), 8, 256)
+    plan = quest.quest_sparse_decode_plan(L, 8, 256)
+    assert need == 8 * 4 * plan["num_splits"] * 8 * (128 + 2) * 4
+    assert plan["num_splits"] * plan["pages_per_split"] >= 256
+    assert decode_call(lib, L, batch=8, max_k=256, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert decode_call(lib, L, batch=8, max_k=256, ws=None) == ERR_WORKSPACE
+    assert decode_call(lib, L, batch=8, max_k=256, ws=ctypes.c_void_p(0x100004)) == ERR_WORKSPACE
+    assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(layout(head_dim=96)), 8, 256) == 0
+
+
+def test_plan_covers_every_page():
+    for batch, hkv, max_k in [(1, 1, 1), (1, 1, 16), (8, 4, 256), (8, 4, 128), (32, 4, 409),
+                              (64, 4, 128), (3, 2, 1000)]:
+        L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8)
+        p = quest.quest_sparse_decode_plan(L, batch, max_k)
+        assert 1 <= p["pages_per_split"] <= max_k
+        assert (p["num_splits"] - 1) * p["pages_per_split"] < max_k
+        assert p["num_splits"] * p["pages_per_split"] >= max_k
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = quest._lib
+    quest._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            quest.load(str(tmp_path / "libquest.so"))
+    finally:
+        quest._lib = saved
+
+
+def test_product_never_touches_the_oracle():
+    """The library package and its kernels name no oracle module or file."""
+    pkg = os.path.join(ROOT, "kv_cache_decode_quest_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "quest_oracle" not in text and "libquest_oracle" not in text, f

@@ -1,0 +1,303 @@
+"""GPU parity: every step of the HIP path against the fp64 oracle.
+
+Inputs are the seeded synthetic workloads (scaled down so the oracle finishes
+in seconds, still spanning several tiles and a ragged tail), plus the full
+benchmark shape on sampled requests.  Tolerances are documented in
+tests/parity.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import to_f64, to_oracle
+from kv_cache_decode_quest_amd import quest, workloads
+from kv_cache_decode_quest_amd.workloads import WORKLOADS, scaled
+from parity import (Layer, check_kmeta, check_out, check_pool_bytes, check_scores,
+                    compare_selection, log)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+SMALL = {
+    "tiny": WORKLOADS["tiny"],
+    "layer32k_small": scaled(WORKLOADS["layer32k"], batch=3, ctx=4000, budget_tokens=512,
+                             steps=3),
+    "bench128k_small": scaled(WORKLOADS["bench128k"], batch=2, ctx=6000, budget_tokens=1024,
+                              steps=3),
+    "ragged_small": scaled(WORKLOADS["ragged"], batch=6, ctx_range=(40, 3000), steps=3),
+    "layers48_small": scaled(WORKLOADS["layers48"], batch=3, ctx=2048, budget_tokens=256,
+                             layers=2, steps=2),
+    "edges": workloads.Workload("edges", 7, 16, 2, 128, 16, "bf16",
+                                ctx_list=(0, 1, 15, 16, 17, 33, 700), budget_tokens=40,
+                                poison=float("nan"), steps=2, seed=77),
+    "edges_d64_p32": workloads.Workload("edges_d64_p32", 5, 12, 4, 64, 32, "bf16",
+                                        ctx_list=(1, 31, 32, 65, 1000), budget_tokens=100,
+                                        poison=float("nan"), steps=2, seed=78),
+    "f32_g1": workloads.Workload("f32_g1", 2, 2, 2, 128, 32, "f32", ctx=2100,
+                                 budget_tokens=300, steps=2, seed=79, permute_pages=True,
+                                 poison=1e4),
+}
+
+
+def run_and_check(w, layer=0, reduce="max"):
+    log(f"workload {w.name} layer {layer} reduce {reduce}: batch {w.batch} ctx "
+        f"{workloads.context_lengths(w).tolist()[:8]}")
+    lay = Layer(w, DEV, layer=layer)
+    check_pool_bytes(lay)
+    for r in range(w.batch):
+        ctx = int(lay.ctx[r])
+        if ctx:
+            check_kmeta(lay, r, oracle.request_bounds(lay.shape, lay.host[0], lay.pt_host[r], ctx))
+    flagged = 0
+    for step in range(w.steps):
+        q, k_new, v_new = lay.step_inputs(step)
+        lay.append_step(k_new, v_new)
+        bufs = lay.buffers()
+        lay.view(q, bufs, reduce)
+        lay.attend(q, bufs)
+        torch.cuda.synchronize()
+        check_pool_bytes(lay)
+        km = to_f64(lay.kmeta)
+        scores = bufs.scores.cpu().numpy().astype(np.float64)
+        sel = bufs.sel_pages.cpu().numpy()
+        nsel = bufs.num_sel.cpu().numpy()
+        out = to_f64(bufs.out)
+        # the oracle's own selection, fed to the decode kernel directly
+        sel_o = torch.full_like(bufs.sel_pages, -1)
+        nsel_o = torch.zeros_like(bufs.num_sel)
+        refs = []
+        for r in range(w.batch):
+            ref = lay.oracle_request(q, r, reduce)
+            refs.append(ref)
+            for g in range(w.num_kv_heads):
+                sel_o[r, g, :len(ref["sel"][g])] = torch.from_numpy(ref["sel"][g])
+                nsel_o[r, g] = len(ref["sel"][g])
+        bufs2 = lay.buffers(bufs.max_k)
+        lay.attend(q, bufs2, sel_o.to(DEV), nsel_o.to(DEV))
+        torch.cuda.synchronize()
+        out2 = to_f64(bufs2.out)
+        qh = to_f64(q)
+        for r, ref in enumerate(refs):
+            if ref["bounds"].shape[0]:
+                check_kmeta(lay, r, ref["bounds"], km)
+                check_scores(scores[r], ref["scores"], qh[r], ref["bounds"], w.group)
+            row_flag = False
+            for g in range(w.num_kv_heads):
+                verdict = compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g],
+                                            ref["scores"][g])
+                row_flag |= verdict == "flagged"
+            check_out(out2[r], ref["out"], w.torch_dtype, f"{w.name} r{r} (oracle selection)")
+            if row_flag:
+                flagged += 1
+            else:
+                check_out(out[r], ref["out"], w.torch_dtype, f"{w.name} r{r}")
+            if int(lay.ctx[r]) == 0:
+                assert np.all(out[r] == 0.0)
+    log(f"workload {w.name}: ok, flagged rows {flagged}")
+    return flagged
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_steps_match_oracle(name, gpu_lib):
+    w = SMALL[name]
+    for layer in range(w.layers):
+        run_and_check(w, layer)
+
+
+def test_group_sum_variant(gpu_lib):
+    run_and_check(SMALL["layer32k_small"], reduce="sum")
+
+
+def test_incremental_append_equals_bulk(gpu_lib):
+    """Pool and metadata after token-by-token appends equal the bulk append's."""
+    w = scaled(WORKLOADS["ragged"], batch=3, ctx_range=(20, 200), steps=0)
+    bulk = Layer(w, DEV, host=False)
+    k_c, v_c = workloads.empty_pool(w, bulk.lay, DEV)
+    km = torch.full_like(bulk.kmeta, -3.0)
+    k_new, v_new, cu, _ = workloads.prefill_tokens(w, bulk.lay, DEV)
+    cuh = cu.cpu().tolist()
+    lens = [cuh[r + 1] - cuh[r] for r in range(w.batch)]
+    ctx = torch.zeros(w.batch, dtype=torch.int32, device=DEV)
+    for t in range(max(lens)):
+        counts = [1 if t < n else 0 for n in lens]
+        rows = [cuh[r] + t for r in range(w.batch) if counts[r]]
+        sub_cu = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int32, device=DEV)
+        idx = torch.tensor(rows, dtype=torch.int64, device=DEV)
+        quest.quest_append_kv(bulk.L, k_new[idx].contiguous(), v_new[idx].contiguous(), sub_cu,
+                              ctx, 1, bulk.pt, k_c, v_c, km)
+        ctx = ctx + torch.tensor(counts, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    assert torch.equal(ctx.cpu(), bulk.ctx.cpu())
+    assert torch.equal(k_c.view(torch.int16), bulk.k_cache.view(torch.int16))
+    assert torch.equal(v_c.view(torch.int16), bulk.v_cache.view(torch.int16))
+    for r in range(w.batch):
+        n = -(-int(bulk.ctx[r]) // w.page_size)
+        phys = bulk.pt[r, :n].long()
+        assert torch.equal(km[phys].view(torch.int16), bulk.kmeta[phys].view(torch.int16))
+
+
+def test_empty_and_one_token_requests(gpu_lib):
+    """A request with no token selects nothing and outputs zeros; the others
+    match the oracle (decode without a preceding append)."""
+    w = SMALL["edges"]
+    lay = Layer(w, DEV)
+    q, _, _ = lay.step_inputs(0)
+    bufs = lay.buffers()
+    lay.view(q, bufs)
+    lay.attend(q, bufs)
+    torch.cuda.synchronize()
+    assert int(lay.ctx[0]) == 0
+    assert bufs.num_sel[0].cpu().tolist() == [0] * w.num_kv_heads
+    assert torch.all(bufs.sel_pages[0] == -1)
+    assert torch.all(bufs.out[0] == 0)
+    out = to_f64(bufs.out)
+    sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+    for r in range(1, w.batch):
+        ref = lay.oracle_request(q, r)
+        for g in range(w.num_kv_heads):
+            assert compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g],
+                                     ref["scores"][g]) == "exact"
+        check_out(out[r], ref["out"], w.torch_dtype, f"edges r{r}")
+
+
+def _topk_rows(n_max, gen):
+    rows = []
+    rows.append(torch.randn(n_max, generator=gen))                           # distinct
+    rows.append(torch.randint(0, 5, (n_max,), generator=gen).float())        # heavy ties
+    rows.append(torch.full((n_max,), 3.25))                                  # all equal
+    z = torch.zeros(n_max)
+    z[::2] = -0.0
+    z[::7] = -1.0
+    rows.append(z)                                                           # signed zeros
+    base = torch.ones(n_max)
+    rows.append(torch.nextafter(base, base + 1) + (torch.arange(n_max) % 13) * 2 ** -23)
+    thr = torch.full((n_max,), 5.0)                                          # > 64 tied keys
+    thr[: n_max // 10] = 9.0 + torch.rand(n_max // 10, generator=gen)
+    thr[n_max // 2:] = -torch.rand(n_max - n_max // 2, generator=gen)
+    rows.append(thr[torch.randperm(n_max, generator=gen)])
+    rows.append(torch.randn(n_max, generator=gen) * 1e30)                    # wide range
+    rows.append(torch.randn(n_max, generator=gen) * 1e-3 + 100.0)            # narrow range
+    return rows
+
+
+@pytest.mark.parametrize("n_max,P", [(64, 16), (300, 16), (2050, 32), (8008, 16)])
+def test_topk_exact(n_max, P, gpu_lib):
+    gen = torch.Generator().manual_seed(5000 + n_max)
+    rows = _topk_rows(n_max, gen)
+    Hkv = 2
+    B = (len(rows) + 1) // 2
+    while len(rows) < B * Hkv:
+        rows.append(torch.randn(n_max, generator=gen))
+    scores = torch.stack(rows).reshape(B, Hkv, n_max).contiguous()
+    # request lengths and budgets exercise k = 1, n-1, n, n+1, truncation by max_k
+    ctx_choices = [n_max * P, n_max * P - P + 1, 1, P + 1, (n_max // 2) * P, n_max * P - 3]
+    bud_choices = [3 * P, (n_max - 1) * P, 5, 0, n_max * P * 2, P * (n_max // 3) + 7]
+    ctx = torch.tensor([ctx_choices[b % 6] for b in range(B)], dtype=torch.int32)
+    bud = torch.tensor([bud_choices[b % 6] for b in range(B)], dtype=torch.int32)
+    max_k = max(1, n_max - 2)          # caps the budget-covers-all rows
+    L = quest.make_layout(8 * Hkv, Hkv, 128, P, torch.bfloat16, 1, n_max)
+    sel = torch.full((B, Hkv, max_k), 12345, dtype=torch.int32, device=DEV)
+    nsel = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
+    quest.quest_topk_pages(L, scores.to(DEV), ctx.to(DEV), bud.to(DEV), max_k, sel, nsel)
+    torch.cuda.synchronize()
+    sel, nsel = sel.cpu().numpy(), nsel.cpu().numpy()
+    s64 = scores.double().numpy()
+    for b in range(B):
+        n = min(-(-int(ctx[b]) // P), n_max)
+        k = min(oracle.pages_for_budget(int(bud[b]), int(ctx[b]), P), max_k)
+        for g in range(Hkv):
+            want = oracle.select(np.ascontiguousarray(s64[b, g, :n]), k)
+            assert nsel[b, g] == k, (b, g)
+            assert np.array_equal(sel[b, g, :k], want), (b, g, n, k)
+            assert np.all(sel[b, g, k:] == -1)
+
+
+def test_topk_empty_request(gpu_lib):
+    L = quest.make_layout(8, 1, 128, 16, torch.bfloat16, 1, 10)
+    scores = torch.randn((2, 1, 10), device=DEV)
+    ctx = torch.tensor([0, 5], dtype=torch.int32, device=DEV)
+    bud = torch.tensor([64, 64], dtype=torch.int32, device=DEV)
+    sel = torch.full((2, 1, 4), 9, dtype=torch.int32, device=DEV)
+    nsel = torch.full((2, 1), 9, dtype=torch.int32, device=DEV)
+    quest.quest_topk_pages(L, scores, ctx, bud, 4, sel, nsel)
+    torch.cuda.synchronize()
+    assert nsel.cpu().tolist() == [[0], [1]]
+    assert sel[0].cpu().tolist() == [[-1, -1, -1, -1]]
+    assert sel[1].cpu().tolist() == [[0, -1, -1, -1]]
+
+
+def test_deterministic_and_budget_covering_all_is_dense(gpu_lib):
+    w = scaled(WORKLOADS["layer32k"], batch=2, ctx=1000, budget_tokens=10 ** 6, steps=1)
+    lay = Layer(w, DEV)
+    q, k_new, v_new = lay.step_inputs(0)
+    lay.append_step(k_new, v_new)
+    n = -(-1001 // 16)
+    outs = []
+    for _ in range(2):
+        bufs = lay.buffers(max_k=n)
+        lay.view(q, bufs)
+        lay.attend(q, bufs)
+        torch.cuda.synchronize()
+        assert torch.equal(bufs.num_sel.cpu(), torch.full((2, 4), n, dtype=torch.int32))
+        outs.append(bufs.out.clone())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    sm = workloads.default_sm_scale(w)
+    for r in range(2):
+        dense = oracle.request_dense(lay.shape, np.ascontiguousarray(to_oracle(q[r])),
+                                     lay.host[0], lay.host[1], lay.pt_host[r], 1001, sm)
+        check_out(to_f64(outs[0][r]), dense, torch.bfloat16, "dense")
+
+
+def test_split_count_invariance(gpu_lib):
+    """Changing max_k changes the split plan; outputs stay within tolerance."""
+    w = scaled(WORKLOADS["layer32k"], batch=2, ctx=8000, budget_tokens=1024, steps=1)
+    lay = Layer(w, DEV, host=False)
+    q, k_new, v_new = lay.step_inputs(0)
+    lay.append_step(k_new, v_new)
+    results = []
+    for max_k in (64, 200, 501):
+        bufs = lay.buffers(max_k=max_k)
+        plan = quest.quest_sparse_decode_plan(lay.L, w.batch, max_k)
+        lay.view(q, bufs)
+        lay.attend(q, bufs)
+        torch.cuda.synchronize()
+        results.append((plan, to_f64(bufs.out), bufs.sel_pages[:, :, :64].cpu()))
+    assert len({p["num_splits"] for p, _, _ in results}) > 1
+    for _, out, sel in results[1:]:
+        assert torch.equal(sel, results[0][2])
+        check_out(out, results[0][1], torch.bfloat16, "split invariance")
+
+
+def test_full_bench_shape_sampled(gpu_lib):
+    """The benchmark's own shape (batch 8 x 128000, budget 4096), two decode
+    steps, requests 0 and 7 checked against the oracle in full."""
+    w = scaled(WORKLOADS["bench128k"], steps=2)
+    log("full-size benchmark shape: building the cache")
+    lay = Layer(w, DEV)
+    log("cache built")
+    for step in range(w.steps):
+        q, k_new, v_new = lay.step_inputs(step)
+        lay.append_step(k_new, v_new)
+    bufs = lay.buffers()
+    lay.view(q, bufs)
+    lay.attend(q, bufs)
+    torch.cuda.synchronize()
+    km = to_f64(lay.kmeta)
+    scores = bufs.scores.cpu().numpy().astype(np.float64)
+    sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+    out = to_f64(bufs.out)
+    qh = to_f64(q)
+    for r in (0, 7):
+        log(f"oracle request {r}")
+        ref = lay.oracle_request(q, r)
+        check_kmeta(lay, r, ref["bounds"], km)
+        check_scores(scores[r], ref["scores"], qh[r], ref["bounds"], w.group)
+        flags = [compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g], ref["scores"][g])
+                 for g in range(w.num_kv_heads)]
+        assert ref["k"] == 256
+        if "flagged" not in flags:
+            check_out(out[r], ref["out"], torch.bfloat16, f"bench r{r}")
+        log(f"request {r}: selections {flags}")
