@@ -9,9 +9,11 @@ quest_sparse_decode (split-K attention + merge).  Inputs are seeded synthetic
 tensors already resident in HBM.
 
 Timing: W warm-up steps, then K timed steps.  Before each timed step an
-untimed write of a 2 GiB scratch buffer evicts the 256 MB Infinity Cache, so
-the metadata and KV are read from HBM as they would be between layers; HIP
-events on the library's stream bracket each step and each kernel.  value =
+untimed read of a 2 GiB scratch buffer evicts the 256 MB Infinity Cache, so
+the metadata and KV are read from HBM as they would be between layers (a read
+sweep, like the other layers' KV reads, leaves no dirty lines whose write-back
+would compete with the step); a HIP event pair on the library's stream
+brackets each step.  value =
 batch * K / (sum of step times).  A warm number (back-to-back steps, no
 eviction) is reported separately and labelled as cache-assisted.
 
@@ -121,16 +123,57 @@ SCORE_SOURCES = ["kv_cache_decode_quest_amd/csrc/page_scores.hip",
                  "kv_cache_decode_quest_amd/csrc/quest_device.h"]
 
 
-def measured_traffic(kernel_bytes_per_launch):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "page_scores_bench128k_traffic.json")
+COPY_KERNEL = "copy"    # the runtime's buffer-copy kernel: the known-size calibration
+
+
+def measured_traffic():
     """HBM traffic of the scoring kernel from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "page_scores_bench128k_traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    rec = json.load(open(path))
+    rec = json.load(open(TRAFFIC_JSON))
     if rec.get("source_hash") != source_hash(SCORE_SOURCES):
         return None
     return rec.get("bytes_per_launch")
+
+
+def traffic_from_pmc(fetch_csv, write_csv, copy_bytes):
+    """Per-launch HBM bytes of the scoring kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for the calibration copy of copy_bytes (read and
+    written once each)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = "scores" if "page_scores" in name else (
+                COPY_KERNEL if "copyBuffer" in name else None)
+            if key:
+                vals.setdefault(key, []).append(float(row["Counter_Value"]))
+        out = {"scores": sum(vals["scores"]) / len(vals["scores"])}
+        # the calibration copy is by far the largest buffer copy of the run
+        big = sorted(vals[COPY_KERNEL])[-3:]
+        out[COPY_KERNEL] = sum(big) / len(big)
+        return out
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    wr = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / (f[COPY_KERNEL] * 1024.0)
+    w_scale = copy_bytes / (wr[COPY_KERNEL] * 1024.0)
+    fetch_b = f["scores"] * 1024.0 * f_scale
+    write_b = wr["scores"] * 1024.0 * w_scale
+    return {"kernel": "page_scores_mfma_kernel<128>", "workload": "bench128k",
+            "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+            "bytes_per_launch": fetch_b + write_b,
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "raw_fetch_kib": f["scores"], "raw_write_kib": wr["scores"],
+            "copy_fetch_kib": f[COPY_KERNEL], "copy_write_kib": wr[COPY_KERNEL],
+            "copy_bytes": copy_bytes, "source_hash": source_hash(SCORE_SOURCES)}
 
 
 def cpu_baseline(w, layer_inputs, steps_inputs, n_req, n_steps):
@@ -203,9 +246,20 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=8)
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=24)
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--roofline-copies", type=int, default=8)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain copy of this size (counter calibration)")
+    ap.add_argument("--traffic-from-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
+                    help="no GPU: turn two rocprofv3 --pmc runs into the committed traffic record")
     args = ap.parse_args()
+    if args.traffic_from_pmc:
+        fcsv, wcsv, mib = args.traffic_from_pmc
+        rec = traffic_from_pmc(fcsv, wcsv, int(mib) * (1 << 20))
+        json.dump(rec, open(TRAFFIC_JSON, "w"), indent=1)
+        print(json.dumps(rec))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -238,7 +292,10 @@ def main():
     bufs = quest.alloc_decode_buffers(layer.L, w.batch, max_k, dev)
     sm = workloads.default_sm_scale(w)
     plan = quest.quest_sparse_decode_plan(layer.L, w.batch, max_k)
-    flush = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+
+    def evict():
+        torch.sum(flush)
 
     # snapshot the metadata rows the warm-up touches, restore them afterwards
     P = w.page_size
@@ -257,22 +314,26 @@ def main():
     layer.kmeta[touched] = saved
     torch.cuda.synchronize()
 
+    def restore():
+        layer.kmeta[touched] = saved
+
+    # 1. the timed steps: one event pair per step, the cache evicted before each
     log(f"timed: {K} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     sels = torch.empty((K,) + tuple(bufs.sel_pages.shape), dtype=torch.int32, device=dev)
     nsels = torch.empty((K,) + tuple(bufs.num_sel.shape), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for s in range(K):
-        flush.fill_(float(s))
-        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm, events[s])
+        evict()
+        ev_step[s][0].record()
+        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+        ev_step[s][1].record()
         sels[s].copy_(bufs.sel_pages)
         nsels[s].copy_(bufs.num_sel)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    step_ms = [e[0].elapsed_time(e[4]) for e in events]
-    phase_ms = {name: [e[i].elapsed_time(e[i + 1]) for e in events]
-                for i, name in enumerate(["append", "scores", "topk", "decode"])}
+    step_ms = [e[0].elapsed_time(e[1]) for e in ev_step]
     total_s = sum(step_ms) / 1e3
     value = w.batch * K / total_s
 
@@ -282,18 +343,57 @@ def main():
         meta_b += m
         kv_b += kv
     gbps = (meta_b + kv_b) / total_s / 1e9
-    score_us = sum(phase_ms["scores"]) / K * 1e3
-    score_bytes = meta_b / K
-    score_gbps = score_bytes / (score_us * 1e-6) / 1e9
+
+    # 2. per-kernel breakdown: the same steps again, an event between kernels
+    #    (each event adds a few microseconds of dispatch gap to its interval)
+    restore()
+    ev_k = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        evict()
+        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm, ev_k[s])
+    torch.cuda.synchronize()
+    phase_ms = {name: [e[i].elapsed_time(e[i + 1]) for e in ev_k]
+                for i, name in enumerate(["append", "scores", "topk", "decode"])}
     decode_us = sum(phase_ms["decode"]) / K * 1e3
     decode_gbps = (kv_b / K) / (decode_us * 1e-6) / 1e9
-    traffic = measured_traffic(score_bytes)
+
+    # 3. the dominant kernel alone: page scoring over R copies of the metadata
+    #    (R * 131 MB >> the 256 MB Infinity Cache, so every launch reads HBM),
+    #    launched back to back between one event pair
+    R = args.roofline_copies
+    copies = [layer.kmeta.clone() for _ in range(R)]
+    ctx_last = ctx_a[K - 1]
+    n_launch = max(R, (K // R) * R)
+    for i in range(R):
+        quest.quest_page_scores(layer.L, inputs[0][0], copies[i], layer.pt, ctx_last, bufs.scores)
+    ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev_r[0].record()
+    for i in range(n_launch):
+        quest.quest_page_scores(layer.L, inputs[i % K][0], copies[i % R], layer.pt, ctx_last,
+                                bufs.scores)
+    ev_r[1].record()
+    torch.cuda.synchronize()
+    score_us = ev_r[0].elapsed_time(ev_r[1]) / n_launch * 1e3
+    n_last = (ctx_last.cpu().to(torch.int64) + w.page_size - 1) // w.page_size
+    score_bytes = int(n_last.sum()) * w.num_kv_heads * 2 * w.head_dim * \
+        (2 if w.dtype == "bf16" else 4)
+    score_gbps = score_bytes / (score_us * 1e-6) / 1e9
+    traffic = measured_traffic()
+    if args.calibrate_copy_mib:
+        src = torch.ones(args.calibrate_copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    del copies
 
     warm = None
     if not args.no_warm:
-        # restore the metadata of the pages the timed steps touched, then run
         # the same steps back to back without evicting the cache
-        layer.kmeta[touched] = saved
+        restore()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         ev[0].record()
@@ -338,8 +438,9 @@ def main():
                      "frac": score_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": score_bytes,
-                     "avg_launch_us": score_us},
-        "kernels_us": {k: sum(v) / K * 1e3 for k, v in phase_ms.items()},
+                     "avg_launch_us": score_us, "launches": n_launch,
+                     "metadata_copies": R},
+        "kernels_us_event_bracketed": {k: sum(v) / K * 1e3 for k, v in phase_ms.items()},
         "decode_kernel": {"achieved_gbps": decode_gbps, "plan": plan},
         "wall_s_timed_loop_incl_flush": t_wall,
         "warm": warm,

@@ -173,7 +173,8 @@ size_t quest_sparse_decode_workspace_bytes(const quest_layout *layout,
  * num_sel[r][g]-1].  A head with no token in its view outputs zeros.
  * Split-K: pages are spread over work-groups, each keeps a running max, sum
  * and fp32 accumulator, and a second kernel merges the partials.  The bf16
- * path rounds softmax weights to bf16 for the matrix-core P*V product.
+ * path feeds each fp32 softmax weight to the matrix-core P*V product as the
+ * sum of two bf16 values (about 16 significant bits).
  * workspace: device memory of at least quest_sparse_decode_workspace_bytes;
  * contents on entry do not matter. */
 int quest_sparse_decode(const quest_layout *layout, int32_t batch,

@@ -29,7 +29,7 @@
 
 namespace quest {
 
-constexpr int kScoreTilesPerWave = 4;
+constexpr int kScoreTilesPerWave = 1;
 constexpr int kScoreWaves = 4;
 constexpr int kScorePagesPerBlock = kScoreWaves * kScoreTilesPerWave * 16;
 
@@ -70,59 +70,67 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
   const int base = block * kScorePagesPerBlock;
   if (base >= n) return;
 
-  // A operand: [q- | q+] of head `col` of the group (zero rows past G).
-  bf16x8 a[kChunks];
-  {
-    const uint16_t *qh = q + ((int64_t)r * Hkv * G + (int64_t)g * G + col) * D;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int k0 = c * 32 + grp * 8;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (col < G) w = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
-      uint4 neg, pos;
-      split_signs(w, neg, pos);
-      a[c] = as_bf16x8(k0 < D ? neg : pos);
-    }
-  }
-
   const int32_t *pt = page_table + (int64_t)r * max_pages;
   float *out = scores + ((int64_t)r * Hkv + g) * max_pages;
 
-  // Physical page of this lane's column in each of the wave's tiles.
+  // Metadata row of this lane's page in each of the wave's tiles; pages past
+  // the request (or with an id outside the pool) read physical page 0 and are
+  // never written back.
   int page[kScoreTilesPerWave];
   int64_t row[kScoreTilesPerWave];
 #pragma unroll
   for (int t = 0; t < kScoreTilesPerWave; ++t) {
     page[t] = base + (t * kScoreWaves + wave) * 16 + col;
-    int64_t phys = -1;
-    if (page[t] < n) {
-      phys = pt[page[t]];
-      if (phys >= pool) phys = -1;
-    }
-    row[t] = phys < 0 ? -1 : (phys * Hkv + g) * (2 * D);
+    row[t] = pt[page[t] < n ? page[t] : 0];
   }
-
-  uint4 b[2][kChunks];
+  // q of head `col` of the group.  All loads in this kernel are
+  // unconditional, from clamped in-bounds addresses, with unwanted lanes
+  // masked afterwards: a load under a branch makes the compiler drain every
+  // outstanding load at the join, which would serialise the prefetch.  Order
+  // of issue: page ids, q, then all metadata tiles of the wave.
+  uint4 qw[kChunks];
+  {
+    const int head = col < G ? col : 0;
+    const uint16_t *qh = q + ((int64_t)r * Hkv * G + (int64_t)g * G + head) * D;
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c)
-    b[0][c] = row[0] >= 0 ? *(const uint4 *)(kmeta + row[0] + c * 32 + grp * 8)
-                          : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < kChunks; ++c) {
+      const int k0 = c * 32 + grp * 8;
+      qw[c] = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
+    }
+  }
 
 #pragma unroll
   for (int t = 0; t < kScoreTilesPerWave; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < kScoreTilesPerWave) {
+    const int64_t phys = row[t];
+    const bool ok = page[t] < n && phys >= 0 && phys < pool;
+    row[t] = (ok ? phys * Hkv + g : (int64_t)g) * (2 * D);
+  }
+
+  uint4 b[kScoreTilesPerWave][kChunks];
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c)
-        b[cur ^ 1][c] = row[t + 1] >= 0
-                            ? *(const uint4 *)(kmeta + row[t + 1] + c * 32 + grp * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-    if (base + (t * kScoreWaves + wave) * 16 >= n) continue;   // whole tile empty
+  for (int t = 0; t < kScoreTilesPerWave; ++t)
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      b[t][c] = *(const uint4 *)(kmeta + row[t] + c * 32 + grp * 8);
+
+  // A operand: [q- | q+] (zero rows past G).
+  bf16x8 a[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int k0 = c * 32 + grp * 8;
+    uint4 neg, pos;
+    split_signs(qw[c], neg, pos);
+    uint4 x = k0 < D ? neg : pos;
+    if (col >= G) x = make_uint4(0, 0, 0, 0);
+    a[c] = as_bf16x8(x);
+  }
+
+#pragma unroll
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], as_bf16x8(b[cur][c]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], as_bf16x8(b[t][c]), acc, 0, 0, 0);
     // lane holds page `col`, heads 4*grp .. 4*grp+3: combine the group.
     float v = reduce == 0 ? -__builtin_huge_valf() : 0.f;
 #pragma unroll

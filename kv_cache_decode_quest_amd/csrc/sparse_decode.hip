@@ -21,28 +21,32 @@
 //               consecutive tokens of one channel as 8 contiguous bytes)
 // The result of the first product leaves lane l with head l % 16 and tokens
 // 4*(l/16)..+3, which is exactly the lane's A operand of the second product:
-// softmax weights never leave their registers.  Weights are rounded to bf16
-// for the second product, and the running sum l adds the rounded weights, so
-// the output stays a convex combination of V rows.  Heads past G are zero
-// columns of q^T.
+// softmax weights never leave their registers.  For the second product each
+// fp32 weight is split into two bf16 values hi + lo (lo = the rounding error
+// of hi), and both go through the matrix cores, so the weights keep about 16
+// significant bits instead of bf16's 8.  Heads past G are zero columns of q^T.
 #include "quest_device.h"
 #include "quest_launch.h"
 
 namespace quest {
 
 constexpr int kDecodeWaves = 4;
-constexpr int kTargetWaves = 2048;     // 8 waves per CU on 256 CUs
+constexpr int kMaxSplits = 256;        // per (request, KV head); bounds the merge's LDS
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Pages one wave loads at once: 64 KB of K and V per wave in flight for
+// 16-token pages at D = 128 (fewer for 32-token pages, to fit the registers).
+__host__ __device__ constexpr int pages_per_wave(int P, int D) {
+  return (P * D <= 2048) ? 4 : 2;
+}
 
 DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
   DecodePlan p{1, max_k > 0 ? max_k : 1};
-  const long rows = (long)batch * dm.Hkv;
-  if (rows <= 0 || max_k <= 0) return p;
-  long ppw = (rows * max_k + kTargetWaves - 1) / kTargetWaves;   // pages per wave
-  if (ppw < 1) ppw = 1;
-  if (ppw > 16) ppw = 16;
-  long pps = ppw * kDecodeWaves;
-  if (pps > max_k) pps = max_k;
+  if (batch <= 0 || max_k <= 0) return p;
+  const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
+  long rounds = 1;
+  while ((max_k + per_round * rounds - 1) / (per_round * rounds) > kMaxSplits) ++rounds;
+  const long pps = per_round * rounds;
   p.pages_per_split = (int)pps;
   p.n_split = (int)((max_k + pps - 1) / pps);
   return p;
@@ -82,6 +86,88 @@ __device__ __forceinline__ void load_page(PageRegs<D, P> &pr, const uint16_t *__
   }
 }
 
+// One page of the online softmax for all heads of the group: logits on the
+// matrix cores, running max/sum update, rescale, then P*V on the matrix cores.
+// m and l belong to head `col`; acc rows are heads 4*grp .. 4*grp+3.
+template <int D, int P>
+__device__ __forceinline__ void attend_page(PageRegs<D, P> &cur, int valid,
+                                            const bf16x8 *qop, float scale2, int grp,
+                                            float &m, float &l, f32x4 *acc) {
+  using PR = PageRegs<D, P>;
+  // A partial page's unwritten slots may hold anything (NaN included): zero
+  // their V values, since a zero weight times NaN is still NaN.
+  if (valid < P) {
+#pragma unroll
+    for (int tt = 0; tt < PR::TT; ++tt) {
+      const int t0 = tt * 16 + 4 * grp;
+      const uint32_t mx = (t0 + 0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u);
+      const uint32_t my = (t0 + 2 < valid ? 0x0000ffffu : 0u) | (t0 + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int nt = 0; nt < PR::NT; ++nt) {
+        cur.v[tt][nt].x &= mx;
+        cur.v[tt][nt].y &= my;
+      }
+    }
+  }
+  // logits: lane holds head `col`, tokens tt*16 + 4*grp + e
+  f32x4 s[PR::TT];
+  float pmax = -__builtin_huge_valf();
+#pragma unroll
+  for (int tt = 0; tt < PR::TT; ++tt) {
+    f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < PR::KC; ++c)
+      c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[tt][c]),
+                                                   qop[c], c4, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = tt * 16 + 4 * grp + e;
+      const float x = tok < valid ? c4[e] * scale2 : -__builtin_huge_valf();
+      s[tt][e] = x;
+      pmax = fmaxf(pmax, x);
+    }
+  }
+  pmax = wave_max_xor(pmax, 16);
+  pmax = wave_max_xor(pmax, 32);
+  const float m_new = fmaxf(m, pmax);
+  const float alpha = (m == -__builtin_huge_valf()) ? 0.f : exp2_fast(m - m_new);
+  // weights as a sum of two bf16 values (hi + lo), so the matrix-core
+  // product keeps about 16 significant bits of every weight
+  float psum = 0.f;
+  s16x4 phi[PR::TT], plo[PR::TT];
+#pragma unroll
+  for (int tt = 0; tt < PR::TT; ++tt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = exp2_fast(s[tt][e] - m_new);
+      const uint32_t hb = f32_to_bf16_bits(p);
+      const uint32_t lb = f32_to_bf16_bits(p - bf16_bits_to_f32(hb));
+      psum += p;
+      phi[tt][e] = (short)hb;
+      plo[tt][e] = (short)lb;
+    }
+  }
+  psum += __shfl_xor(psum, 16, kWave);
+  psum += __shfl_xor(psum, 32, kWave);
+  l = l * alpha + psum;
+  m = m_new;
+  // rescale: this lane's accumulator rows are heads 4*grp .. 4*grp+3
+  float a4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a4[e] = __shfl(alpha, 4 * grp + e, kWave);
+#pragma unroll
+  for (int nt = 0; nt < PR::NT; ++nt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[nt][e] *= a4[e];
+#pragma unroll
+    for (int tt = 0; tt < PR::TT; ++tt) {
+      const s16x4 vv = __builtin_bit_cast(s16x4, cur.v[tt][nt]);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[tt], vv, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[tt], vv, acc[nt], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int P>
 __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
     int Hkv, int G, int64_t pool, int max_pages, int max_k, int n_split, int pps,
@@ -90,11 +176,14 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
     const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
     const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
   using PR = PageRegs<D, P>;
+  constexpr int PPW = pages_per_wave(P, D);
   __shared__ float lds_m[kDecodeWaves][16];
   __shared__ float lds_l[kDecodeWaves][16];
   __shared__ float lds_acc[kDecodeWaves][16][D];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave index as a scalar: the page lookups below become scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x % n_split;
   const int row = blockIdx.x / n_split;
@@ -107,17 +196,21 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   const int n = pages_in(ctx, P, max_pages);
   const int32_t *sel = sel_pages + (int64_t)row * max_k;
   const int32_t *pt = page_table + (int64_t)r * max_pages;
+  const int64_t page_elems = (int64_t)P * D;
 
   // q^T operand: column `col` = head, K slots of group `grp` (zero past G).
+  // Loads here and below are unconditional, from clamped in-bounds
+  // addresses: a load under a branch makes the compiler drain every
+  // outstanding load at the join.
   bf16x8 qop[PR::KC];
   {
-    const uint16_t *qh = q + ((int64_t)r * Hkv * G + (int64_t)g * G + col) * D;
+    const uint16_t *qh = q + ((int64_t)r * Hkv * G + (int64_t)g * G + (col < G ? col : 0)) * D;
+    uint4 w[PR::KC];
 #pragma unroll
-    for (int c = 0; c < PR::KC; ++c) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (col < G) w = *(const uint4 *)(qh + c * 32 + grp * 8);
-      qop[c] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int c = 0; c < PR::KC; ++c) w[c] = *(const uint4 *)(qh + c * 32 + grp * 8);
+#pragma unroll
+    for (int c = 0; c < PR::KC; ++c)
+      qop[c] = __builtin_bit_cast(bf16x8, col < G ? w[c] : make_uint4(0, 0, 0, 0));
   }
 
   f32x4 acc[PR::NT];
@@ -126,112 +219,30 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   float m = -__builtin_huge_valf();     // running max of head `col` (base-2 logits)
   float l = 0.f;                        // running sum of head `col`
 
-  const int64_t page_elems = (int64_t)P * D;
-  // Page i of this wave: logical page, physical page, valid tokens.
-  auto page_of = [&](int i, int64_t &phys, int &valid) {
-    const int j = sel[i];
-    phys = -1;
-    valid = 0;
-    if (j >= 0 && j < n) {
-      const int64_t ph = pt[j];
-      if (ph >= 0 && ph < pool) {
-        phys = ph;
-        valid = min(P, ctx - j * P);
-      }
+  // Each round, wave w takes PPW consecutive selected pages; page slots past
+  // the split re-read the split's last page (a cache hit) and are skipped.
+  for (int base = first; base < last; base += kDecodeWaves * PPW) {
+    const int p0 = base + wave * PPW;
+    int64_t phys[PPW];
+    int valid[PPW];
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+      const int i = p0 + u;
+      const int j = sel[i < last ? i : last - 1];
+      const bool jok = j >= 0 && j < n;
+      const int64_t ph = pt[jok ? j : 0];
+      const bool ok = jok && ph >= 0 && ph < pool;
+      phys[u] = ok ? ph : 0;
+      valid[u] = (ok && i < last) ? min(P, ctx - j * P) : 0;
     }
-  };
-
-  int i = first + wave;
-  PR cur, nxt;
-  int64_t phys_c = -1, phys_n = -1;
-  int valid_c = 0, valid_n = 0;
-  if (i < last) {
-    page_of(i, phys_c, valid_c);
-    if (phys_c >= 0)
-      load_page<D, P>(cur, k_cache + (phys_c * Hkv + g) * page_elems,
-                      v_cache + (phys_c * Hkv + g) * page_elems, col, grp);
-  }
-  for (; i < last; i += kDecodeWaves) {
-    const int inext = i + kDecodeWaves;
-    if (inext < last) {
-      page_of(inext, phys_n, valid_n);
-      if (phys_n >= 0)
-        load_page<D, P>(nxt, k_cache + (phys_n * Hkv + g) * page_elems,
-                        v_cache + (phys_n * Hkv + g) * page_elems, col, grp);
-    }
-    if (phys_c >= 0) {
-      // A partial page's unwritten slots may hold anything (NaN included):
-      // zero their V values, since a zero weight times NaN is still NaN.
-      if (valid_c < P) {
+    PR pg[PPW];
 #pragma unroll
-        for (int tt = 0; tt < PR::TT; ++tt) {
-          const int t0 = tt * 16 + 4 * grp;
-          const uint32_t mx = (t0 + 0 < valid_c ? 0x0000ffffu : 0u) |
-                              (t0 + 1 < valid_c ? 0xffff0000u : 0u);
-          const uint32_t my = (t0 + 2 < valid_c ? 0x0000ffffu : 0u) |
-                              (t0 + 3 < valid_c ? 0xffff0000u : 0u);
+    for (int u = 0; u < PPW; ++u)
+      load_page<D, P>(pg[u], k_cache + (phys[u] * Hkv + g) * page_elems,
+                      v_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
 #pragma unroll
-          for (int nt = 0; nt < PR::NT; ++nt) {
-            cur.v[tt][nt].x &= mx;
-            cur.v[tt][nt].y &= my;
-          }
-        }
-      }
-      // logits: lane holds head `col`, tokens tt*16 + 4*grp + e
-      f32x4 s[PR::TT];
-      float pmax = -__builtin_huge_valf();
-#pragma unroll
-      for (int tt = 0; tt < PR::TT; ++tt) {
-        f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < PR::KC; ++c)
-          c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, cur.k[tt][c]), qop[c], c4, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = tt * 16 + 4 * grp + e;
-          const float x = tok < valid_c ? c4[e] * scale2 : -__builtin_huge_valf();
-          s[tt][e] = x;
-          pmax = fmaxf(pmax, x);
-        }
-      }
-      pmax = wave_max_xor(pmax, 16);
-      pmax = wave_max_xor(pmax, 32);
-      const float m_new = fmaxf(m, pmax);
-      const float alpha = (m == -__builtin_huge_valf()) ? 0.f : exp2_fast(m - m_new);
-      float psum = 0.f;
-      s16x4 pop[PR::TT];
-#pragma unroll
-      for (int tt = 0; tt < PR::TT; ++tt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t b = f32_to_bf16_bits(exp2_fast(s[tt][e] - m_new));
-          psum += bf16_bits_to_f32(b);
-          pop[tt][e] = (short)b;
-        }
-      }
-      psum += __shfl_xor(psum, 16, kWave);
-      psum += __shfl_xor(psum, 32, kWave);
-      l = l * alpha + psum;
-      m = m_new;
-      // rescale: this lane's accumulator rows are heads 4*grp .. 4*grp+3
-      float a4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a4[e] = __shfl(alpha, 4 * grp + e, kWave);
-#pragma unroll
-      for (int nt = 0; nt < PR::NT; ++nt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[nt][e] *= a4[e];
-#pragma unroll
-        for (int tt = 0; tt < PR::TT; ++tt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              pop[tt], __builtin_bit_cast(s16x4, cur.v[tt][nt]), acc[nt], 0, 0, 0);
-      }
-    }
-    cur = nxt;
-    phys_c = phys_n;
-    valid_c = valid_n;
-    phys_n = -1;
+    for (int u = 0; u < PPW; ++u)
+      if (valid[u] > 0) attend_page<D, P>(pg[u], valid[u], qop, scale2, grp, m, l, acc);
   }
 
   // merge the waves of this work-group
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) lds_acc[wave][4 * grp + e][nt * 16 + col] = acc[nt][e];
   __syncthreads();
-  float *base = partial + ((int64_t)row * n_split + split) * G * (D + 2);
+  float *out = partial + ((int64_t)row * n_split + split) * G * (D + 2);
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int h = idx / D, d = idx - h * D;
     float M = -__builtin_huge_valf();
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
       a += f * lds_acc[w][h][d];
       L += f * lds_l[w][h];
     }
-    float *ph = base + h * (D + 2);
+    float *ph = out + h * (D + 2);
     ph[d] = a;
     if (d == 0) {
       ph[D] = M;
@@ -375,33 +386,65 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
 
 // ---------------------------------------------------------------------------
 // merge: out[r][h] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+// One work-group per (request, q head), one thread per channel.  The split
+// statistics are read once into LDS; each thread then issues the loads of
+// eight splits at a time from clamped addresses before summing them.
 // ---------------------------------------------------------------------------
+constexpr int kMergeUnroll = 8;
+
 template <typename T>
-__global__ __launch_bounds__(128) void merge_kernel(int Hkv, int G, int D, int max_k,
-                                                    int n_split, int pps,
-                                                    const int32_t *__restrict__ num_sel,
-                                                    const float *__restrict__ partial,
-                                                    T *__restrict__ out) {
+__global__ __launch_bounds__(128) void merge_kernel(
+    int Hkv, int G, int D, int max_k, int n_split, int pps, const int32_t *__restrict__ num_sel,
+    const float *__restrict__ partial, T *__restrict__ out) {
+  __shared__ float w_lds[kMaxSplits];        // split max, then the split's weight
+  __shared__ float l_lds[kMaxSplits];        // split sum
+  __shared__ float red[2];
   const int hq = blockIdx.x;                 // r * Hq + h
   const int Hq = Hkv * G;
   const int r = hq / Hq, h = hq - r * Hq;
   const int g = h / G, hl = h - g * G;
   const int row = r * Hkv + g;
   const int nsel = min(num_sel[row], max_k);
-  const int live = nsel <= 0 ? 0 : (nsel + pps - 1) / pps;
-  const float *base = partial + (int64_t)row * n_split * G * (D + 2) + (int64_t)hl * (D + 2);
+  const int live = nsel <= 0 ? 0 : min((nsel + pps - 1) / pps, n_split);
   const int64_t stride = (int64_t)G * (D + 2);
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < live; ++s) M = fmaxf(M, base[s * stride + D]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float a = 0.f, L = 0.f;
-    for (int s = 0; s < live; ++s) {
-      const float ms = base[s * stride + D];
+  const float *base = partial + (int64_t)row * n_split * stride + (int64_t)hl * (D + 2);
+  for (int s = threadIdx.x; s < live; s += blockDim.x) {
+    w_lds[s] = base[s * stride + D];
+    l_lds[s] = base[s * stride + D + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    float M = -__builtin_huge_valf();
+    for (int s = threadIdx.x; s < live; s += kWave) M = fmaxf(M, w_lds[s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    float L = 0.f;
+    for (int s = threadIdx.x; s < live; s += kWave) {
+      const float ms = w_lds[s];
       const float f = (ms == -__builtin_huge_valf()) ? 0.f : exp2_fast(ms - M);
-      a += f * base[s * stride + d];
-      L += f * base[s * stride + D + 1];
+      w_lds[s] = f;
+      L += f * l_lds[s];
     }
-    Elem<T>::store(out, (int64_t)hq * D + d, L > 0.f ? a / L : 0.f);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, kWave);
+    if (threadIdx.x == 0) red[0] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  const float inv_l = red[0];
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float a = 0.f;
+    for (int s0 = 0; s0 < live; s0 += kMergeUnroll) {
+      float v[kMergeUnroll];
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int s = s0 + u < live ? s0 + u : s0;
+        v[u] = base[s * stride + d];
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u)
+        if (s0 + u < live) a += w_lds[s0 + u] * v[u];
+    }
+    Elem<T>::store(out, (int64_t)hq * D + d, a * inv_l);
   }
 }
 

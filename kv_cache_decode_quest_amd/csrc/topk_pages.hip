@@ -7,15 +7,18 @@
 //     (orderable(score) << 32) | (0xffffffff - page),
 // so the selected set is unique and any exact top-k algorithm returns it.
 //
-// One work-group per row, radix select on the 32-bit orderable score keys:
+// One work-group per row, radix select on the 32-bit orderable score keys
+// (staged in LDS for rows of up to 8192 pages):
 //  1. block min/max of the keys: every key shares the bits above the highest
 //     bit where min and max differ;
-//  2. an (up to) 11-bit histogram on the next bits finds the bucket that holds
-//     the k-th largest key, and how many keys above it are kept outright;
-//  3. the bucket's keys (typically a handful) are gathered into LDS; if they
-//     fit in one wave, each lane ranks its (key, page) pair against the others
-//     in the 64-bit order; otherwise further 8-bit histogram passes over the
-//     row narrow the bucket to a single key value;
+//  2. refinement passes: an (up to) 11-bit histogram of the keys that match
+//     the known prefix, on the next bits, finds the bucket holding the k-th
+//     largest key and how many keys above it are kept outright; the bucket's
+//     bits join the prefix;
+//  3. as soon as the bucket holds at most 64 keys, they are gathered into LDS
+//     and one wave ranks its (key, page) pairs in the 64-bit order, which
+//     fixes the threshold pair; otherwise refinement continues down to the
+//     last bit;
 //  4. a final pass writes the kept pages in ascending order: every page whose
 //     key is above the threshold key, and the lowest-index pages among those
 //     equal to it up to the count still needed.  Each thread owns a
@@ -28,7 +31,9 @@ namespace quest {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kBins1 = 2048;
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+static_assert(kBins == 2 * kTopkThreads, "each thread owns two histogram buckets");
 
 // Larger score <-> larger key; -0.0 and +0.0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -46,62 +51,64 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
   return v;
 }
 
-// Exclusive block scan of one value per thread (kTopkThreads threads).
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) wave_tot[wave] = incl;
-  __syncthreads();
-  uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += wave_tot[w];
-  __syncthreads();
-  return off + incl - v;
-}
-
 struct TopkShared {
-  uint32_t hist[kBins1];
-  uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves];
+  uint32_t hist[kBins];
+  uint32_t wave_tot[kTopkWaves];
   uint32_t cand_key[kWave];
   int32_t cand_idx[kWave];
   uint32_t cand_count;
   uint32_t prefix;     // known high bits of the threshold key
   uint32_t krem;       // keys still to take at or below the known prefix
+  uint32_t bucket;     // keys in the chosen bucket
+  uint32_t lo, hi;
 };
 
-// Finds, in hist[0..bins), the bucket holding the krem-th largest element
-// (buckets scanned from the top).  Wave 0 only.  Returns via sh.
-__device__ void pick_bucket(TopkShared &sh, int bins, uint32_t krem, uint32_t prefix,
-                            int shift) {
-  const int lane = threadIdx.x & 63;
-  const int per = (bins + kWave - 1) / kWave;       // buckets per lane, top first
-  uint32_t tot = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = bins - 1 - (lane * per + i);
-    if (b >= 0) tot += sh.hist[b];
-  }
-  const uint32_t incl = wave_incl_scan(tot, lane);
-  const uint32_t excl = incl - tot;
-  if (excl < krem && krem <= incl) {
-    uint32_t cum = excl;
-    for (int i = 0; i < per; ++i) {
-      const int b = bins - 1 - (lane * per + i);
-      if (b < 0) break;
-      const uint32_t c = sh.hist[b];
-      if (cum + c >= krem) {
-        sh.prefix = prefix | ((uint32_t)b << shift);
-        sh.krem = krem - cum;
-        break;
-      }
-      cum += c;
-    }
-  }
+// Inclusive scan over the block in thread order.  Ends with a barrier, so
+// wave_tot may be reused right after.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, TopkShared &sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) sh.wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0;
+  for (int w = 0; w < wave; ++w) off += sh.wave_tot[w];
+  __syncthreads();
+  return off + incl;
 }
 
+// The bucket (of `bins`) that holds the krem-th largest counted key, scanning
+// buckets from the top; thread t owns buckets bins-1-2t and bins-2-2t, read
+// from consecutive LDS words.  Results in sh.prefix / sh.krem / sh.bucket.
+__device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t krem,
+                                            uint32_t prefix, int shift) {
+  const int b1 = bins - 1 - 2 * (int)threadIdx.x, b0 = b1 - 1;
+  const uint32_t c1 = b1 >= 0 ? sh.hist[b1] : 0u;
+  const uint32_t c0 = b0 >= 0 ? sh.hist[b0] : 0u;
+  const uint32_t incl = block_incl_scan(c1 + c0, sh);
+  const uint32_t excl = incl - c1 - c0;
+  if (excl < krem && krem <= incl) {
+    const bool upper = excl + c1 >= krem;
+    const int b = upper ? b1 : b0;
+    sh.prefix = prefix | ((uint32_t)b << shift);
+    sh.krem = krem - (upper ? excl : excl + c1);
+    sh.bucket = upper ? c1 : c0;
+  }
+  __syncthreads();
+}
+
+// Rows of up to kStagedKeys pages are read from HBM once, into LDS, as
+// orderable keys; every later pass reads LDS.  Longer rows read their scores
+// from global memory in every pass.
+constexpr int kStagedKeys = 8192;
+constexpr int kLoadUnroll = kStagedKeys / kTopkThreads;
+
+template <bool kStaged>
 __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     int Hkv, int P, int max_pages, int max_k, const float *__restrict__ scores,
     const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ budget_tokens,
     int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel) {
   __shared__ TopkShared sh;
+  __shared__ uint32_t staged[kStaged ? kStagedKeys : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   const int r = row / Hkv;
@@ -120,71 +127,109 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
     return;
   }
+  auto key = [&](int j) -> uint32_t {
+    if constexpr (kStaged) return staged[j];
+    else return order_key(s[j]);
+  };
 
-  // 1. min and max key
+  // 1. min and max key (and, for short rows, the keys into LDS: all loads of
+  //    a thread are issued together from clamped addresses)
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int j = tid; j < n; j += kTopkThreads) {
-    const uint32_t u = order_key(s[j]);
-    lo = min(lo, u);
-    hi = max(hi, u);
+  if constexpr (kStaged) {
+    float v[kLoadUnroll];
+#pragma unroll
+    for (int i = 0; i < kLoadUnroll; ++i) {
+      const int j = tid + i * kTopkThreads;
+      v[i] = s[j < n ? j : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadUnroll; ++i) {
+      const int j = tid + i * kTopkThreads;
+      const uint32_t u = order_key(v[i]);
+      if (j < n) {
+        staged[j] = u;
+        lo = min(lo, u);
+        hi = max(hi, u);
+      }
+    }
+  } else {
+    for (int j = tid; j < n; j += kTopkThreads) {
+      const uint32_t u = order_key(s[j]);
+      lo = min(lo, u);
+      hi = max(hi, u);
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     lo = min(lo, (uint32_t)__shfl_xor(lo, o, kWave));
     hi = max(hi, (uint32_t)__shfl_xor(hi, o, kWave));
   }
-  if (lane == 0) {
-    sh.wave_a[wave] = lo;
-    sh.wave_b[wave] = hi;
+  if (tid == 0) {
+    sh.lo = 0xffffffffu;
+    sh.hi = 0u;
+    sh.cand_count = 0;
   }
-  for (int i = tid; i < kBins1; i += kTopkThreads) sh.hist[i] = 0;
-  if (tid == 0) sh.cand_count = 0;
+  sh.hist[2 * tid] = 0;
+  sh.hist[2 * tid + 1] = 0;
   __syncthreads();
-  lo = sh.wave_a[0];
-  hi = sh.wave_b[0];
-  for (int w = 1; w < kTopkWaves; ++w) {
-    lo = min(lo, sh.wave_a[w]);
-    hi = max(hi, sh.wave_b[w]);
+  if (lane == 0) {
+    atomicMin(&sh.lo, lo);
+    atomicMax(&sh.hi, hi);
   }
+  __syncthreads();
+  lo = sh.lo;
+  hi = sh.hi;
 
-  uint32_t thresh, krem;
+  uint32_t thresh, krem = (uint32_t)k;
   if (lo == hi) {                                     // every key equal
     thresh = lo;
-    krem = (uint32_t)k;
   } else {
-    // 2. first histogram on the bits just below the common prefix
+    // 2./3. refine the threshold key, 11 bits at a time
     const int hb = 31 - __builtin_clz(lo ^ hi);
-    const int shift1 = hb >= 10 ? hb - 10 : 0;
-    const int bins = 1 << (hb - shift1 + 1);
-    const uint32_t bmask = (uint32_t)bins - 1u;
-    for (int j = tid; j < n; j += kTopkThreads) {
-      const uint32_t u = order_key(s[j]);
-      atomicAdd(&sh.hist[(u >> shift1) & bmask], 1u);
-    }
-    __syncthreads();
-    const uint32_t common = (hb == 31) ? 0u : (hi >> (hb + 1)) << (hb + 1);
-    if (wave == 0) pick_bucket(sh, bins, (uint32_t)k, common, shift1);
-    __syncthreads();
-    uint32_t prefix = sh.prefix;
-    krem = sh.krem;
-    int lowbit = shift1;             // bits >= lowbit of the threshold are known
-
-    // 3. gather the bucket's keys; rank them in one wave if they fit
-    if (lowbit > 0) {
+    int lowbit = hb + 1;                              // bits >= lowbit are known
+    uint32_t prefix = (uint32_t)(((uint64_t)hi >> lowbit) << lowbit);
+    bool first_pass = true;
+    for (;;) {
+      const int w = lowbit < kDigitBits ? lowbit : kDigitBits;
+      const int shift = lowbit - w;
+      const uint32_t bmask = (1u << w) - 1u;
+      if (!first_pass) {
+        sh.hist[2 * tid] = 0;
+        sh.hist[2 * tid + 1] = 0;
+        __syncthreads();
+      }
+      first_pass = false;
+      const uint64_t want = (uint64_t)prefix >> lowbit;
       for (int j = tid; j < n; j += kTopkThreads) {
-        const uint32_t u = order_key(s[j]);
-        if ((u >> lowbit) == (prefix >> lowbit)) {
-          const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
-          if (slot < (uint32_t)kWave) {
-            sh.cand_key[slot] = u;
-            sh.cand_idx[slot] = j;
-          }
-        }
+        const uint32_t u = key(j);
+        if (((uint64_t)u >> lowbit) == want) atomicAdd(&sh.hist[(u >> shift) & bmask], 1u);
       }
       __syncthreads();
-      const uint32_t c = sh.cand_count;
-      if (c <= (uint32_t)kWave) {
+      pick_bucket(sh, 1 << w, krem, prefix, shift);
+      prefix = sh.prefix;
+      krem = sh.krem;
+      const uint32_t count = sh.bucket;
+      lowbit = shift;
+      if (lowbit == 0) {                              // the threshold key itself
+        thresh = prefix;
+        break;
+      }
+      if (count <= (uint32_t)kWave) {
+        // gather the bucket and rank it in one wave
+        const uint32_t want2 = prefix >> lowbit;
+        for (int j = tid; j < n; j += kTopkThreads) {
+          const uint32_t u = key(j);
+          if ((u >> lowbit) == want2) {
+            const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
+            if (slot < (uint32_t)kWave) {
+              sh.cand_key[slot] = u;
+              sh.cand_idx[slot] = j;
+            }
+          }
+        }
+        __syncthreads();
         if (wave == 0) {
+          const uint32_t c = count;
           const bool mine = (uint32_t)lane < c;
           const uint64_t me = mine ? (((uint64_t)sh.cand_key[lane] << 32) |
                                       (0xffffffffu - (uint32_t)sh.cand_idx[lane]))
@@ -207,48 +252,38 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
           }
         }
         __syncthreads();
-        prefix = sh.prefix;
+        thresh = sh.prefix;
         krem = sh.krem;
-        lowbit = 0;
+        break;
       }
     }
-    // 3b. many keys in the bucket: narrow it 8 bits at a time over the row
-    while (lowbit > 0) {
-      const int w = lowbit < 8 ? lowbit : 8;
-      const int shift = lowbit - w;
-      const uint32_t wmask = (1u << w) - 1u;
-      for (int i = tid; i < (1 << w); i += kTopkThreads) sh.hist[i] = 0;
-      __syncthreads();
-      for (int j = tid; j < n; j += kTopkThreads) {
-        const uint32_t u = order_key(s[j]);
-        if ((u >> lowbit) == (prefix >> lowbit)) atomicAdd(&sh.hist[(u >> shift) & wmask], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) pick_bucket(sh, 1 << w, krem, prefix, shift);
-      __syncthreads();
-      prefix = sh.prefix;
-      krem = sh.krem;
-      lowbit = shift;
-    }
-    thresh = prefix;
   }
 
   // 4. ascending output: keys above the threshold, then the first `krem`
-  //    pages whose key equals it.
+  //    pages whose key equals it.  One scan of (above, equal) counts packed
+  //    in 16-bit halves when the row fits, two scans otherwise.
   const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
   const int j0 = tid * chunk;
   const int j1 = min(n, j0 + chunk);
   uint32_t gt = 0, eq = 0;
   for (int j = j0; j < j1; ++j) {
-    const uint32_t u = order_key(s[j]);
+    const uint32_t u = key(j);
     gt += u > thresh;
     eq += u == thresh;
   }
-  const uint32_t gt_before = block_excl_scan(gt, sh.wave_a);
-  uint32_t eq_before = block_excl_scan(eq, sh.wave_b);
+  uint32_t gt_before, eq_before;
+  if (n < 65536) {
+    const uint32_t packed = (gt << 16) | eq;
+    const uint32_t before = block_incl_scan(packed, sh) - packed;
+    gt_before = before >> 16;
+    eq_before = before & 0xffffu;
+  } else {
+    gt_before = block_incl_scan(gt, sh) - gt;
+    eq_before = block_incl_scan(eq, sh) - eq;
+  }
   uint32_t pos = gt_before + min(eq_before, krem);
   for (int j = j0; j < j1; ++j) {
-    const uint32_t u = order_key(s[j]);
+    const uint32_t u = key(j);
     const bool take = u > thresh || (u == thresh && eq_before++ < krem);
     if (take) {
       if (pos < (uint32_t)k) out[pos] = j;      // never past the row
@@ -262,9 +297,14 @@ hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        int max_k, int32_t *sel_pages, int32_t *num_sel,
                        hipStream_t stream) {
   dim3 grid((unsigned)(batch * dm.Hkv));
-  hipLaunchKernelGGL(topk_pages_kernel, grid, dim3(kTopkThreads), 0, stream, dm.Hkv, dm.P,
-                     dm.max_pages, max_k, scores, ctx_lens, budget_tokens, sel_pages,
-                     num_sel);
+  if (dm.max_pages <= kStagedKeys)
+    hipLaunchKernelGGL(topk_pages_kernel<true>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
+                       dm.P, dm.max_pages, max_k, scores, ctx_lens, budget_tokens, sel_pages,
+                       num_sel);
+  else
+    hipLaunchKernelGGL(topk_pages_kernel<false>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
+                       dm.P, dm.max_pages, max_k, scores, ctx_lens, budget_tokens, sel_pages,
+                       num_sel);
   return hipGetLastError();
 }
 
