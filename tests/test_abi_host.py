@@ -140,13 +140,17 @@ def test_workspace_contract(lib):
 
 
 def test_plan_covers_every_page():
+    """Splits cover max_k pages with no empty split, and never exceed the 256
+    splits the merge kernel holds in LDS."""
     for batch, hkv, max_k in [(1, 1, 1), (1, 1, 16), (8, 4, 256), (8, 4, 128), (32, 4, 409),
-                              (64, 4, 128), (3, 2, 1000)]:
-        L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8)
-        p = quest.quest_sparse_decode_plan(L, batch, max_k)
-        assert 1 <= p["pages_per_split"] <= max_k
-        assert (p["num_splits"] - 1) * p["pages_per_split"] < max_k
-        assert p["num_splits"] * p["pages_per_split"] >= max_k
+                              (64, 4, 128), (3, 2, 1000), (1, 1, 60000), (2, 4, 4097)]:
+        for page_size in (16, 32):
+            L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8, page_size=page_size)
+            p = quest.quest_sparse_decode_plan(L, batch, max_k)
+            assert p["pages_per_split"] >= 1
+            assert 1 <= p["num_splits"] <= 256
+            assert (p["num_splits"] - 1) * p["pages_per_split"] < max_k
+            assert p["num_splits"] * p["pages_per_split"] >= max_k
 
 
 def test_missing_library_fails_loudly(tmp_path):
