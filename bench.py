@@ -3,8 +3,8 @@
 Workload (default "bench128k"): one Qwen3-30B-A3B-class attention layer
 (32 q / 4 KV heads, head_dim 128, bf16), batch 8, 128000-token contexts in a
 paged cache (page 16), token budget 4096 (256 pages per KV head).  A step is
-the whole hot path for one new token per request: quest_append_kv (KV store +
-fused min/max refresh), quest_page_scores, quest_topk_pages and
+the whole hot path for one new token per request: quest_append_score (KV store
+and min/max refresh fused with the page scores), quest_topk_pages and
 quest_sparse_decode (split-K attention + merge).  Inputs are seeded synthetic
 tensors already resident in HBM.
 
@@ -79,12 +79,10 @@ def run_step(layer, bufs, s, inp, ctx_before, ctx_after, budgets, sm, events=Non
     L = layer.L
     if events:
         events[0].record()
-    quest.quest_append_kv(L, k_new, v_new, layer.cu1, ctx_before, 1, layer.pt, layer.k_cache,
-                          layer.v_cache, layer.kmeta)
+    quest.quest_append_score(L, q, k_new, v_new, layer.cu1, ctx_before, 1, layer.pt,
+                             layer.k_cache, layer.v_cache, layer.kmeta, bufs.scores)
     if events:
         events[1].record()
-    quest.quest_page_scores(L, q, layer.kmeta, layer.pt, ctx_after, bufs.scores)
-    if events:
         events[2].record()
     quest.quest_topk_pages(L, bufs.scores, ctx_after, budgets, bufs.max_k, bufs.sel_pages,
                            bufs.num_sel)
@@ -95,6 +93,64 @@ def run_step(layer, bufs, s, inp, ctx_before, ctx_after, budgets, sm, events=Non
                               bufs.workspace)
     if events:
         events[4].record()
+
+
+class Stepper:
+    """Issues decode steps for the whole batch, split by request into
+    contiguous chunks, one chunk per HIP stream (default priority).  Chunks
+    are independent requests, so the latency-bound kernels of one chunk
+    (append, top-k, merge) overlap the HBM-bound kernels of another."""
+
+    def __init__(self, layer, max_k, n_streams, dev):
+        B = layer.w.batch
+        n_streams = max(1, min(n_streams, B))
+        edges = [round(i * B / n_streams) for i in range(n_streams + 1)]
+        self.chunks = [(edges[i], edges[i + 1]) for i in range(n_streams)]
+        self.layer = layer
+        self.streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(n_streams - 1)]
+        self.bufs = [quest.alloc_decode_buffers(layer.L, r1 - r0, max_k, dev)
+                     for r0, r1 in self.chunks]
+        self.cu1 = [torch.arange(r1 - r0 + 1, dtype=torch.int32, device=dev)
+                    for r0, r1 in self.chunks]
+        self.start = torch.cuda.Event()
+        self.done = [torch.cuda.Event() for _ in self.chunks]
+        self.max_k = max_k
+
+    def _chunk(self, c, inp, ctx_before, ctx_after, budgets, sm):
+        r0, r1 = self.chunks[c]
+        lay, L, b = self.layer, self.layer.L, self.bufs[c]
+        q, k_new, v_new = (x[r0:r1] for x in inp)
+        pt = lay.pt[r0:r1]
+        ca, cb, bud = ctx_after[r0:r1], ctx_before[r0:r1], budgets[r0:r1]
+        quest.quest_append_score(L, q, k_new, v_new, self.cu1[c], cb, 1, pt, lay.k_cache,
+                                 lay.v_cache, lay.kmeta, b.scores)
+        quest.quest_topk_pages(L, b.scores, ca, bud, b.max_k, b.sel_pages, b.num_sel)
+        quest.quest_sparse_decode(L, q, lay.k_cache, lay.v_cache, pt, ca, b.sel_pages,
+                                  b.num_sel, b.max_k, sm, b.out, b.workspace)
+
+    def step(self, inp, ctx_before, ctx_after, budgets, sm):
+        if len(self.chunks) == 1:
+            self._chunk(0, inp, ctx_before, ctx_after, budgets, sm)
+            return
+        main = torch.cuda.current_stream()
+        self.start.record(main)
+        for c in range(len(self.chunks)):
+            st = main if c == 0 else self.streams[c]
+            if c > 0:
+                st.wait_event(self.start)
+            with torch.cuda.stream(st):
+                self._chunk(c, inp, ctx_before, ctx_after, budgets, sm)
+            if c > 0:
+                self.done[c].record(st)
+        for c in range(1, len(self.chunks)):
+            main.wait_event(self.done[c])
+
+    def record_selection(self, sels, nsels):
+        """Copy the last step's selections into full-batch tensors (main stream,
+        after step() has joined the chunk streams)."""
+        for (r0, r1), b in zip(self.chunks, self.bufs):
+            sels[r0:r1].copy_(b.sel_pages)
+            nsels[r0:r1].copy_(b.num_sel)
 
 
 def step_bytes(w, ctx_after, sel, nsel):
@@ -120,6 +176,7 @@ def source_hash(files):
 
 
 SCORE_SOURCES = ["kv_cache_decode_quest_amd/csrc/page_scores.hip",
+                 "kv_cache_decode_quest_amd/csrc/append_inline.h",
                  "kv_cache_decode_quest_amd/csrc/quest_device.h"]
 
 
@@ -167,7 +224,7 @@ def traffic_from_pmc(fetch_csv, write_csv, copy_bytes):
     w_scale = copy_bytes / (wr[COPY_KERNEL] * 1024.0)
     fetch_b = f["scores"] * 1024.0 * f_scale
     write_b = wr["scores"] * 1024.0 * w_scale
-    return {"kernel": "page_scores_mfma_kernel<128>", "workload": "bench128k",
+    return {"kernel": "page_scores_mfma_kernel<128, true>", "workload": "bench128k",
             "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
             "bytes_per_launch": fetch_b + write_b,
             "fetch_scale": f_scale, "write_scale": w_scale,
@@ -249,6 +306,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=24)
     ap.add_argument("--no-warm", action="store_true")
     ap.add_argument("--roofline-copies", type=int, default=8)
+    ap.add_argument("--streams", type=int, default=1,
+                    help="split the batch by request over this many HIP streams")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain copy of this size (counter calibration)")
     ap.add_argument("--traffic-from-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
@@ -307,9 +366,10 @@ def main():
     touched = torch.tensor(sorted(set(touched)), dtype=torch.int64, device=dev)
     saved = layer.kmeta[touched].clone()
 
-    log(f"warm-up: {W} steps")
+    stepper = Stepper(layer, max_k, args.streams, dev)
+    log(f"warm-up: {W} steps ({len(stepper.chunks)} stream(s))")
     for s in range(W):
-        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+        stepper.step(inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
     torch.cuda.synchronize()
     layer.kmeta[touched] = saved
     torch.cuda.synchronize()
@@ -327,10 +387,9 @@ def main():
     for s in range(K):
         evict()
         ev_step[s][0].record()
-        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+        stepper.step(inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
         ev_step[s][1].record()
-        sels[s].copy_(bufs.sel_pages)
-        nsels[s].copy_(bufs.num_sel)
+        stepper.record_selection(sels[s], nsels[s])
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     step_ms = [e[0].elapsed_time(e[1]) for e in ev_step]
@@ -354,29 +413,36 @@ def main():
         run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm, ev_k[s])
     torch.cuda.synchronize()
     phase_ms = {name: [e[i].elapsed_time(e[i + 1]) for e in ev_k]
-                for i, name in enumerate(["append", "scores", "topk", "decode"])}
+                for i, name in [(0, "append_score"), (2, "topk"), (3, "decode")]}
     decode_us = sum(phase_ms["decode"]) / K * 1e3
     decode_gbps = (kv_b / K) / (decode_us * 1e-6) / 1e9
 
-    # 3. the dominant kernel alone: page scoring over R copies of the metadata
-    #    (R * 131 MB >> the 256 MB Infinity Cache, so every launch reads HBM),
-    #    launched back to back between one event pair
+    # 3. the dominant kernel alone: the fused append + page-scoring kernel over
+    #    R copies of the metadata (R * 131 MB >> the 256 MB Infinity Cache, so
+    #    every launch reads HBM), launched back to back between one event pair.
+    #    Re-appending the same token is idempotent, so every launch does the
+    #    same work as the first step's.
     R = args.roofline_copies
+    restore()
     copies = [layer.kmeta.clone() for _ in range(R)]
-    ctx_last = ctx_a[K - 1]
+    q0, k0, v0 = inputs[0]
     n_launch = max(R, (K // R) * R)
+
+    def fused(i):
+        quest.quest_append_score(layer.L, q0, k0, v0, layer.cu1, ctx_b[0], 1, layer.pt,
+                                 layer.k_cache, layer.v_cache, copies[i % R], bufs.scores)
+
     for i in range(R):
-        quest.quest_page_scores(layer.L, inputs[0][0], copies[i], layer.pt, ctx_last, bufs.scores)
+        fused(i)
     ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev_r[0].record()
     for i in range(n_launch):
-        quest.quest_page_scores(layer.L, inputs[i % K][0], copies[i % R], layer.pt, ctx_last,
-                                bufs.scores)
+        fused(i)
     ev_r[1].record()
     torch.cuda.synchronize()
     score_us = ev_r[0].elapsed_time(ev_r[1]) / n_launch * 1e3
-    n_last = (ctx_last.cpu().to(torch.int64) + w.page_size - 1) // w.page_size
+    n_last = (ctx_a[0].cpu().to(torch.int64) + w.page_size - 1) // w.page_size
     score_bytes = int(n_last.sum()) * w.num_kv_heads * 2 * w.head_dim * \
         (2 if w.dtype == "bf16" else 4)
     score_gbps = score_bytes / (score_us * 1e-6) / 1e9
@@ -398,7 +464,7 @@ def main():
         torch.cuda.synchronize()
         ev[0].record()
         for s in range(K):
-            run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+            stepper.step(inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
         ev[1].record()
         torch.cuda.synchronize()
         warm_s = ev[0].elapsed_time(ev[1]) / 1e3
@@ -433,7 +499,8 @@ def main():
         "hbm_gbps": gbps,
         "hbm_frac_peak": gbps / PEAK_HBM_GBPS,
         "bytes_per_step": {"metadata": meta_b / K, "selected_kv": kv_b / K},
-        "roofline": {"kernel": "page_scores_mfma_kernel<128>", "bound": "hbm",
+        "roofline": {"kernel": "page_scores_mfma_kernel<128, true> (append + scores)",
+                     "bound": "hbm",
                      "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": score_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic,
@@ -442,6 +509,8 @@ def main():
                      "metadata_copies": R},
         "kernels_us_event_bracketed": {k: sum(v) / K * 1e3 for k, v in phase_ms.items()},
         "decode_kernel": {"achieved_gbps": decode_gbps, "plan": plan},
+        "launch": {"streams": len(stepper.chunks),
+                   "requests_per_stream": [r1 - r0 for r0, r1 in stepper.chunks]},
         "wall_s_timed_loop_incl_flush": t_wall,
         "warm": warm,
         "cpu_baseline": cpu,

@@ -21,6 +21,7 @@
  * those steps:
  *     quest_append_kv      on_kv_stored: KV store + fused min/max refresh
  *     quest_page_scores    build_decode_view, part 1: per-page bounds from q
+ *     quest_append_score   the two above fused into one pass
  *     quest_topk_pages     build_decode_view, part 2: top-k within the budget
  *     quest_sparse_decode  attention over the selected explicit-KV view
  *
@@ -148,6 +149,21 @@ int quest_page_scores(const quest_layout *layout, int32_t batch,
                       const void *q, const void *kmeta,
                       const int32_t *page_table, const int32_t *ctx_lens,
                       int32_t group_reduce, float *scores, void *stream);
+
+/* on_kv_stored followed by build_decode_view part 1, in one pass: exactly
+ * quest_append_kv(layout, batch, k_new, v_new, cu_new, ctx_before,
+ * max_new_per_seq, page_table, k_cache, v_cache, kmeta) then
+ * quest_page_scores(layout, batch, q, kmeta, page_table, ctx_lens,
+ * group_reduce, scores) with ctx_lens[r] = ctx_before[r] + (cu_new[r+1] -
+ * cu_new[r]).  On bf16 it is one kernel: the scoring work-group that owns a
+ * touched page stores the new tokens and refreshes the page's min/max first,
+ * so the metadata is read once.  Arguments and layouts as in those two
+ * calls. */
+int quest_append_score(const quest_layout *layout, int32_t batch, const void *q,
+                       const void *k_new, const void *v_new, const int32_t *cu_new,
+                       const int32_t *ctx_before, int32_t max_new_per_seq,
+                       const int32_t *page_table, void *k_cache, void *v_cache,
+                       void *kmeta, int32_t group_reduce, float *scores, void *stream);
 
 /* build_decode_view, part 2: k_r = min(max_k, clamp(floor(budget_tokens[r] /
  * P), 1, n_r)) pages per (request, KV head), n_r = ceil(ctx_lens[r]/P);

@@ -6,12 +6,9 @@
 // written.  The metadata is Quest's per-page elementwise key min and max.
 //
 // One work-group owns one touched page of one request, so every metadata row
-// has exactly one writer.  Threads walk the page's (KV head, channel) pairs;
-// each thread scans that channel of the page's new tokens in position order.
-// The comparisons are strict (x < lo, x > hi), which keeps the first-seen
-// value among equal ones: the incremental result equals a from-scratch scan
-// of the page in position order bit for bit, signed zeros included.
-#include "quest_device.h"
+// has exactly one writer; its threads walk the page's (KV head, channel)
+// pairs (append_inline.h holds the per-channel body).
+#include "append_inline.h"
 #include "quest_launch.h"
 
 namespace quest {
@@ -38,34 +35,10 @@ __global__ __launch_bounds__(256) void append_kv_kernel(
     if (page >= max_pages) break;
     const int64_t phys = pt[page];
     if (phys < 0 || phys >= pool) continue;
-    const int lo_pos = max(p0, page * P);
-    const int hi_pos = min(p1, (page + 1) * P);
-    const bool fresh = (lo_pos == page * P);   // first new token at slot 0
     for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
       const int g = e / D, d = e - g * D;
-      const int64_t head = phys * Hkv + g;
-      float lo, hi;
-      if (fresh) {
-        lo = __builtin_huge_valf();
-        hi = -__builtin_huge_valf();
-      } else {
-        lo = Elem<T>::load(kmeta, (head * 2 + 0) * D + d);
-        hi = Elem<T>::load(kmeta, (head * 2 + 1) * D + d);
-      }
-      for (int pos = lo_pos; pos < hi_pos; ++pos) {
-        const int64_t src = ((int64_t)(row0 + pos - p0) * Hkv + g) * D + d;
-        const int slot = pos - page * P;
-        const T kx = k_new[src];
-        k_cache[(head * P + slot) * D + d] = kx;
-        v_cache[(head * D + d) * P + slot] = v_new[src];
-        const float x = Elem<T>::load(&kx, 0);
-        if (x < lo) lo = x;
-        if (x > hi) hi = x;
-      }
-      // lo and hi are stored values (or the unchanged metadata), so writing
-      // them back in the storage type is exact.
-      Elem<T>::store(kmeta, (head * 2 + 0) * D + d, lo);
-      Elem<T>::store(kmeta, (head * 2 + 1) * D + d, hi);
+      const AppendSpan a = append_span(phys, Hkv, g, P, page, p0, p1, row0);
+      append_channel<T>(a, d, Hkv, D, P, k_new, v_new, k_cache, v_cache, kmeta);
     }
   }
 }

@@ -24,7 +24,7 @@
 // group l / 16; the 16x16 fp32 result gives lane l column l % 16, rows
 // 4*(l/16) .. 4*(l/16)+3.  Both operands use the same (group, element) -> k
 // assignment, so the sum over k is exact whatever order the unit uses inside.
-#include "quest_device.h"
+#include "append_inline.h"
 #include "quest_launch.h"
 
 namespace quest {
@@ -52,12 +52,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-template <int D>
+// New tokens to store before scoring (the fused on_kv_stored + scores path);
+// all null in the plain scoring path.
+struct FusedAppend {
+  const uint16_t *k_new, *v_new;
+  const int32_t *cu_new, *ctx_before;
+  uint16_t *k_cache, *v_cache;
+};
+
+template <int D, bool kAppend>
 __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
     int Hkv, int G, int64_t pool, int P, int max_pages, int reduce,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kmeta,
+    const uint16_t *__restrict__ q, uint16_t *kmeta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
-    float *__restrict__ scores) {
+    FusedAppend fa, float *__restrict__ scores) {
   constexpr int kChunks = 2 * D / 32;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -66,7 +74,16 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
   const int g = blockIdx.x % Hkv;
   const int block = blockIdx.x / Hkv;
   const int r = blockIdx.y;
-  const int n = pages_in(ctx_lens[r], P, max_pages);
+  int ctx, row0 = 0, p0 = 0, n_new = 0;
+  if constexpr (kAppend) {
+    row0 = fa.cu_new[r];
+    n_new = fa.cu_new[r + 1] - row0;
+    p0 = fa.ctx_before[r];
+    ctx = p0 + (n_new > 0 ? n_new : 0);
+  } else {
+    ctx = ctx_lens[r];
+  }
+  const int n = pages_in(ctx, P, max_pages);
   const int base = block * kScorePagesPerBlock;
   if (base >= n) return;
 
@@ -96,6 +113,31 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
     for (int c = 0; c < kChunks; ++c) {
       const int k0 = c * 32 + grp * 8;
       qw[c] = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
+    }
+  }
+
+  if constexpr (kAppend) {
+    // on_kv_stored for this work-group's pages and KV head: the new tokens'
+    // K/V go to their slots and the pages' min/max rows are refreshed, then a
+    // barrier makes the rows visible to the waves that score them.  Only the
+    // work-groups that own a touched page do this (one per request and head
+    // at decode); the page-id and q loads above are already in flight.
+    if (n_new > 0 && p0 >= 0) {
+      const int p1 = p0 + n_new;
+      const int a0 = max(p0 / P, base);
+      const int a1 = min((p1 - 1) / P, base + kScorePagesPerBlock - 1);
+      if (a0 <= a1) {
+        const int32_t *ptr = page_table + (int64_t)r * max_pages;
+        for (int pg = a0; pg <= a1 && pg < max_pages; ++pg) {
+          const int64_t phys = ptr[pg];
+          if (phys < 0 || phys >= pool) continue;
+          const AppendSpan a = append_span(phys, Hkv, g, P, pg, p0, p1, row0);
+          for (int d = threadIdx.x; d < D; d += blockDim.x)
+            append_channel<uint16_t>(a, d, Hkv, D, P, fa.k_new, fa.v_new, fa.k_cache,
+                                     fa.v_cache, kmeta);
+        }
+        __syncthreads();
+      }
     }
   }
 
@@ -148,17 +190,21 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
 // fp32 path: one thread per page, the group's q in LDS.  Each term takes the
 // product on the side the sign of q selects; rounding is monotonic, so this
 // is the larger of the two rounded products.
+// With cu_new non-null the request length is ctx_before + its new tokens
+// (the fused path, after a separate append launch), else ctx_lens.
 __global__ __launch_bounds__(256) void page_scores_valu_kernel(
     int Hkv, int G, int D, int64_t pool, int P, int max_pages, int reduce,
     const float *__restrict__ q, const float *__restrict__ kmeta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
+    const int32_t *__restrict__ cu_new, const int32_t *__restrict__ ctx_before,
     float *__restrict__ scores) {
   extern __shared__ float q_lds[];     // [G][D]
   const int g = blockIdx.y, r = blockIdx.z;
   const float *qg = q + ((int64_t)r * Hkv * G + (int64_t)g * G) * D;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_lds[i] = qg[i];
   __syncthreads();
-  const int n = pages_in(ctx_lens[r], P, max_pages);
+  const int ctx = cu_new ? ctx_before[r] + max(cu_new[r + 1] - cu_new[r], 0) : ctx_lens[r];
+  const int n = pages_in(ctx, P, max_pages);
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
   const int64_t phys = page_table[(int64_t)r * max_pages + j];
@@ -177,30 +223,60 @@ __global__ __launch_bounds__(256) void page_scores_valu_kernel(
   scores[((int64_t)r * Hkv + g) * max_pages + j] = v;
 }
 
-hipError_t launch_page_scores(const Dims &dm, int batch, const void *q,
-                              const void *kmeta, const int32_t *page_table,
-                              const int32_t *ctx_lens, int reduce,
-                              float *scores, hipStream_t stream) {
+static hipError_t launch_scores(const Dims &dm, int batch, const void *q, void *kmeta,
+                                const int32_t *page_table, const int32_t *ctx_lens, int reduce,
+                                const FusedAppend &fa, bool fused, float *scores,
+                                hipStream_t stream) {
   if (dm.dtype == 1) {
     const int blocks = (dm.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock;
     dim3 grid((unsigned)(blocks * dm.Hkv), (unsigned)batch);
     dim3 block(64 * kScoreWaves);
-    if (dm.D == 128)
-      hipLaunchKernelGGL(page_scores_mfma_kernel<128>, grid, block, 0, stream, dm.Hkv, dm.G,
-                         dm.pool, dm.P, dm.max_pages, reduce, (const uint16_t *)q,
-                         (const uint16_t *)kmeta, page_table, ctx_lens, scores);
-    else
-      hipLaunchKernelGGL(page_scores_mfma_kernel<64>, grid, block, 0, stream, dm.Hkv, dm.G,
-                         dm.pool, dm.P, dm.max_pages, reduce, (const uint16_t *)q,
-                         (const uint16_t *)kmeta, page_table, ctx_lens, scores);
+#define QUEST_SCORES(DD, AA)                                                                \
+  hipLaunchKernelGGL((page_scores_mfma_kernel<DD, AA>), grid, block, 0, stream, dm.Hkv, dm.G, \
+                     dm.pool, dm.P, dm.max_pages, reduce, (const uint16_t *)q,              \
+                     (uint16_t *)kmeta, page_table, ctx_lens, fa, scores)
+    if (dm.D == 128) {
+      if (fused) QUEST_SCORES(128, true); else QUEST_SCORES(128, false);
+    } else {
+      if (fused) QUEST_SCORES(64, true); else QUEST_SCORES(64, false);
+    }
+#undef QUEST_SCORES
   } else {
     dim3 grid((unsigned)((dm.max_pages + 255) / 256), (unsigned)dm.Hkv, (unsigned)batch);
     hipLaunchKernelGGL(page_scores_valu_kernel, grid, dim3(256),
                        (size_t)dm.G * dm.D * sizeof(float), stream, dm.Hkv, dm.G, dm.D,
                        dm.pool, dm.P, dm.max_pages, reduce, (const float *)q,
-                       (const float *)kmeta, page_table, ctx_lens, scores);
+                       (const float *)kmeta, page_table, ctx_lens,
+                       fused ? fa.cu_new : nullptr, fused ? fa.ctx_before : nullptr, scores);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_page_scores(const Dims &dm, int batch, const void *q,
+                              const void *kmeta, const int32_t *page_table,
+                              const int32_t *ctx_lens, int reduce,
+                              float *scores, hipStream_t stream) {
+  const FusedAppend none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  return launch_scores(dm, batch, q, const_cast<void *>(kmeta), page_table, ctx_lens, reduce,
+                       none, false, scores, stream);
+}
+
+hipError_t launch_append_scores(const Dims &dm, int batch, const void *q, const void *k_new,
+                                const void *v_new, const int32_t *cu_new,
+                                const int32_t *ctx_before, int max_new,
+                                const int32_t *page_table, void *k_cache, void *v_cache,
+                                void *kmeta, int reduce, float *scores, hipStream_t stream) {
+  const FusedAppend fa{(const uint16_t *)k_new, (const uint16_t *)v_new, cu_new, ctx_before,
+                       (uint16_t *)k_cache, (uint16_t *)v_cache};
+  if (dm.dtype != 1) {
+    // fp32: the append runs as its own launch, then the scores read the
+    // request lengths from cu_new / ctx_before
+    const hipError_t e = launch_append(dm, batch, k_new, v_new, cu_new, ctx_before, max_new,
+                                       page_table, k_cache, v_cache, kmeta, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_scores(dm, batch, q, kmeta, page_table, nullptr, reduce, fa, true, scores,
+                       stream);
 }
 
 }  // namespace quest

@@ -107,6 +107,29 @@ int quest_page_scores(const quest_layout *layout, int32_t batch, const void *q,
                                             group_reduce, scores, (hipStream_t)stream));
 }
 
+int quest_append_score(const quest_layout *layout, int32_t batch, const void *q,
+                       const void *k_new, const void *v_new, const int32_t *cu_new,
+                       const int32_t *ctx_before, int32_t max_new_per_seq,
+                       const int32_t *page_table, void *k_cache, void *v_cache, void *kmeta,
+                       int32_t group_reduce, float *scores, void *stream) {
+  Dims dm;
+  int st = check_layout(layout, dm);
+  if (st != QUEST_OK) return st;
+  if ((st = check_batch(batch, dm)) != QUEST_OK) return st;
+  if (max_new_per_seq < 0) return QUEST_ERR_SHAPE;
+  if (group_reduce != QUEST_REDUCE_MAX && group_reduce != QUEST_REDUCE_SUM)
+    return QUEST_ERR_UNSUPPORTED;
+  if (batch == 0) return QUEST_OK;
+  if (!q || !k_new || !v_new || !cu_new || !ctx_before || !page_table || !k_cache ||
+      !v_cache || !kmeta || !scores)
+    return QUEST_ERR_NULL;
+  if (dm.dtype == QUEST_BF16 && (!aligned16(q) || !aligned16(kmeta))) return QUEST_ERR_SHAPE;
+  return launched(quest::launch_append_scores(dm, batch, q, k_new, v_new, cu_new, ctx_before,
+                                              max_new_per_seq, page_table, k_cache, v_cache,
+                                              kmeta, group_reduce, scores,
+                                              (hipStream_t)stream));
+}
+
 int quest_topk_pages(const quest_layout *layout, int32_t batch, const float *scores,
                      const int32_t *ctx_lens, const int32_t *budget_tokens, int32_t max_k,
                      int32_t *sel_pages, int32_t *num_sel, void *stream) {

@@ -47,6 +47,49 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
 }
 
+// Cross-lane steps on the DPP network (register-to-register, no LDS round
+// trip).  dpp_row<ctrl>(old, src): the src value of the lane `ctrl` selects
+// inside the same row of 16 lanes; lanes whose source falls outside the row
+// keep `old`.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_row(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, kCtrl, 0xf, 0xf, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += dpp_row<kRowShr1>(0u, x);       // scan inside each row of 16
+  x += dpp_row<kRowShr2>(0u, x);
+  x += dpp_row<kRowShr4>(0u, x);
+  x += dpp_row<kRowShr8>(0u, x);
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15);   // row totals
+  const uint32_t r1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 47);
+  const uint32_t row = lane_id() >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Wave-wide min / max of uint32 (all lanes active); the result is uniform.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_row<kRowShr1>(x, x));
+  x = min(x, dpp_row<kRowShr2>(x, x));
+  x = min(x, dpp_row<kRowShr4>(x, x));
+  x = min(x, dpp_row<kRowShr8>(x, x));
+  return min(min((uint32_t)__builtin_amdgcn_readlane(x, 15), (uint32_t)__builtin_amdgcn_readlane(x, 31)),
+             min((uint32_t)__builtin_amdgcn_readlane(x, 47), (uint32_t)__builtin_amdgcn_readlane(x, 63)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_row<kRowShr1>(x, x));
+  x = max(x, dpp_row<kRowShr2>(x, x));
+  x = max(x, dpp_row<kRowShr4>(x, x));
+  x = max(x, dpp_row<kRowShr8>(x, x));
+  return max(max((uint32_t)__builtin_amdgcn_readlane(x, 15), (uint32_t)__builtin_amdgcn_readlane(x, 31)),
+             max((uint32_t)__builtin_amdgcn_readlane(x, 47), (uint32_t)__builtin_amdgcn_readlane(x, 63)));
+}
+
 // Pages of a request of ctx tokens, limited to the page-table row.
 __device__ __forceinline__ int pages_in(int ctx, int page_size, int max_pages) {
   int n = ctx <= 0 ? 0 : (ctx + page_size - 1) / page_size;

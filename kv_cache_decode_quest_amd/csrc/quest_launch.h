@@ -26,6 +26,14 @@ hipError_t launch_page_scores(const Dims &dm, int batch, const void *q,
                               const int32_t *ctx_lens, int reduce,
                               float *scores, hipStream_t stream);
 
+// on_kv_stored and the page scores in one pass over the metadata (bf16: one
+// kernel; fp32: two launches).  Request lengths are ctx_before + new tokens.
+hipError_t launch_append_scores(const Dims &dm, int batch, const void *q, const void *k_new,
+                                const void *v_new, const int32_t *cu_new,
+                                const int32_t *ctx_before, int max_new,
+                                const int32_t *page_table, void *k_cache, void *v_cache,
+                                void *kmeta, int reduce, float *scores, hipStream_t stream);
+
 hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        const int32_t *ctx_lens, const int32_t *budget_tokens,
                        int max_k, int32_t *sel_pages, int32_t *num_sel,

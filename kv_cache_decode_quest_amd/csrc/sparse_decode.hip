@@ -188,15 +188,26 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   const int split = blockIdx.x % n_split;
   const int row = blockIdx.x / n_split;
   const int r = row / Hkv, g = row - r * Hkv;
-  const int nsel = min(num_sel[row], max_k);
   const int first = split * pps;
-  if (first >= nsel) return;                       // merge reads only live splits
-  const int last = min(nsel, first + pps);
-  const int ctx = ctx_lens[r];
-  const int n = pages_in(ctx, P, max_pages);
   const int32_t *sel = sel_pages + (int64_t)row * max_k;
   const int32_t *pt = page_table + (int64_t)r * max_pages;
   const int64_t page_elems = (int64_t)P * D;
+  // The first round of page ids is read together with the row's count and
+  // length (ids past the count are ignored below), so the chain to the first
+  // K/V load is ids -> page table -> K/V.
+  constexpr int kFirst = kDecodeWaves * PPW;
+  int sel0[PPW];
+#pragma unroll
+  for (int u = 0; u < PPW; ++u) {
+    const int i = first + wave * PPW + u;
+    sel0[u] = sel[i < max_k ? i : max_k - 1];
+  }
+  const int jfirst = sel[first < max_k ? first : max_k - 1];
+  const int nsel = min(num_sel[row], max_k);
+  const int ctx = ctx_lens[r];
+  if (first >= nsel) return;                       // merge reads only live splits
+  const int last = min(nsel, first + pps);
+  const int n = pages_in(ctx, P, max_pages);
 
   // q^T operand: column `col` = head, K slots of group `grp` (zero past G).
   // Loads here and below are unconditional, from clamped in-bounds
@@ -219,21 +230,23 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   float m = -__builtin_huge_valf();     // running max of head `col` (base-2 logits)
   float l = 0.f;                        // running sum of head `col`
 
-  // Each round, wave w takes PPW consecutive selected pages; page slots past
-  // the split re-read the split's last page (a cache hit) and are skipped.
-  for (int base = first; base < last; base += kDecodeWaves * PPW) {
+  // Each round, wave w takes PPW consecutive selected pages.
+  for (int base = first; base < last; base += kFirst) {
     const int p0 = base + wave * PPW;
     int64_t phys[PPW];
     int valid[PPW];
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
       const int i = p0 + u;
-      const int j = sel[i < last ? i : last - 1];
-      const bool jok = j >= 0 && j < n;
-      const int64_t ph = pt[jok ? j : 0];
-      const bool ok = jok && ph >= 0 && ph < pool;
+      const int j = (base == first) ? sel0[u] : sel[i < last ? i : last - 1];
+      // slots past the split, or with an id outside the request, re-read the
+      // split's first page (a cache hit) and are skipped
+      const bool live = i < last && j >= 0 && j < n;
+      const int jj = live ? j : ((jfirst >= 0 && jfirst < n) ? jfirst : 0);
+      const int64_t ph = pt[jj];
+      const bool ok = ph >= 0 && ph < pool;
       phys[u] = ok ? ph : 0;
-      valid[u] = (ok && i < last) ? min(P, ctx - j * P) : 0;
+      valid[u] = (live && ok) ? min(P, ctx - j * P) : 0;
     }
     PR pg[PPW];
 #pragma unroll
@@ -386,19 +399,16 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
 
 // ---------------------------------------------------------------------------
 // merge: out[r][h] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// One work-group per (request, q head), one thread per channel.  The split
-// statistics are read once into LDS; each thread then issues the loads of
-// eight splits at a time from clamped addresses before summing them.
+// One work-group per (request, q head), one thread per channel.  Splits are
+// taken 16 at a time with all of their loads issued together (the max and
+// sum are the same address across the work-group), merged online.
 // ---------------------------------------------------------------------------
-constexpr int kMergeUnroll = 8;
+constexpr int kMergeChunk = 16;
 
 template <typename T>
 __global__ __launch_bounds__(128) void merge_kernel(
     int Hkv, int G, int D, int max_k, int n_split, int pps, const int32_t *__restrict__ num_sel,
     const float *__restrict__ partial, T *__restrict__ out) {
-  __shared__ float w_lds[kMaxSplits];        // split max, then the split's weight
-  __shared__ float l_lds[kMaxSplits];        // split sum
-  __shared__ float red[2];
   const int hq = blockIdx.x;                 // r * Hq + h
   const int Hq = Hkv * G;
   const int r = hq / Hq, h = hq - r * Hq;
@@ -408,43 +418,35 @@ __global__ __launch_bounds__(128) void merge_kernel(
   const int live = nsel <= 0 ? 0 : min((nsel + pps - 1) / pps, n_split);
   const int64_t stride = (int64_t)G * (D + 2);
   const float *base = partial + (int64_t)row * n_split * stride + (int64_t)hl * (D + 2);
-  for (int s = threadIdx.x; s < live; s += blockDim.x) {
-    w_lds[s] = base[s * stride + D];
-    l_lds[s] = base[s * stride + D + 1];
-  }
-  __syncthreads();
-  if (threadIdx.x < kWave) {
-    float M = -__builtin_huge_valf();
-    for (int s = threadIdx.x; s < live; s += kWave) M = fmaxf(M, w_lds[s]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-    float L = 0.f;
-    for (int s = threadIdx.x; s < live; s += kWave) {
-      const float ms = w_lds[s];
-      const float f = (ms == -__builtin_huge_valf()) ? 0.f : exp2_fast(ms - M);
-      w_lds[s] = f;
-      L += f * l_lds[s];
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, kWave);
-    if (threadIdx.x == 0) red[0] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-  const float inv_l = red[0];
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float a = 0.f;
-    for (int s0 = 0; s0 < live; s0 += kMergeUnroll) {
-      float v[kMergeUnroll];
+    float M = -__builtin_huge_valf(), L = 0.f, a = 0.f;
+    for (int s0 = 0; s0 < live; s0 += kMergeChunk) {
+      float mv[kMergeChunk], lv[kMergeChunk], av[kMergeChunk];
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        const int s = s0 + u < live ? s0 + u : s0;
-        v[u] = base[s * stride + d];
+      for (int u = 0; u < kMergeChunk; ++u) {
+        const float *p = base + (s0 + u < live ? s0 + u : s0) * stride;
+        mv[u] = p[D];
+        lv[u] = p[D + 1];
+        av[u] = p[d];
       }
+      float cm = M;
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u)
-        if (s0 + u < live) a += w_lds[s0 + u] * v[u];
+      for (int u = 0; u < kMergeChunk; ++u)
+        if (s0 + u < live) cm = fmaxf(cm, mv[u]);
+      if (cm == -__builtin_huge_valf()) continue;  // nothing but empty splits so far
+      const float f0 = (M == -__builtin_huge_valf()) ? 0.f : exp2_fast(M - cm);
+      a *= f0;
+      L *= f0;
+#pragma unroll
+      for (int u = 0; u < kMergeChunk; ++u) {
+        const float f = (s0 + u < live && mv[u] != -__builtin_huge_valf())
+                            ? exp2_fast(mv[u] - cm) : 0.f;
+        a += f * av[u];
+        L += f * lv[u];
+      }
+      M = cm;
     }
-    Elem<T>::store(out, (int64_t)hq * D + d, a * inv_l);
+    Elem<T>::store(out, (int64_t)hq * D + d, L > 0.f ? a / L : 0.f);
   }
 }
 

@@ -7,23 +7,22 @@
 //     (orderable(score) << 32) | (0xffffffff - page),
 // so the selected set is unique and any exact top-k algorithm returns it.
 //
-// One work-group per row, radix select on the 32-bit orderable score keys
-// (staged in LDS for rows of up to 8192 pages):
-//  1. block min/max of the keys: every key shares the bits above the highest
-//     bit where min and max differ;
-//  2. refinement passes: an (up to) 11-bit histogram of the keys that match
-//     the known prefix, on the next bits, finds the bucket holding the k-th
-//     largest key and how many keys above it are kept outright; the bucket's
-//     bits join the prefix;
-//  3. as soon as the bucket holds at most 64 keys, they are gathered into LDS
-//     and one wave ranks its (key, page) pairs in the 64-bit order, which
-//     fixes the threshold pair; otherwise refinement continues down to the
-//     last bit;
-//  4. a final pass writes the kept pages in ascending order: every page whose
-//     key is above the threshold key, and the lowest-index pages among those
-//     equal to it up to the count still needed.  Each thread owns a
-//     contiguous run of pages, and an exclusive scan of per-thread counts gives
-//     each its output position.
+// One 1024-thread work-group per row, radix select on the 32-bit orderable
+// score keys (staged in LDS for rows of up to 8192 pages).  The work is a
+// handful of barrier-separated phases, each short; wave-level scans and
+// reductions use the DPP network and ballots, not LDS round trips.
+//  1. min and max key: every key shares the bits above the highest bit where
+//     they differ;
+//  2. refinement: an (up to) 11-bit histogram of the keys matching the known
+//     prefix, on the next bits, gives the bucket holding the k-th largest key
+//     and the count kept above it; repeated until the bucket holds at most 64
+//     keys (usually once) or the key is fully known;
+//  3. the bucket's keys are gathered into LDS and every wave ranks the
+//     (key, page) pairs in the 64-bit order, which fixes the threshold;
+//  4. each wave walks a contiguous range of pages with ballots: a count pass,
+//     one barrier to exchange the per-wave counts, then a write pass that puts
+//     every page above the threshold, and the lowest-index pages equal to it
+//     up to the count still needed, at its ascending position.
 #include "quest_device.h"
 #include "quest_launch.h"
 
@@ -33,7 +32,8 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-static_assert(kBins == 2 * kTopkThreads, "each thread owns two histogram buckets");
+constexpr int kBinsPerWave = kBins / kTopkWaves;     // 128: two per lane
+static_assert(kBinsPerWave == 2 * kWave, "each lane owns two histogram buckets");
 
 // Larger score <-> larger key; -0.0 and +0.0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -42,54 +42,36 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
 struct TopkShared {
   uint32_t hist[kBins];
-  uint32_t wave_tot[kTopkWaves];
+  uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves];
   uint32_t cand_key[kWave];
   int32_t cand_idx[kWave];
   uint32_t cand_count;
   uint32_t prefix;     // known high bits of the threshold key
   uint32_t krem;       // keys still to take at or below the known prefix
   uint32_t bucket;     // keys in the chosen bucket
-  uint32_t lo, hi;
 };
 
-// Inclusive scan over the block in thread order.  Ends with a barrier, so
-// wave_tot may be reused right after.
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, TopkShared &sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) sh.wave_tot[wave] = incl;
-  __syncthreads();
-  uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += sh.wave_tot[w];
-  __syncthreads();
-  return off + incl;
-}
-
-// The bucket (of `bins`) that holds the krem-th largest counted key, scanning
-// buckets from the top; thread t owns buckets bins-1-2t and bins-2-2t, read
-// from consecutive LDS words.  Results in sh.prefix / sh.krem / sh.bucket.
+// The bucket (of `bins` <= kBins) holding the krem-th largest counted key,
+// buckets ranked from the top: wave w owns the 128 buckets below the top
+// 128*w, lane l two of them.  Results in sh.prefix / sh.krem / sh.bucket.
 __device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t krem,
                                             uint32_t prefix, int shift) {
-  const int b1 = bins - 1 - 2 * (int)threadIdx.x, b0 = b1 - 1;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int b1 = bins - 1 - kBinsPerWave * wave - 2 * lane, b0 = b1 - 1;
   const uint32_t c1 = b1 >= 0 ? sh.hist[b1] : 0u;
   const uint32_t c0 = b0 >= 0 ? sh.hist[b0] : 0u;
-  const uint32_t incl = block_incl_scan(c1 + c0, sh);
-  const uint32_t excl = incl - c1 - c0;
-  if (excl < krem && krem <= incl) {
+  const uint32_t incl = wave_incl_sum(c1 + c0);
+  if (lane == kWave - 1) sh.wave_a[wave] = incl;
+  __syncthreads();
+  uint32_t above = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) above += (w < wave) ? sh.wave_a[w] : 0u;
+  const uint32_t excl = above + incl - c1 - c0;
+  if (excl < krem && krem <= excl + c1 + c0) {
     const bool upper = excl + c1 >= krem;
-    const int b = upper ? b1 : b0;
-    sh.prefix = prefix | ((uint32_t)b << shift);
+    sh.prefix = prefix | ((uint32_t)(upper ? b1 : b0) << shift);
     sh.krem = krem - (upper ? excl : excl + c1);
     sh.bucket = upper ? c1 : c0;
   }
@@ -109,7 +91,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel) {
   __shared__ TopkShared sh;
   __shared__ uint32_t staged[kStaged ? kStagedKeys : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int row = blockIdx.x;
   const int r = row / Hkv;
   const int n = pages_in(ctx_lens[r], P, max_pages);
@@ -132,8 +114,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     else return order_key(s[j]);
   };
 
-  // 1. min and max key (and, for short rows, the keys into LDS: all loads of
-  //    a thread are issued together from clamped addresses)
+  // 1. min and max key (short rows: all loads of a thread issued together
+  //    from clamped addresses, keys kept in LDS)
   uint32_t lo = 0xffffffffu, hi = 0u;
   if constexpr (kStaged) {
     float v[kLoadUnroll];
@@ -159,37 +141,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
       hi = max(hi, u);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor(lo, o, kWave));
-    hi = max(hi, (uint32_t)__shfl_xor(hi, o, kWave));
-  }
-  if (tid == 0) {
-    sh.lo = 0xffffffffu;
-    sh.hi = 0u;
-    sh.cand_count = 0;
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    sh.wave_a[wave] = lo;
+    sh.wave_b[wave] = hi;
   }
   sh.hist[2 * tid] = 0;
   sh.hist[2 * tid + 1] = 0;
+  if (tid == 0) sh.cand_count = 0;
   __syncthreads();
-  if (lane == 0) {
-    atomicMin(&sh.lo, lo);
-    atomicMax(&sh.hi, hi);
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    lo = min(lo, sh.wave_a[w]);
+    hi = max(hi, sh.wave_b[w]);
   }
-  __syncthreads();
-  lo = sh.lo;
-  hi = sh.hi;
 
   uint32_t thresh, krem = (uint32_t)k;
   if (lo == hi) {                                     // every key equal
     thresh = lo;
   } else {
-    // 2./3. refine the threshold key, 11 bits at a time
+    // 2. refine the threshold key, 11 bits at a time
     const int hb = 31 - __builtin_clz(lo ^ hi);
     int lowbit = hb + 1;                              // bits >= lowbit are known
     uint32_t prefix = (uint32_t)(((uint64_t)hi >> lowbit) << lowbit);
-    bool first_pass = true;
-    for (;;) {
+    uint32_t count;
+    for (bool first_pass = true;; first_pass = false) {
       const int w = lowbit < kDigitBits ? lowbit : kDigitBits;
       const int shift = lowbit - w;
       const uint32_t bmask = (1u << w) - 1u;
@@ -198,7 +175,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
         sh.hist[2 * tid + 1] = 0;
         __syncthreads();
       }
-      first_pass = false;
       const uint64_t want = (uint64_t)prefix >> lowbit;
       for (int j = tid; j < n; j += kTopkThreads) {
         const uint32_t u = key(j);
@@ -208,87 +184,83 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
       pick_bucket(sh, 1 << w, krem, prefix, shift);
       prefix = sh.prefix;
       krem = sh.krem;
-      const uint32_t count = sh.bucket;
+      count = sh.bucket;
       lowbit = shift;
-      if (lowbit == 0) {                              // the threshold key itself
-        thresh = prefix;
-        break;
-      }
-      if (count <= (uint32_t)kWave) {
-        // gather the bucket and rank it in one wave
-        const uint32_t want2 = prefix >> lowbit;
-        for (int j = tid; j < n; j += kTopkThreads) {
-          const uint32_t u = key(j);
-          if ((u >> lowbit) == want2) {
-            const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
-            if (slot < (uint32_t)kWave) {
-              sh.cand_key[slot] = u;
-              sh.cand_idx[slot] = j;
-            }
+      if (lowbit == 0 || count <= (uint32_t)kWave) break;
+    }
+    if (lowbit == 0) {                                // the threshold key itself
+      thresh = prefix;
+    } else {
+      // 3. gather the bucket; every wave ranks it (no barrier needed after)
+      const uint32_t want2 = prefix >> lowbit;
+      for (int j = tid; j < n; j += kTopkThreads) {
+        const uint32_t u = key(j);
+        if ((u >> lowbit) == want2) {
+          const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
+          if (slot < (uint32_t)kWave) {
+            sh.cand_key[slot] = u;
+            sh.cand_idx[slot] = j;
           }
         }
-        __syncthreads();
-        if (wave == 0) {
-          const uint32_t c = count;
-          const bool mine = (uint32_t)lane < c;
-          const uint64_t me = mine ? (((uint64_t)sh.cand_key[lane] << 32) |
-                                      (0xffffffffu - (uint32_t)sh.cand_idx[lane]))
-                                   : 0ull;
-          uint32_t rank = 0;
-          for (uint32_t m = 0; m < c; ++m) {
-            const uint64_t other = ((uint64_t)sh.cand_key[m] << 32) |
-                                   (0xffffffffu - (uint32_t)sh.cand_idx[m]);
-            rank += other > me;
-          }
-          if (mine && rank == krem - 1) {
-            // threshold = this pair; count the equal-key pairs at or above it
-            const uint32_t tkey = sh.cand_key[lane];
-            const int32_t tidx = sh.cand_idx[lane];
-            uint32_t eq = 0;
-            for (uint32_t m = 0; m < c; ++m)
-              eq += (sh.cand_key[m] == tkey && sh.cand_idx[m] <= tidx);
-            sh.prefix = tkey;
-            sh.krem = eq;
-          }
-        }
-        __syncthreads();
-        thresh = sh.prefix;
-        krem = sh.krem;
-        break;
       }
+      __syncthreads();
+      const bool mine = (uint32_t)lane < count;
+      const uint32_t mkey = mine ? sh.cand_key[lane] : 0u;
+      const int32_t midx = mine ? sh.cand_idx[lane] : 0;
+      const uint64_t me = ((uint64_t)mkey << 32) | (0xffffffffu - (uint32_t)midx);
+      uint32_t rank = 0;
+      for (uint32_t m = 0; m < count; ++m) {
+        const uint64_t other = ((uint64_t)sh.cand_key[m] << 32) |
+                               (0xffffffffu - (uint32_t)sh.cand_idx[m]);
+        rank += other > me;
+      }
+      const uint64_t hit = __ballot(mine && rank == krem - 1);
+      const int tl = (int)__ffsll((unsigned long long)hit) - 1;
+      thresh = (uint32_t)__builtin_amdgcn_readlane((int)mkey, tl);
+      const int32_t tidx = __builtin_amdgcn_readlane(midx, tl);
+      // equal-key pairs at or above the threshold pair
+      const uint64_t eq = __ballot(mine && mkey == thresh && midx <= tidx);
+      krem = (uint32_t)__popcll(eq);
     }
   }
 
-  // 4. ascending output: keys above the threshold, then the first `krem`
-  //    pages whose key equals it.  One scan of (above, equal) counts packed
-  //    in 16-bit halves when the row fits, two scans otherwise.
-  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
-  const int j0 = tid * chunk;
-  const int j1 = min(n, j0 + chunk);
-  uint32_t gt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t u = key(j);
-    gt += u > thresh;
-    eq += u == thresh;
+  // 4. ascending output.  Wave w owns pages [w*span, (w+1)*span), 64 at a time.
+  const int span = ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
+  const int w0 = wave * span;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t gt_w = 0, eq_w = 0;
+  for (int j0 = w0; j0 < w0 + span && j0 < n; j0 += kWave) {
+    const int j = j0 + lane;
+    const uint32_t u = j < n ? key(j) : 0u;
+    gt_w += (uint32_t)__popcll(__ballot(j < n && u > thresh));
+    eq_w += (uint32_t)__popcll(__ballot(j < n && u == thresh));
   }
-  uint32_t gt_before, eq_before;
-  if (n < 65536) {
-    const uint32_t packed = (gt << 16) | eq;
-    const uint32_t before = block_incl_scan(packed, sh) - packed;
-    gt_before = before >> 16;
-    eq_before = before & 0xffffu;
-  } else {
-    gt_before = block_incl_scan(gt, sh) - gt;
-    eq_before = block_incl_scan(eq, sh) - eq;
+  __syncthreads();                                    // wave_a/b free again
+  if (lane == 0) {
+    sh.wave_a[wave] = gt_w;
+    sh.wave_b[wave] = eq_w;
   }
-  uint32_t pos = gt_before + min(eq_before, krem);
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t u = key(j);
-    const bool take = u > thresh || (u == thresh && eq_before++ < krem);
-    if (take) {
-      if (pos < (uint32_t)k) out[pos] = j;      // never past the row
-      ++pos;
+  __syncthreads();
+  uint32_t gt_b = 0, eq_b = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    gt_b += (w < wave) ? sh.wave_a[w] : 0u;
+    eq_b += (w < wave) ? sh.wave_b[w] : 0u;
+  }
+  for (int j0 = w0; j0 < w0 + span && j0 < n; j0 += kWave) {
+    const int j = j0 + lane;
+    const uint32_t u = j < n ? key(j) : 0u;
+    const bool is_gt = j < n && u > thresh;
+    const bool is_eq = j < n && u == thresh;
+    const uint64_t mgt = __ballot(is_gt), meq = __ballot(is_eq);
+    const uint32_t gt_before = gt_b + (uint32_t)__popcll(mgt & below);
+    const uint32_t eq_before = eq_b + (uint32_t)__popcll(meq & below);
+    if (is_gt || (is_eq && eq_before < krem)) {
+      const uint32_t pos = gt_before + min(eq_before, krem);
+      if (pos < (uint32_t)k) out[pos] = j;            // never past the row
     }
+    gt_b += (uint32_t)__popcll(mgt);
+    eq_b += (uint32_t)__popcll(meq);
   }
 }
 

@@ -23,8 +23,8 @@ REDUCE = {"max": 0, "sum": 1}
 
 # exported symbols declared in include/quest.h
 EXPORTS = ("quest_abi_version", "quest_status_string", "quest_append_kv", "quest_page_scores",
-           "quest_topk_pages", "quest_sparse_decode_workspace_bytes", "quest_sparse_decode",
-           "quest_sparse_decode_plan")
+           "quest_append_score", "quest_topk_pages", "quest_sparse_decode_workspace_bytes",
+           "quest_sparse_decode", "quest_sparse_decode_plan")
 
 
 class QuestError(RuntimeError):
@@ -66,13 +66,15 @@ def load(path: str = LIB_PATH):
     L.quest_status_string.argtypes, L.quest_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.quest_append_kv.argtypes = [lp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
     L.quest_page_scores.argtypes = [lp, i32, vp, vp, vp, vp, i32, vp, vp]
+    L.quest_append_score.argtypes = [lp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
+                                     vp]
     L.quest_topk_pages.argtypes = [lp, i32, vp, vp, vp, i32, vp, vp, vp]
     L.quest_sparse_decode_workspace_bytes.argtypes = [lp, i32, i32]
     L.quest_sparse_decode_workspace_bytes.restype = sz
     L.quest_sparse_decode.argtypes = [lp, i32, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp,
                                       sz, vp]
     L.quest_sparse_decode_plan.argtypes = [lp, i32, i32, ip, ip]
-    for name in ("quest_append_kv", "quest_page_scores", "quest_topk_pages",
+    for name in ("quest_append_kv", "quest_page_scores", "quest_append_score", "quest_topk_pages",
                  "quest_sparse_decode", "quest_sparse_decode_plan"):
         getattr(L, name).restype = ctypes.c_int
     if L.quest_abi_version() != ABI_VERSION:
@@ -183,6 +185,33 @@ def quest_page_scores(L: QuestLayout, q, kmeta, page_table, ctx_lens, scores, gr
     _raise("quest_page_scores", st)
 
 
+def quest_append_score(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq,
+                       page_table, k_cache, v_cache, kmeta, scores, group_reduce="max"):
+    """on_kv_stored + build_decode_view part 1 in one pass (request lengths
+    after the append are ctx_before + new tokens)."""
+    dt, dev = _layout_dtype(L), q.device
+    batch = ctx_before.shape[0]
+    kshape, vshape, mshape = _pool_shapes(L)
+    _check(q, "q", dt, (batch, L.num_q_heads, L.head_dim), dev)
+    _check(k_cache, "k_cache", dt, kshape, dev)
+    _check(v_cache, "v_cache", dt, vshape, dev)
+    _check(kmeta, "kmeta", dt, mshape, dev)
+    T = k_new.shape[0]
+    _check(k_new, "k_new", dt, (T, L.num_kv_heads, L.head_dim), dev)
+    _check(v_new, "v_new", dt, (T, L.num_kv_heads, L.head_dim), dev)
+    _check(cu_new, "cu_new", torch.int32, (batch + 1,), dev)
+    _check(ctx_before, "ctx_before", torch.int32, (batch,), dev)
+    _check(page_table, "page_table", torch.int32, (batch, L.max_pages_per_seq), dev)
+    _check(scores, "scores", torch.float32, (batch, L.num_kv_heads, L.max_pages_per_seq), dev)
+    if T == 0:                       # nothing to store: a plain scoring pass
+        k_new = v_new = torch.empty((1, L.num_kv_heads, L.head_dim), dtype=dt, device=dev)
+    st = load().quest_append_score(ctypes.byref(L), batch, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(cu_new), _ptr(ctx_before), int(max_new_per_seq),
+                                   _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _ptr(kmeta),
+                                   REDUCE[group_reduce], _ptr(scores), _stream(dev))
+    _raise("quest_append_score", st)
+
+
 def quest_topk_pages(L: QuestLayout, scores, ctx_lens, budget_tokens, max_k, sel_pages, num_sel):
     """build_decode_view part 2: ascending top-k logical pages per (r, KV head)."""
     dev = scores.device
@@ -260,12 +289,12 @@ def alloc_decode_buffers(L: QuestLayout, batch: int, max_k: int, device) -> Deco
 def decode_step(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, ctx_lens, budget_tokens,
                 page_table, k_cache, v_cache, kmeta, bufs: DecodeBuffers, sm_scale,
                 group_reduce="max", max_new_per_seq=1):
-    """One Quest decode step of one layer: on_kv_stored, then build_decode_view
-    (scores, top-k), then attention over the view.  Four ABI calls, all
-    asynchronous on the current stream."""
-    quest_append_kv(L, k_new, v_new, cu_new, ctx_before, max_new_per_seq, page_table, k_cache,
-                    v_cache, kmeta)
-    quest_page_scores(L, q, kmeta, page_table, ctx_lens, bufs.scores, group_reduce)
+    """One Quest decode step of one layer: on_kv_stored fused with the page
+    scores, then the top-k (the rest of build_decode_view), then attention
+    over the view.  Three ABI calls, all asynchronous on the current stream;
+    ctx_lens must equal ctx_before + the new tokens."""
+    quest_append_score(L, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq, page_table,
+                       k_cache, v_cache, kmeta, bufs.scores, group_reduce)
     quest_topk_pages(L, bufs.scores, ctx_lens, budget_tokens, bufs.max_k, bufs.sel_pages,
                      bufs.num_sel)
     quest_sparse_decode(L, q, k_cache, v_cache, page_table, ctx_lens, bufs.sel_pages,

@@ -84,6 +84,24 @@ class Layer:
                                     self.pt_host[r], self.host[0], self.host[1])
         self.ctx = self.ctx + 1
 
+    def append_score_step(self, q, k_new, v_new, bufs, reduce="max"):
+        """One token per request through the fused quest_append_score (and the
+        same store on the host), then the top-k."""
+        B = self.w.batch
+        cu = torch.arange(B + 1, dtype=torch.int32, device=self.device)
+        quest.quest_append_score(self.L, q, k_new, v_new, cu, self.ctx, 1, self.pt, self.k_cache,
+                                 self.v_cache, self.kmeta, bufs.scores, reduce)
+        if self.host is not None:
+            kn, vn = to_oracle(k_new), to_oracle(v_new)
+            ctx = self.ctx.cpu().numpy()
+            for r in range(B):
+                oracle.store_tokens(self.shape, np.ascontiguousarray(kn[r:r + 1]),
+                                    np.ascontiguousarray(vn[r:r + 1]), int(ctx[r]),
+                                    self.pt_host[r], self.host[0], self.host[1])
+        self.ctx = self.ctx + 1
+        quest.quest_topk_pages(self.L, bufs.scores, self.ctx, self.budgets(), bufs.max_k,
+                               bufs.sel_pages, bufs.num_sel)
+
     def budgets(self):
         return workloads.budget_tokens(self.w, self.ctx).to(self.device)
 
@@ -103,9 +121,11 @@ class Layer:
                                   bufs.num_sel if nsel is None else nsel, bufs.max_k, sm,
                                   bufs.out, bufs.workspace)
 
-    def buffers(self, max_k=None):
-        return quest.alloc_decode_buffers(self.L, self.w.batch, max_k or self.max_k(),
-                                          self.device)
+    def buffers(self, max_k=None, extra=0):
+        if max_k is None:
+            b = workloads.budget_tokens(self.w, self.ctx + extra).cpu()
+            max_k = max(1, int((b // self.w.page_size).max()))
+        return quest.alloc_decode_buffers(self.L, self.w.batch, max_k, self.device)
 
     # ----- oracle side -------------------------------------------------------
     def oracle_request(self, q, r, reduce="max", sm_scale=None):

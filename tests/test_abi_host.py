@@ -83,6 +83,24 @@ def test_layout_rejections(lib, kw, want):
     assert decode_call(lib, L) == want
     assert lib.quest_append_kv(ctypes.byref(L), 1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE,
                                FAKE, None) == want
+    assert fused_call(lib, L) == want
+
+
+def fused_call(lib, L, batch=1, reduce=0, q=FAKE, kmeta=FAKE, max_new=1, k_new=FAKE):
+    return lib.quest_append_score(ctypes.byref(L), batch, q, k_new, FAKE, FAKE, FAKE, max_new,
+                                  FAKE, FAKE, FAKE, kmeta, reduce, FAKE, None)
+
+
+def test_fused_append_score_rejections(lib):
+    L = layout()
+    assert fused_call(lib, L, q=None) == ERR_NULL
+    assert fused_call(lib, L, k_new=None) == ERR_NULL
+    assert fused_call(lib, L, reduce=3) == ERR_UNSUPPORTED
+    assert fused_call(lib, L, max_new=-1) == ERR_SHAPE
+    assert fused_call(lib, L, kmeta=ctypes.c_void_p(0x100002)) == ERR_SHAPE
+    assert fused_call(lib, L, batch=-1) == ERR_SHAPE
+    assert lib.quest_append_score(ctypes.byref(L), 0, None, None, None, None, None, 0, None,
+                                  None, None, None, 0, None, None) == OK
 
 
 def test_null_layout(lib):

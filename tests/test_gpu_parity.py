@@ -42,8 +42,8 @@ SMALL = {
 }
 
 
-def run_and_check(w, layer=0, reduce="max"):
-    log(f"workload {w.name} layer {layer} reduce {reduce}: batch {w.batch} ctx "
+def run_and_check(w, layer=0, reduce="max", fused=False):
+    log(f"workload {w.name} layer {layer} reduce {reduce} fused {fused}: batch {w.batch} ctx "
         f"{workloads.context_lengths(w).tolist()[:8]}")
     lay = Layer(w, DEV, layer=layer)
     check_pool_bytes(lay)
@@ -54,9 +54,13 @@ def run_and_check(w, layer=0, reduce="max"):
     flagged = 0
     for step in range(w.steps):
         q, k_new, v_new = lay.step_inputs(step)
-        lay.append_step(k_new, v_new)
-        bufs = lay.buffers()
-        lay.view(q, bufs, reduce)
+        if fused:
+            bufs = lay.buffers(extra=1)
+            lay.append_score_step(q, k_new, v_new, bufs, reduce)
+        else:
+            lay.append_step(k_new, v_new)
+            bufs = lay.buffers()
+            lay.view(q, bufs, reduce)
         lay.attend(q, bufs)
         torch.cuda.synchronize()
         check_pool_bytes(lay)
@@ -105,6 +109,12 @@ def test_decode_steps_match_oracle(name, gpu_lib):
     w = SMALL[name]
     for layer in range(w.layers):
         run_and_check(w, layer)
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer32k_small", "ragged_small", "edges",
+                                  "edges_d64_p32", "f32_g1"])
+def test_fused_append_score_matches_oracle(name, gpu_lib):
+    run_and_check(SMALL[name], fused=True)
 
 
 def test_group_sum_variant(gpu_lib):
