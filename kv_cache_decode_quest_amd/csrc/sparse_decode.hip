@@ -205,7 +205,14 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   const int jfirst = sel[first < max_k ? first : max_k - 1];
   const int nsel = min(num_sel[row], max_k);
   const int ctx = ctx_lens[r];
-  if (first >= nsel) return;                       // merge reads only live splits
+  if (first >= nsel) {                             // no page in this split:
+    float *mine = partial + ((int64_t)row * n_split + split) * G * (D + 2);
+    for (int h = threadIdx.x; h < G; h += blockDim.x) {   // an empty partial
+      mine[h * (D + 2) + D] = -__builtin_huge_valf();
+      mine[h * (D + 2) + D + 1] = 0.f;
+    }
+    return;
+  }
   const int last = min(nsel, first + pps);
   const int n = pages_in(ctx, P, max_pages);
 
@@ -315,7 +322,14 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
   const int r = row / Hkv, g = row - r * Hkv;
   const int nsel = min(num_sel[row], max_k);
   const int first = split * pps;
-  if (first >= nsel) return;
+  if (first >= nsel) {                             // no page in this split:
+    float *mine = partial + ((int64_t)row * n_split + split) * G * (D + 2);
+    for (int h = threadIdx.x; h < G; h += blockDim.x) {   // an empty partial
+      mine[h * (D + 2) + D] = -__builtin_huge_valf();
+      mine[h * (D + 2) + D + 1] = 0.f;
+    }
+    return;
+  }
   const int last = min(nsel, first + pps);
   const int ctx = ctx_lens[r];
   const int n = pages_in(ctx, P, max_pages);
@@ -405,17 +419,18 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kMergeChunk = 16;
 
+// Every split writes a partial (an empty one has max -inf and sum 0), so the
+// merge reads all n_split of them without waiting for the selection count.
 template <typename T>
-__global__ __launch_bounds__(128) void merge_kernel(
-    int Hkv, int G, int D, int max_k, int n_split, int pps, const int32_t *__restrict__ num_sel,
-    const float *__restrict__ partial, T *__restrict__ out) {
+__global__ __launch_bounds__(128) void merge_kernel(int Hkv, int G, int D, int n_split,
+                                                    const float *__restrict__ partial,
+                                                    T *__restrict__ out) {
   const int hq = blockIdx.x;                 // r * Hq + h
   const int Hq = Hkv * G;
   const int r = hq / Hq, h = hq - r * Hq;
   const int g = h / G, hl = h - g * G;
   const int row = r * Hkv + g;
-  const int nsel = min(num_sel[row], max_k);
-  const int live = nsel <= 0 ? 0 : min((nsel + pps - 1) / pps, n_split);
+  const int live = n_split;
   const int64_t stride = (int64_t)G * (D + 2);
   const float *base = partial + (int64_t)row * n_split * stride + (int64_t)hl * (D + 2);
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
@@ -439,10 +454,13 @@ __global__ __launch_bounds__(128) void merge_kernel(
       L *= f0;
 #pragma unroll
       for (int u = 0; u < kMergeChunk; ++u) {
-        const float f = (s0 + u < live && mv[u] != -__builtin_huge_valf())
-                            ? exp2_fast(mv[u] - cm) : 0.f;
-        a += f * av[u];
-        L += f * lv[u];
+        // an empty split (max -inf) leaves its accumulator unwritten: select,
+        // never multiply it by a zero weight
+        if (s0 + u < live && mv[u] != -__builtin_huge_valf()) {
+          const float f = exp2_fast(mv[u] - cm);
+          a += f * av[u];
+          L += f * lv[u];
+        }
       }
       M = cm;
     }
@@ -485,12 +503,10 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   const unsigned mblocks = (unsigned)((long)batch * dm.Hkv * dm.G);
   if (dm.dtype == 1)
     hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.Hkv,
-                       dm.G, dm.D, max_k, plan.n_split, plan.pages_per_split, num_sel,
-                       workspace, (uint16_t *)out);
+                       dm.G, dm.D, plan.n_split, workspace, (uint16_t *)out);
   else
     hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.Hkv,
-                       dm.G, dm.D, max_k, plan.n_split, plan.pages_per_split, num_sel,
-                       workspace, (float *)out);
+                       dm.G, dm.D, plan.n_split, workspace, (float *)out);
   return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@
 // so the selected set is unique and any exact top-k algorithm returns it.
 //
 // One 1024-thread work-group per row, radix select on the 32-bit orderable
-// score keys (staged in LDS for rows of up to 8192 pages).  The work is a
+// score keys (held in registers for rows of up to 8192 pages).  The work is a
 // handful of barrier-separated phases, each short; wave-level scans and
 // reductions use the DPP network and ballots, not LDS round trips.
 //  1. min and max key: every key shares the bits above the highest bit where
@@ -78,22 +78,34 @@ __device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t k
   __syncthreads();
 }
 
-// Rows of up to kStagedKeys pages are read from HBM once, into LDS, as
-// orderable keys; every later pass reads LDS.  Longer rows read their scores
-// from global memory in every pass.
-constexpr int kStagedKeys = 8192;
-constexpr int kLoadUnroll = kStagedKeys / kTopkThreads;
+// Rows of up to kRegKeys pages are read from HBM once, into registers: wave w
+// holds pages [512 w, 512 w + 512), lane l pages 512 w + 64 i + l (i < 8), the
+// same wave-contiguous order the output pass needs, so no pass re-reads
+// memory.  Longer rows read their scores from global memory in every pass.
+constexpr int kPerThread = 8;
+constexpr int kRegKeys = kPerThread * kTopkThreads;      // 8192
+constexpr int kRegSpan = kPerThread * kWave;              // pages per wave
 
-template <bool kStaged>
+template <bool kRegs>
 __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     int Hkv, int P, int max_pages, int max_k, const float *__restrict__ scores,
     const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ budget_tokens,
     int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel) {
   __shared__ TopkShared sh;
-  __shared__ uint32_t staged[kStaged ? kStagedKeys : 1];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int row = blockIdx.x;
   const int r = row / Hkv;
+  const float *s = scores + (int64_t)row * max_pages;
+  // Register rows: the whole score row is loaded in the same round trip as
+  // the request's length and budget (entries past the length are ignored).
+  float sv[kRegs ? kPerThread : 1];
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int j = wave * kRegSpan + i * kWave + lane;
+      sv[i] = s[j < max_pages ? j : 0];
+    }
+  }
   const int n = pages_in(ctx_lens[r], P, max_pages);
   int k = 0;
   if (n > 0) {
@@ -101,7 +113,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     k = k < 1 ? 1 : (k > n ? n : k);
     k = k < max_k ? k : max_k;
   }
-  const float *s = scores + (int64_t)row * max_pages;
   int32_t *out = sel_pages + (int64_t)row * max_k;
   if (tid == 0) num_sel[row] = k;
   for (int i = k + tid; i < max_k; i += kTopkThreads) out[i] = -1;
@@ -109,36 +120,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
     return;
   }
-  auto key = [&](int j) -> uint32_t {
-    if constexpr (kStaged) return staged[j];
-    else return order_key(s[j]);
-  };
+  // The thread's keys: registers, or global memory for long rows.  Invalid
+  // slots (past the row) never count; their key is 0.
+  uint32_t u[kRegs ? kPerThread : 1];
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int j = wave * kRegSpan + i * kWave + lane;
+      u[i] = j < n ? order_key(sv[i]) : 0u;
+    }
+  }
+  auto valid = [&](int i) { return wave * kRegSpan + i * kWave + lane < n; };
 
-  // 1. min and max key (short rows: all loads of a thread issued together
-  //    from clamped addresses, keys kept in LDS)
+  // 1. min and max key
   uint32_t lo = 0xffffffffu, hi = 0u;
-  if constexpr (kStaged) {
-    float v[kLoadUnroll];
+  if constexpr (kRegs) {
 #pragma unroll
-    for (int i = 0; i < kLoadUnroll; ++i) {
-      const int j = tid + i * kTopkThreads;
-      v[i] = s[j < n ? j : 0];
-    }
-#pragma unroll
-    for (int i = 0; i < kLoadUnroll; ++i) {
-      const int j = tid + i * kTopkThreads;
-      const uint32_t u = order_key(v[i]);
-      if (j < n) {
-        staged[j] = u;
-        lo = min(lo, u);
-        hi = max(hi, u);
+    for (int i = 0; i < kPerThread; ++i)
+      if (valid(i)) {
+        lo = min(lo, u[i]);
+        hi = max(hi, u[i]);
       }
-    }
   } else {
     for (int j = tid; j < n; j += kTopkThreads) {
-      const uint32_t u = order_key(s[j]);
-      lo = min(lo, u);
-      hi = max(hi, u);
+      const uint32_t x = order_key(s[j]);
+      lo = min(lo, x);
+      hi = max(hi, x);
     }
   }
   lo = wave_min_u32(lo);
@@ -176,9 +183,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
         __syncthreads();
       }
       const uint64_t want = (uint64_t)prefix >> lowbit;
-      for (int j = tid; j < n; j += kTopkThreads) {
-        const uint32_t u = key(j);
-        if (((uint64_t)u >> lowbit) == want) atomicAdd(&sh.hist[(u >> shift) & bmask], 1u);
+      if constexpr (kRegs) {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+          if (valid(i) && ((uint64_t)u[i] >> lowbit) == want)
+            atomicAdd(&sh.hist[(u[i] >> shift) & bmask], 1u);
+      } else {
+        for (int j = tid; j < n; j += kTopkThreads) {
+          const uint32_t x = order_key(s[j]);
+          if (((uint64_t)x >> lowbit) == want) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
+        }
       }
       __syncthreads();
       pick_bucket(sh, 1 << w, krem, prefix, shift);
@@ -193,15 +207,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     } else {
       // 3. gather the bucket; every wave ranks it (no barrier needed after)
       const uint32_t want2 = prefix >> lowbit;
-      for (int j = tid; j < n; j += kTopkThreads) {
-        const uint32_t u = key(j);
-        if ((u >> lowbit) == want2) {
+      auto gather = [&](uint32_t x, int j) {
+        if ((x >> lowbit) == want2) {
           const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
           if (slot < (uint32_t)kWave) {
-            sh.cand_key[slot] = u;
+            sh.cand_key[slot] = x;
             sh.cand_idx[slot] = j;
           }
         }
+      };
+      if constexpr (kRegs) {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+          if (valid(i)) gather(u[i], wave * kRegSpan + i * kWave + lane);
+      } else {
+        for (int j = tid; j < n; j += kTopkThreads) gather(order_key(s[j]), j);
       }
       __syncthreads();
       const bool mine = (uint32_t)lane < count;
@@ -225,15 +245,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
   }
 
   // 4. ascending output.  Wave w owns pages [w*span, (w+1)*span), 64 at a time.
-  const int span = ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
+  const int span = kRegs ? kRegSpan : ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
   const int w0 = wave * span;
+  const int iters = kRegs ? kPerThread : span / kWave;
   const uint64_t below = (1ull << lane) - 1ull;
+  auto key_at = [&](int i, int j) -> uint32_t {
+    if constexpr (kRegs) return u[i];
+    else return j < n ? order_key(s[j]) : 0u;
+  };
   uint32_t gt_w = 0, eq_w = 0;
-  for (int j0 = w0; j0 < w0 + span && j0 < n; j0 += kWave) {
-    const int j = j0 + lane;
-    const uint32_t u = j < n ? key(j) : 0u;
-    gt_w += (uint32_t)__popcll(__ballot(j < n && u > thresh));
-    eq_w += (uint32_t)__popcll(__ballot(j < n && u == thresh));
+#pragma unroll
+  for (int i = 0; i < iters; ++i) {
+    const int j = w0 + i * kWave + lane;
+    const uint32_t x = key_at(i, j);
+    gt_w += (uint32_t)__popcll(__ballot(j < n && x > thresh));
+    eq_w += (uint32_t)__popcll(__ballot(j < n && x == thresh));
   }
   __syncthreads();                                    // wave_a/b free again
   if (lane == 0) {
@@ -247,11 +273,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     gt_b += (w < wave) ? sh.wave_a[w] : 0u;
     eq_b += (w < wave) ? sh.wave_b[w] : 0u;
   }
-  for (int j0 = w0; j0 < w0 + span && j0 < n; j0 += kWave) {
-    const int j = j0 + lane;
-    const uint32_t u = j < n ? key(j) : 0u;
-    const bool is_gt = j < n && u > thresh;
-    const bool is_eq = j < n && u == thresh;
+#pragma unroll
+  for (int i = 0; i < iters; ++i) {
+    const int j = w0 + i * kWave + lane;
+    const uint32_t x = key_at(i, j);
+    const bool is_gt = j < n && x > thresh;
+    const bool is_eq = j < n && x == thresh;
     const uint64_t mgt = __ballot(is_gt), meq = __ballot(is_eq);
     const uint32_t gt_before = gt_b + (uint32_t)__popcll(mgt & below);
     const uint32_t eq_before = eq_b + (uint32_t)__popcll(meq & below);
@@ -269,7 +296,7 @@ hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        int max_k, int32_t *sel_pages, int32_t *num_sel,
                        hipStream_t stream) {
   dim3 grid((unsigned)(batch * dm.Hkv));
-  if (dm.max_pages <= kStagedKeys)
+  if (dm.max_pages <= kRegKeys)
     hipLaunchKernelGGL(topk_pages_kernel<true>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
                        dm.P, dm.max_pages, max_k, scores, ctx_lens, budget_tokens, sel_pages,
                        num_sel);
