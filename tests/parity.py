@@ -36,7 +36,7 @@ class Layer:
     and, optionally, its host mirror for the oracle (filled by oracle.store)."""
 
     def __init__(self, w: workloads.Workload, device, layer=0, capacity=None, host=True,
-                 kmeta_junk=7.0):
+                 kmeta_junk=7.0, host_requests=None):
         self.w, self.device, self.layer = w, device, layer
         self.lay = workloads.make_layout(w, device, capacity)
         self.L = quest.make_layout(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
@@ -57,13 +57,18 @@ class Layer:
         if host:
             kh, vh = workloads.empty_pool(w, self.lay, "cpu")
             self.host = [to_oracle(kh).copy(), to_oracle(vh).copy()]
-            kn, vn, cuh = to_oracle(k_new), to_oracle(v_new), cu.cpu().numpy()
-            for r in range(w.batch):
+            # the host mirror holds every request, or only the sampled ones
+            # (then only those requests may be compared)
+            self.host_requests = list(range(w.batch)) if host_requests is None \
+                else list(host_requests)
+            cuh = cu.cpu().numpy()
+            for r in self.host_requests:
                 a, b = int(cuh[r]), int(cuh[r + 1])
                 if b > a:
-                    oracle.store_tokens(self.shape, np.ascontiguousarray(kn[a:b]),
-                                        np.ascontiguousarray(vn[a:b]), 0, self.pt_host[r],
-                                        self.host[0], self.host[1])
+                    oracle.store_tokens(self.shape, np.ascontiguousarray(to_oracle(k_new[a:b])),
+                                        np.ascontiguousarray(to_oracle(v_new[a:b])), 0,
+                                        self.pt_host[r], self.host[0], self.host[1])
+        del k_new, v_new
         torch.cuda.synchronize()
 
     # ----- one decode step ---------------------------------------------------
@@ -78,7 +83,7 @@ class Layer:
         if self.host is not None:
             kn, vn = to_oracle(k_new), to_oracle(v_new)
             ctx = self.ctx.cpu().numpy()
-            for r in range(B):
+            for r in self.host_requests:
                 oracle.store_tokens(self.shape, np.ascontiguousarray(kn[r:r + 1]),
                                     np.ascontiguousarray(vn[r:r + 1]), int(ctx[r]),
                                     self.pt_host[r], self.host[0], self.host[1])
@@ -94,7 +99,7 @@ class Layer:
         if self.host is not None:
             kn, vn = to_oracle(k_new), to_oracle(v_new)
             ctx = self.ctx.cpu().numpy()
-            for r in range(B):
+            for r in self.host_requests:
                 oracle.store_tokens(self.shape, np.ascontiguousarray(kn[r:r + 1]),
                                     np.ascontiguousarray(vn[r:r + 1]), int(ctx[r]),
                                     self.pt_host[r], self.host[0], self.host[1])
