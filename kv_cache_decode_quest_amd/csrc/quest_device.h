@@ -47,6 +47,40 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
 }
 
+// The value of lane l and of lane l ^ 16 (resp. l ^ 32), through the gfx950
+// row-swap instructions (VALU, no LDS): with both operands equal,
+// v_permlane16_swap returns the even row of each pair of rows in its first
+// result and the odd row in its second, in every lane; v_permlane32_swap
+// does the same for the two halves of the wave.
+__device__ __forceinline__ void pair_xor16(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair_xor32(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// max / sum over the 4 lanes l, l^16, l^32, l^48; every lane gets the same
+// value (the two operands of each step are the same pair in every lane).
+__device__ __forceinline__ float max_over_rows(float v) {
+  float a, b;
+  pair_xor16(v, a, b);
+  v = fmaxf(a, b);
+  pair_xor32(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+  float a, b;
+  pair_xor16(v, a, b);
+  v = a + b;
+  pair_xor32(v, a, b);
+  return a + b;
+}
+
 // Cross-lane steps on the DPP network (register-to-register, no LDS round
 // trip).  dpp_row<ctrl>(old, src): the src value of the lane `ctrl` selects
 // inside the same row of 16 lanes; lanes whose source falls outside the row

@@ -11,31 +11,37 @@
 // through LDS and write one partial (acc, m, l) per head; merge_kernel then
 // combines the splits.
 //
-// bf16 path (matrix cores, one 64-lane wave per page at a time):
-//   S = K q^T   C[16 tokens][16 heads] += K[16 tokens][32 d] * q^T[32 d][16 heads]
-//               (v_mfma_f32_16x16x32_bf16, D/32 steps per 16-token tile; K
-//               pages are token-major, so each lane loads 16 contiguous bytes)
-//   O += P V    C[16 heads][16 d] += P[16 heads][16 tokens] * V[16 tokens][16 d]
-//               (v_mfma_f32_16x16x16_bf16, one step per 16-token tile and
-//               16-channel tile; V pages are dim-major, so each lane loads 4
-//               consecutive tokens of one channel as 8 contiguous bytes)
-// The result of the first product leaves lane l with head l % 16 and tokens
-// 4*(l/16)..+3, which is exactly the lane's A operand of the second product:
-// softmax weights never leave their registers.  For the second product each
-// fp32 weight is split into two bf16 values hi + lo (lo = the rounding error
-// of hi), and both go through the matrix cores, so the weights keep about 16
-// significant bits instead of bf16's 8.  Heads past G are zero columns of q^T.
+// bf16 path (matrix cores).  A wave takes a round of PPW pages at a time:
+// it issues the K loads of all of them, then the V loads, and folds the
+// whole round into its running softmax with one max / sum update:
+//   S   = K q^T    C[16 tokens][16 heads] += K[16 tokens][32 d] * q^T[32 d][16 heads]
+//                  (v_mfma_f32_16x16x32_bf16, D/32 steps per 16-token tile; K
+//                  pages are token-major, so each lane loads 16 contiguous bytes)
+//   O^T += V^T P^T C[16 d][16 heads] += V^T[16 d][16 tokens] * P^T[16 tokens][16 heads]
+//                  (v_mfma_f32_16x16x16_bf16, one step per 16-token tile and
+//                  16-channel tile; V pages are dim-major, so each lane loads 4
+//                  consecutive tokens of one channel as 8 contiguous bytes)
+// The first product leaves lane l with head l % 16 and tokens 4*(l/16)..+3,
+// which is exactly the lane's B operand of the second: softmax weights never
+// leave their registers.  The second product's result keeps the head in the
+// lane's column too, so a lane's running max, running sum and accumulator
+// all belong to one head and rescaling is lane-local.  For the second
+// product each fp32 weight is split into two bf16 values hi + lo (lo = the
+// rounding error of hi), and both go through the matrix cores, so the weights
+// keep about 16 significant bits instead of bf16's 8.  Heads past G are zero
+// columns of q^T.
 #include "quest_device.h"
 #include "quest_launch.h"
 
 namespace quest {
 
-constexpr int kDecodeWaves = 4;
-constexpr int kMaxSplits = 256;        // per (request, KV head); bounds the merge's LDS
+constexpr int kDecodeWaves = 8;
+constexpr int kMaxSplits = 256;        // per (request, KV head); bounds the partials
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Pages one wave loads at once: 64 KB of K and V per wave in flight for
-// 16-token pages at D = 128 (fewer for 32-token pages, to fit the registers).
+// Pages one wave loads at once (one round): 32 KB of K and V per wave in
+// flight for 16-token pages at D = 128 (fewer for 32-token pages at D = 128,
+// to fit the registers).
 __host__ __device__ constexpr int pages_per_wave(int P, int D) {
   return (P * D <= 2048) ? 4 : 2;
 }
@@ -67,109 +73,135 @@ template <int D, int P>
 struct PageRegs {
   static constexpr int TT = P / 16;     // 16-token tiles
   static constexpr int KC = D / 32;     // 32-channel chunks of q.k
-  static constexpr int NT = D / 16;     // 16-channel tiles of P.V
+  static constexpr int NT = D / 16;     // 16-channel tiles of the output
   uint4 k[TT][KC];
   uint2 v[TT][NT];
 };
 
+// K (token-major): lane (col, grp) takes token tt*16 + col, channels
+// c*32 + 8*grp .. +7 -- its A operand of S = K q^T.
 template <int D, int P>
-__device__ __forceinline__ void load_page(PageRegs<D, P> &pr, const uint16_t *__restrict__ kp,
-                                         const uint16_t *__restrict__ vp, int col, int grp) {
+__device__ __forceinline__ void load_k(PageRegs<D, P> &pr, const uint16_t *__restrict__ kp,
+                                       int col, int grp) {
 #pragma unroll
-  for (int tt = 0; tt < PageRegs<D, P>::TT; ++tt) {
+  for (int tt = 0; tt < PageRegs<D, P>::TT; ++tt)
 #pragma unroll
     for (int c = 0; c < PageRegs<D, P>::KC; ++c)
       pr.k[tt][c] = *(const uint4 *)(kp + (tt * 16 + col) * D + c * 32 + grp * 8);
+}
+
+// V (dim-major): lane (col, grp) takes channel nt*16 + col, tokens
+// tt*16 + 4*grp .. +3 -- its A operand of O^T = V^T P^T.
+template <int D, int P>
+__device__ __forceinline__ void load_v(PageRegs<D, P> &pr, const uint16_t *__restrict__ vp,
+                                       int col, int grp) {
+#pragma unroll
+  for (int tt = 0; tt < PageRegs<D, P>::TT; ++tt)
 #pragma unroll
     for (int nt = 0; nt < PageRegs<D, P>::NT; ++nt)
       pr.v[tt][nt] = *(const uint2 *)(vp + (nt * 16 + col) * P + tt * 16 + grp * 4);
-  }
 }
 
-// One page of the online softmax for all heads of the group: logits on the
-// matrix cores, running max/sum update, rescale, then P*V on the matrix cores.
-// m and l belong to head `col`; acc rows are heads 4*grp .. 4*grp+3.
-template <int D, int P>
-__device__ __forceinline__ void attend_page(PageRegs<D, P> &cur, int valid,
-                                            const bf16x8 *qop, float scale2, int grp,
-                                            float &m, float &l, f32x4 *acc) {
+// One round of the online softmax over the NPG pages a wave holds, for all
+// heads of the group at once: the logits of every page on the matrix cores,
+// one running-max / running-sum update for the whole round, then
+// O^T += V^T P^T on the matrix cores.  Lane (col, grp) owns head `col`: its
+// running max m and sum l, and accumulator channels nt*16 + 4*grp .. +3, so
+// the rescale needs no cross-lane traffic.  valid[u] is the number of tokens
+// of page u that take part (0 for an unused slot).
+template <int D, int P, int NPG>
+__device__ __forceinline__ void attend_round(PageRegs<D, P> (&pg)[NPG], const int (&valid)[NPG],
+                                             const bf16x8 *qop, float scale2, int grp,
+                                             float &m, float &l, f32x4 *acc) {
   using PR = PageRegs<D, P>;
-  // A partial page's unwritten slots may hold anything (NaN included): zero
-  // their V values, since a zero weight times NaN is still NaN.
-  if (valid < P) {
+  constexpr float kNegInf = -__builtin_huge_valf();
+  // logits: lane holds head `col`, tokens tt*16 + 4*grp + e
+  f32x4 s[NPG][PR::TT];
+  float pmax = kNegInf;
+#pragma unroll
+  for (int u = 0; u < NPG; ++u) {
 #pragma unroll
     for (int tt = 0; tt < PR::TT; ++tt) {
-      const int t0 = tt * 16 + 4 * grp;
-      const uint32_t mx = (t0 + 0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u);
-      const uint32_t my = (t0 + 2 < valid ? 0x0000ffffu : 0u) | (t0 + 3 < valid ? 0xffff0000u : 0u);
+      f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < PR::NT; ++nt) {
-        cur.v[tt][nt].x &= mx;
-        cur.v[tt][nt].y &= my;
+      for (int c = 0; c < PR::KC; ++c)
+        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pg[u].k[tt][c]),
+                                                     qop[c], c4, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = tt * 16 + 4 * grp + e;
+        const float x = tok < valid[u] ? c4[e] * scale2 : kNegInf;
+        s[u][tt][e] = x;
+        pmax = fmaxf(pmax, x);
       }
     }
   }
-  // logits: lane holds head `col`, tokens tt*16 + 4*grp + e
-  f32x4 s[PR::TT];
-  float pmax = -__builtin_huge_valf();
-#pragma unroll
-  for (int tt = 0; tt < PR::TT; ++tt) {
-    f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < PR::KC; ++c)
-      c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[tt][c]),
-                                                   qop[c], c4, 0, 0, 0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tok = tt * 16 + 4 * grp + e;
-      const float x = tok < valid ? c4[e] * scale2 : -__builtin_huge_valf();
-      s[tt][e] = x;
-      pmax = fmaxf(pmax, x);
-    }
-  }
-  pmax = wave_max_xor(pmax, 16);
-  pmax = wave_max_xor(pmax, 32);
+  pmax = max_over_rows(pmax);
   const float m_new = fmaxf(m, pmax);
-  const float alpha = (m == -__builtin_huge_valf()) ? 0.f : exp2_fast(m - m_new);
+  // while no token has been seen m stays -inf: subtract 0 then, so every
+  // weight is exp2(-inf) = 0 rather than NaN
+  const float m_sub = (m_new == kNegInf) ? 0.f : m_new;
+  const float alpha = (m == kNegInf) ? 0.f : exp2_fast(m - m_new);
   // weights as a sum of two bf16 values (hi + lo), so the matrix-core
   // product keeps about 16 significant bits of every weight
   float psum = 0.f;
-  s16x4 phi[PR::TT], plo[PR::TT];
+  s16x4 phi[NPG][PR::TT], plo[NPG][PR::TT];
 #pragma unroll
-  for (int tt = 0; tt < PR::TT; ++tt) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = exp2_fast(s[tt][e] - m_new);
-      const uint32_t hb = f32_to_bf16_bits(p);
-      const uint32_t lb = f32_to_bf16_bits(p - bf16_bits_to_f32(hb));
-      psum += p;
-      phi[tt][e] = (short)hb;
-      plo[tt][e] = (short)lb;
-    }
-  }
-  psum += __shfl_xor(psum, 16, kWave);
-  psum += __shfl_xor(psum, 32, kWave);
-  l = l * alpha + psum;
-  m = m_new;
-  // rescale: this lane's accumulator rows are heads 4*grp .. 4*grp+3
-  float a4[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) a4[e] = __shfl(alpha, 4 * grp + e, kWave);
-#pragma unroll
-  for (int nt = 0; nt < PR::NT; ++nt) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[nt][e] *= a4[e];
+  for (int u = 0; u < NPG; ++u) {
 #pragma unroll
     for (int tt = 0; tt < PR::TT; ++tt) {
-      const s16x4 vv = __builtin_bit_cast(s16x4, cur.v[tt][nt]);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[tt], vv, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[tt], vv, acc[nt], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = exp2_fast(s[u][tt][e] - m_sub);
+        const uint32_t hb = f32_to_bf16_bits(p);
+        const uint32_t lb = f32_to_bf16_bits(p - bf16_bits_to_f32(hb));
+        psum += p;
+        phi[u][tt][e] = (short)hb;
+        plo[u][tt][e] = (short)lb;
+      }
+    }
+  }
+  psum = sum_over_rows(psum);
+  l = l * alpha + psum;
+  m = m_new;
+#pragma unroll
+  for (int nt = 0; nt < PR::NT; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[nt][e] *= alpha;
+#pragma unroll
+  for (int u = 0; u < NPG; ++u) {
+    // The slots of a partial page past its valid tokens may hold anything
+    // (NaN included): zero their V values, since a zero weight times NaN is
+    // still NaN.
+    if (valid[u] < P) {
+#pragma unroll
+      for (int tt = 0; tt < PR::TT; ++tt) {
+        const int t0 = tt * 16 + 4 * grp;
+        const uint32_t mx = (t0 + 0 < valid[u] ? 0x0000ffffu : 0u) |
+                            (t0 + 1 < valid[u] ? 0xffff0000u : 0u);
+        const uint32_t my = (t0 + 2 < valid[u] ? 0x0000ffffu : 0u) |
+                            (t0 + 3 < valid[u] ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int nt = 0; nt < PR::NT; ++nt) {
+          pg[u].v[tt][nt].x &= mx;
+          pg[u].v[tt][nt].y &= my;
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < PR::TT; ++tt) {
+#pragma unroll
+      for (int nt = 0; nt < PR::NT; ++nt) {
+        const s16x4 vv = __builtin_bit_cast(s16x4, pg[u].v[tt][nt]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, phi[u][tt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, plo[u][tt], acc[nt], 0, 0, 0);
+      }
     }
   }
 }
 
 template <int D, int P>
-__global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
+__global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
     int Hkv, int G, int64_t pool, int max_pages, int max_k, int n_split, int pps,
     float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ page_table,
@@ -177,9 +209,10 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
     const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
   using PR = PageRegs<D, P>;
   constexpr int PPW = pages_per_wave(P, D);
+  constexpr int kLdsRow = D + 4;       // padded so the 16-byte stores below spread over banks
   __shared__ float lds_m[kDecodeWaves][16];
   __shared__ float lds_l[kDecodeWaves][16];
-  __shared__ float lds_acc[kDecodeWaves][16][D];
+  __shared__ __align__(16) float lds_acc[kDecodeWaves][16][kLdsRow];
 
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: the page lookups below become scalar loads
@@ -195,7 +228,7 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   // The first round of page ids is read together with the row's count and
   // length (ids past the count are ignored below), so the chain to the first
   // K/V load is ids -> page table -> K/V.
-  constexpr int kFirst = kDecodeWaves * PPW;
+  constexpr int kRound = kDecodeWaves * PPW;
   int sel0[PPW];
 #pragma unroll
   for (int u = 0; u < PPW; ++u) {
@@ -238,7 +271,7 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   float l = 0.f;                        // running sum of head `col`
 
   // Each round, wave w takes PPW consecutive selected pages.
-  for (int base = first; base < last; base += kFirst) {
+  for (int base = first; base < last; base += kRound) {
     const int p0 = base + wave * PPW;
     int64_t phys[PPW];
     int valid[PPW];
@@ -247,7 +280,7 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
       const int i = p0 + u;
       const int j = (base == first) ? sel0[u] : sel[i < last ? i : last - 1];
       // slots past the split, or with an id outside the request, re-read the
-      // split's first page (a cache hit) and are skipped
+      // split's first page (a cache hit) with no valid token
       const bool live = i < last && j >= 0 && j < n;
       const int jj = live ? j : ((jfirst >= 0 && jfirst < n) ? jfirst : 0);
       const int64_t ph = pt[jj];
@@ -255,14 +288,17 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
       phys[u] = ok ? ph : 0;
       valid[u] = (live && ok) ? min(P, ctx - j * P) : 0;
     }
+    // all K first, then all V: the logits of the round need only the K loads
     PR pg[PPW];
 #pragma unroll
     for (int u = 0; u < PPW; ++u)
-      load_page<D, P>(pg[u], k_cache + (phys[u] * Hkv + g) * page_elems,
-                      v_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+      load_k<D, P>(pg[u], k_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
 #pragma unroll
     for (int u = 0; u < PPW; ++u)
-      if (valid[u] > 0) attend_page<D, P>(pg[u], valid[u], qop, scale2, grp, m, l, acc);
+      load_v<D, P>(pg[u], v_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+    // keep every load of the round ahead of the first wait on any of them
+    __builtin_amdgcn_sched_barrier(0);
+    attend_round<D, P, PPW>(pg, valid, qop, scale2, grp, m, l, acc);
   }
 
   // merge the waves of this work-group
@@ -272,8 +308,7 @@ __global__ __launch_bounds__(256) void sparse_decode_mfma_kernel(
   }
 #pragma unroll
   for (int nt = 0; nt < PR::NT; ++nt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lds_acc[wave][4 * grp + e][nt * 16 + col] = acc[nt][e];
+    *(f32x4 *)&lds_acc[wave][col][nt * 16 + 4 * grp] = acc[nt];
   __syncthreads();
   float *out = partial + ((int64_t)row * n_split + split) * G * (D + 2);
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
@@ -479,7 +514,7 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   const unsigned blocks = (unsigned)((long)batch * dm.Hkv * plan.n_split);
   if (dm.dtype == 1) {
 #define QUEST_DECODE(DD, PP)                                                              \
-  hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP>), dim3(blocks), dim3(256), 0, stream, \
+  hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP>), dim3(blocks), dim3(kDecodeWaves * 64), 0, stream, \
                      dm.Hkv, dm.G, dm.pool, dm.max_pages, max_k, plan.n_split,            \
                      plan.pages_per_split, scale2, (const uint16_t *)q,                   \
                      (const uint16_t *)k_cache, (const uint16_t *)v_cache, page_table,    \

@@ -10,19 +10,21 @@
 // One 1024-thread work-group per row, radix select on the 32-bit orderable
 // score keys (held in registers for rows of up to 8192 pages).  The work is a
 // handful of barrier-separated phases, each short; wave-level scans and
-// reductions use the DPP network and ballots, not LDS round trips.
+// reductions use the DPP network and ballots, not LDS round trips, and
+// cross-wave sums read one LDS word per lane.
 //  1. min and max key: every key shares the bits above the highest bit where
 //     they differ;
 //  2. refinement: an (up to) 11-bit histogram of the keys matching the known
 //     prefix, on the next bits, gives the bucket holding the k-th largest key
 //     and the count kept above it; repeated until the bucket holds at most 64
-//     keys (usually once) or the key is fully known;
-//  3. the bucket's keys are gathered into LDS and every wave ranks the
+//     keys (usually twice) or the key is fully known;
+//  3. the bucket's keys are gathered into LDS and one wave ranks the
 //     (key, page) pairs in the 64-bit order, which fixes the threshold;
 //  4. each wave walks a contiguous range of pages with ballots: a count pass,
 //     one barrier to exchange the per-wave counts, then a write pass that puts
 //     every page above the threshold, and the lowest-index pages equal to it
-//     up to the count still needed, at its ascending position.
+//     up to the count still needed, at its ascending position (lane prefixes
+//     of the ballot masks by v_mbcnt).
 #include "quest_device.h"
 #include "quest_launch.h"
 
@@ -47,11 +49,45 @@ struct TopkShared {
   uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves];
   uint32_t cand_key[kWave];
   int32_t cand_idx[kWave];
+  uint32_t cnt_gt[kTopkWaves], cnt_eq[kTopkWaves];   // per-wave output counts
   uint32_t cand_count;
   uint32_t prefix;     // known high bits of the threshold key
   uint32_t krem;       // keys still to take at or below the known prefix
   uint32_t bucket;     // keys in the chosen bucket
+  uint32_t thresh;     // the threshold key, once ranked
+  uint32_t keq;        // keys equal to it that are kept
 };
+
+// Sum of vals[w] over the waves w before `wave` (vals: kTopkWaves entries in
+// LDS): lane l < 16 reads vals[l], masked by l < wave, and row 0 sums its 16
+// lanes on the DPP network.  Uniform result.
+__device__ __forceinline__ uint32_t sum_of_earlier_waves(const uint32_t *vals, int wave) {
+  const int lane = lane_id();
+  uint32_t x = lane < wave ? vals[lane & (kTopkWaves - 1)] : 0u;
+  x += dpp_row<kRowShr1>(0u, x);
+  x += dpp_row<kRowShr2>(0u, x);
+  x += dpp_row<kRowShr4>(0u, x);
+  x += dpp_row<kRowShr8>(0u, x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+}
+
+// min and max of vals_lo[w] / vals_hi[w] over all waves, the same way.
+__device__ __forceinline__ void minmax_over_waves(const uint32_t *vals_lo,
+                                                  const uint32_t *vals_hi, uint32_t &lo,
+                                                  uint32_t &hi) {
+  const int lane = lane_id() & (kTopkWaves - 1);
+  uint32_t a = vals_lo[lane], b = vals_hi[lane];
+  a = min(a, dpp_row<kRowShr1>(a, a));
+  a = min(a, dpp_row<kRowShr2>(a, a));
+  a = min(a, dpp_row<kRowShr4>(a, a));
+  a = min(a, dpp_row<kRowShr8>(a, a));
+  b = max(b, dpp_row<kRowShr1>(b, b));
+  b = max(b, dpp_row<kRowShr2>(b, b));
+  b = max(b, dpp_row<kRowShr4>(b, b));
+  b = max(b, dpp_row<kRowShr8>(b, b));
+  lo = (uint32_t)__builtin_amdgcn_readlane((int)a, 15);
+  hi = (uint32_t)__builtin_amdgcn_readlane((int)b, 15);
+}
 
 // The bucket (of `bins` <= kBins) holding the krem-th largest counted key,
 // buckets ranked from the top: wave w owns the 128 buckets below the top
@@ -65,10 +101,7 @@ __device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t k
   const uint32_t incl = wave_incl_sum(c1 + c0);
   if (lane == kWave - 1) sh.wave_a[wave] = incl;
   __syncthreads();
-  uint32_t above = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) above += (w < wave) ? sh.wave_a[w] : 0u;
-  const uint32_t excl = above + incl - c1 - c0;
+  const uint32_t excl = sum_of_earlier_waves(sh.wave_a, wave) + incl - c1 - c0;
   if (excl < krem && krem <= excl + c1 + c0) {
     const bool upper = excl + c1 >= krem;
     sh.prefix = prefix | ((uint32_t)(upper ? b1 : b0) << shift);
@@ -158,11 +191,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
   sh.hist[2 * tid + 1] = 0;
   if (tid == 0) sh.cand_count = 0;
   __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    lo = min(lo, sh.wave_a[w]);
-    hi = max(hi, sh.wave_b[w]);
-  }
+  minmax_over_waves(sh.wave_a, sh.wave_b, lo, hi);
 
   uint32_t thresh, krem = (uint32_t)k;
   if (lo == hi) {                                     // every key equal
@@ -177,38 +206,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
       const int w = lowbit < kDigitBits ? lowbit : kDigitBits;
       const int shift = lowbit - w;
       const uint32_t bmask = (1u << w) - 1u;
+      const uint32_t himask = lowbit >= 32 ? 0u : (0xffffffffu << lowbit);
       if (!first_pass) {
         sh.hist[2 * tid] = 0;
         sh.hist[2 * tid + 1] = 0;
         __syncthreads();
       }
-      const uint64_t want = (uint64_t)prefix >> lowbit;
       if constexpr (kRegs) {
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i)
-          if (valid(i) && ((uint64_t)u[i] >> lowbit) == want)
+          if (valid(i) && ((u[i] ^ prefix) & himask) == 0u)
             atomicAdd(&sh.hist[(u[i] >> shift) & bmask], 1u);
       } else {
         for (int j = tid; j < n; j += kTopkThreads) {
           const uint32_t x = order_key(s[j]);
-          if (((uint64_t)x >> lowbit) == want) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
+          if (((x ^ prefix) & himask) == 0u) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
         }
       }
       __syncthreads();
       pick_bucket(sh, 1 << w, krem, prefix, shift);
       prefix = sh.prefix;
       krem = sh.krem;
-      count = sh.bucket;
+      count = __builtin_amdgcn_readfirstlane(sh.bucket);
       lowbit = shift;
       if (lowbit == 0 || count <= (uint32_t)kWave) break;
     }
     if (lowbit == 0) {                                // the threshold key itself
       thresh = prefix;
     } else {
-      // 3. gather the bucket; every wave ranks it (no barrier needed after)
-      const uint32_t want2 = prefix >> lowbit;
+      // 3. gather the bucket (at most 64 keys) into LDS; wave 0 ranks the
+      // (key, page) pairs in the 64-bit order and publishes the threshold
+      const uint32_t himask = 0xffffffffu << lowbit;  // 1 <= lowbit <= 31 here
       auto gather = [&](uint32_t x, int j) {
-        if ((x >> lowbit) == want2) {
+        if (((x ^ prefix) & himask) == 0u) {
           const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
           if (slot < (uint32_t)kWave) {
             sh.cand_key[slot] = x;
@@ -224,70 +254,95 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
         for (int j = tid; j < n; j += kTopkThreads) gather(order_key(s[j]), j);
       }
       __syncthreads();
-      const bool mine = (uint32_t)lane < count;
-      const uint32_t mkey = mine ? sh.cand_key[lane] : 0u;
-      const int32_t midx = mine ? sh.cand_idx[lane] : 0;
-      const uint64_t me = ((uint64_t)mkey << 32) | (0xffffffffu - (uint32_t)midx);
-      uint32_t rank = 0;
-      for (uint32_t m = 0; m < count; ++m) {
-        const uint64_t other = ((uint64_t)sh.cand_key[m] << 32) |
-                               (0xffffffffu - (uint32_t)sh.cand_idx[m]);
-        rank += other > me;
+      if (wave == 0) {
+        const bool mine = (uint32_t)lane < count;
+        const uint32_t mkey = mine ? sh.cand_key[lane] : 0u;
+        const int32_t midx = mine ? sh.cand_idx[lane] : 0;
+        // rank = candidates before this one: a larger key, or the same key
+        // at a lower page
+        uint32_t rank = 0;
+        for (uint32_t m = 0; m < count; ++m) {
+          const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mkey, (int)m);
+          const int32_t oi = __builtin_amdgcn_readlane(midx, (int)m);
+          rank += (ok > mkey || (ok == mkey && oi < midx)) ? 1u : 0u;
+        }
+        const uint64_t hit = __ballot(mine && rank == krem - 1);
+        const int tl = (int)__ffsll((unsigned long long)hit) - 1;
+        const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)mkey, tl);
+        const int32_t tidx = __builtin_amdgcn_readlane(midx, tl);
+        // equal-key pairs at or above the threshold pair
+        const uint64_t eq = __ballot(mine && mkey == th && midx <= tidx);
+        if (lane == 0) {
+          sh.thresh = th;
+          sh.keq = (uint32_t)__popcll(eq);
+        }
       }
-      const uint64_t hit = __ballot(mine && rank == krem - 1);
-      const int tl = (int)__ffsll((unsigned long long)hit) - 1;
-      thresh = (uint32_t)__builtin_amdgcn_readlane((int)mkey, tl);
-      const int32_t tidx = __builtin_amdgcn_readlane(midx, tl);
-      // equal-key pairs at or above the threshold pair
-      const uint64_t eq = __ballot(mine && mkey == thresh && midx <= tidx);
-      krem = (uint32_t)__popcll(eq);
+      __syncthreads();
+      thresh = sh.thresh;
+      krem = sh.keq;
     }
   }
 
-  // 4. ascending output.  Wave w owns pages [w*span, (w+1)*span), 64 at a time.
+  // 4. ascending output.  Wave w owns pages [w*span, (w+1)*span), 64 at a
+  // time: a pass of ballots counts the wave's kept pages (above the
+  // threshold, and equal to it), one barrier exchanges the counts, and a
+  // second pass writes every kept page at its position, with lane prefixes
+  // of the ballot masks from v_mbcnt.  Register rows keep the masks from the
+  // first pass; long rows recompute them.
   const int span = kRegs ? kRegSpan : ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
   const int w0 = wave * span;
   const int iters = kRegs ? kPerThread : span / kWave;
-  const uint64_t below = (1ull << lane) - 1ull;
-  auto key_at = [&](int i, int j) -> uint32_t {
-    if constexpr (kRegs) return u[i];
-    else return j < n ? order_key(s[j]) : 0u;
+  auto masks = [&](int i, uint64_t &mg, uint64_t &me) {
+    const int j = w0 + i * kWave + lane;
+    uint32_t x;
+    if constexpr (kRegs) x = u[i];
+    else x = j < n ? order_key(s[j]) : 0u;
+    mg = __ballot(j < n && x > thresh);
+    me = __ballot(j < n && x == thresh);
   };
+  constexpr int kSaved = kRegs ? kPerThread : 1;
+  uint64_t sg[kSaved], se[kSaved];
   uint32_t gt_w = 0, eq_w = 0;
 #pragma unroll
   for (int i = 0; i < iters; ++i) {
-    const int j = w0 + i * kWave + lane;
-    const uint32_t x = key_at(i, j);
-    gt_w += (uint32_t)__popcll(__ballot(j < n && x > thresh));
-    eq_w += (uint32_t)__popcll(__ballot(j < n && x == thresh));
+    uint64_t mg, me;
+    masks(i, mg, me);
+    if constexpr (kRegs) {
+      sg[i] = mg;
+      se[i] = me;
+    }
+    gt_w += (uint32_t)__popcll(mg);
+    eq_w += (uint32_t)__popcll(me);
   }
-  __syncthreads();                                    // wave_a/b free again
   if (lane == 0) {
-    sh.wave_a[wave] = gt_w;
-    sh.wave_b[wave] = eq_w;
+    sh.cnt_gt[wave] = gt_w;
+    sh.cnt_eq[wave] = eq_w;
   }
   __syncthreads();
-  uint32_t gt_b = 0, eq_b = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    gt_b += (w < wave) ? sh.wave_a[w] : 0u;
-    eq_b += (w < wave) ? sh.wave_b[w] : 0u;
-  }
+  uint32_t gt_b = sum_of_earlier_waves(sh.cnt_gt, wave);
+  uint32_t eq_b = sum_of_earlier_waves(sh.cnt_eq, wave);
 #pragma unroll
   for (int i = 0; i < iters; ++i) {
-    const int j = w0 + i * kWave + lane;
-    const uint32_t x = key_at(i, j);
-    const bool is_gt = j < n && x > thresh;
-    const bool is_eq = j < n && x == thresh;
-    const uint64_t mgt = __ballot(is_gt), meq = __ballot(is_eq);
-    const uint32_t gt_before = gt_b + (uint32_t)__popcll(mgt & below);
-    const uint32_t eq_before = eq_b + (uint32_t)__popcll(meq & below);
+    uint64_t mg, me;
+    if constexpr (kRegs) {
+      mg = sg[i];
+      me = se[i];
+    } else {
+      masks(i, mg, me);
+    }
+    // kept pages of this wave before this lane, plus those of earlier waves
+    const uint32_t gt_before =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, gt_b));
+    const uint32_t eq_before =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, eq_b));
+    const bool is_gt = (mg >> lane) & 1ull;
+    const bool is_eq = (me >> lane) & 1ull;
     if (is_gt || (is_eq && eq_before < krem)) {
       const uint32_t pos = gt_before + min(eq_before, krem);
-      if (pos < (uint32_t)k) out[pos] = j;            // never past the row
+      if (pos < (uint32_t)k) out[pos] = w0 + i * kWave + lane;   // never past the row
     }
-    gt_b += (uint32_t)__popcll(mgt);
-    eq_b += (uint32_t)__popcll(meq);
+    gt_b += (uint32_t)__popcll(mg);
+    eq_b += (uint32_t)__popcll(me);
   }
 }
 
