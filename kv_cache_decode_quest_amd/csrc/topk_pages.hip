@@ -34,8 +34,9 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kBinsPerWave = kBins / kTopkWaves;     // 128: two per lane
-static_assert(kBinsPerWave == 2 * kWave, "each lane owns two histogram buckets");
+constexpr int kBinsPerLane = kBins / kTopkThreads;   // each lane owns this many buckets
+constexpr int kBinsPerWave = kBinsPerLane * kWave;
+static_assert(kBinsPerLane * kTopkThreads == kBins && kTopkWaves <= 16, "bucket ownership");
 
 // Larger score <-> larger key; -0.0 and +0.0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -54,8 +55,9 @@ struct TopkShared {
   uint32_t prefix;     // known high bits of the threshold key
   uint32_t krem;       // keys still to take at or below the known prefix
   uint32_t bucket;     // keys in the chosen bucket
-  uint32_t thresh;     // the threshold key, once ranked
-  uint32_t keq;        // keys equal to it that are kept
+  uint32_t thresh;     // the threshold pair (key, page), once ranked
+  int32_t tidx;
+  uint32_t keq;        // keys equal to the threshold key that are kept
 };
 
 // Sum of vals[w] over the waves w before `wave` (vals: kTopkWaves entries in
@@ -90,33 +92,41 @@ __device__ __forceinline__ void minmax_over_waves(const uint32_t *vals_lo,
 }
 
 // The bucket (of `bins` <= kBins) holding the krem-th largest counted key,
-// buckets ranked from the top: wave w owns the 128 buckets below the top
-// 128*w, lane l two of them.  Results in sh.prefix / sh.krem / sh.bucket.
+// buckets ranked from the top: wave w owns the kBinsPerWave buckets below the
+// top kBinsPerWave*w, lane l kBinsPerLane of them.  Results in sh.prefix /
+// sh.krem / sh.bucket.
 __device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t krem,
                                             uint32_t prefix, int shift) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int b1 = bins - 1 - kBinsPerWave * wave - 2 * lane, b0 = b1 - 1;
-  const uint32_t c1 = b1 >= 0 ? sh.hist[b1] : 0u;
-  const uint32_t c0 = b0 >= 0 ? sh.hist[b0] : 0u;
-  const uint32_t incl = wave_incl_sum(c1 + c0);
+  const int top = bins - 1 - kBinsPerWave * wave - kBinsPerLane * lane;
+  uint32_t c[kBinsPerLane], total = 0;
+#pragma unroll
+  for (int e = 0; e < kBinsPerLane; ++e) {
+    c[e] = top - e >= 0 ? sh.hist[top - e] : 0u;
+    total += c[e];
+  }
+  const uint32_t incl = wave_incl_sum(total);
   if (lane == kWave - 1) sh.wave_a[wave] = incl;
   __syncthreads();
-  const uint32_t excl = sum_of_earlier_waves(sh.wave_a, wave) + incl - c1 - c0;
-  if (excl < krem && krem <= excl + c1 + c0) {
-    const bool upper = excl + c1 >= krem;
-    sh.prefix = prefix | ((uint32_t)(upper ? b1 : b0) << shift);
-    sh.krem = krem - (upper ? excl : excl + c1);
-    sh.bucket = upper ? c1 : c0;
+  uint32_t run = sum_of_earlier_waves(sh.wave_a, wave) + incl - total;   // keys above `top`
+#pragma unroll
+  for (int e = 0; e < kBinsPerLane; ++e) {
+    if (run < krem && krem <= run + c[e]) {
+      sh.prefix = prefix | ((uint32_t)(top - e) << shift);
+      sh.krem = krem - run;
+      sh.bucket = c[e];
+    }
+    run += c[e];
   }
   __syncthreads();
 }
 
 // Rows of up to kRegKeys pages are read from HBM once, into registers: wave w
-// holds pages [512 w, 512 w + 512), lane l pages 512 w + 64 i + l (i < 8), the
-// same wave-contiguous order the output pass needs, so no pass re-reads
-// memory.  Longer rows read their scores from global memory in every pass.
-constexpr int kPerThread = 8;
-constexpr int kRegKeys = kPerThread * kTopkThreads;      // 8192
+// holds pages [S w, S w + S) with S = kRegSpan, lane l pages S w + 64 i + l
+// (i < kPerThread), the same wave-contiguous order the output pass needs, so
+// no pass re-reads memory.  Longer rows read their scores from global memory in every pass.
+constexpr int kRegKeys = 8192;
+constexpr int kPerThread = kRegKeys / kTopkThreads;
 constexpr int kRegSpan = kPerThread * kWave;              // pages per wave
 
 template <bool kRegs>
@@ -126,8 +136,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel) {
   __shared__ TopkShared sh;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int row = blockIdx.x;
-  const int r = row / Hkv;
+  // grid (KV head, request): no division by runtime values
+  const int r = blockIdx.y;
+  const int row = r * Hkv + (int)blockIdx.x;
+  const int log2p = __builtin_ctz(P);                 // the page size is a power of two
   const float *s = scores + (int64_t)row * max_pages;
   // Register rows: the whole score row is loaded in the same round trip as
   // the request's length and budget (entries past the length are ignored).
@@ -139,10 +151,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
       sv[i] = s[j < max_pages ? j : 0];
     }
   }
-  const int n = pages_in(ctx_lens[r], P, max_pages);
+  const int ctx = ctx_lens[r];
+  const int n = ctx <= 0 ? 0 : min((ctx + P - 1) >> log2p, max_pages);
   int k = 0;
   if (n > 0) {
-    k = budget_tokens[r] / P;
+    k = budget_tokens[r] >> log2p;                    // floor; negatives clamp to 1 below
     k = k < 1 ? 1 : (k > n ? n : k);
     k = k < max_k ? k : max_k;
   }
@@ -187,108 +200,145 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     sh.wave_a[wave] = lo;
     sh.wave_b[wave] = hi;
   }
-  sh.hist[2 * tid] = 0;
-  sh.hist[2 * tid + 1] = 0;
+#pragma unroll
+  for (int e = 0; e < kBinsPerLane; ++e) sh.hist[kBinsPerLane * tid + e] = 0;
   if (tid == 0) sh.cand_count = 0;
   __syncthreads();
   minmax_over_waves(sh.wave_a, sh.wave_b, lo, hi);
 
   uint32_t thresh, krem = (uint32_t)k;
-  if (lo == hi) {                                     // every key equal
-    thresh = lo;
-  } else {
-    // 2. refine the threshold key, 11 bits at a time
-    const int hb = 31 - __builtin_clz(lo ^ hi);
-    int lowbit = hb + 1;                              // bits >= lowbit are known
-    uint32_t prefix = (uint32_t)(((uint64_t)hi >> lowbit) << lowbit);
-    uint32_t count;
-    for (bool first_pass = true;; first_pass = false) {
-      const int w = lowbit < kDigitBits ? lowbit : kDigitBits;
-      const int shift = lowbit - w;
-      const uint32_t bmask = (1u << w) - 1u;
-      const uint32_t himask = lowbit >= 32 ? 0u : (0xffffffffu << lowbit);
-      if (!first_pass) {
-        sh.hist[2 * tid] = 0;
-        sh.hist[2 * tid + 1] = 0;
-        __syncthreads();
-      }
-      if constexpr (kRegs) {
+  if (lo == hi) {                                     // every key equal: the first k pages
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i;
+    return;
+  }
+  // 2. refine the threshold key, 11 bits at a time
+  const int hb = 31 - __builtin_clz(lo ^ hi);
+  int lowbit = hb + 1;                                // bits >= lowbit are known
+  uint32_t prefix = (uint32_t)(((uint64_t)hi >> lowbit) << lowbit);
+  uint32_t count;
+  for (bool first_pass = true;; first_pass = false) {
+    const int w = lowbit < kDigitBits ? lowbit : kDigitBits;
+    const int shift = lowbit - w;
+    const uint32_t bmask = (1u << w) - 1u;
+    const uint32_t himask = lowbit >= 32 ? 0u : (0xffffffffu << lowbit);
+    if (!first_pass) {
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i)
-          if (valid(i) && ((u[i] ^ prefix) & himask) == 0u)
-            atomicAdd(&sh.hist[(u[i] >> shift) & bmask], 1u);
-      } else {
-        for (int j = tid; j < n; j += kTopkThreads) {
-          const uint32_t x = order_key(s[j]);
-          if (((x ^ prefix) & himask) == 0u) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
-        }
-      }
+      for (int e = 0; e < kBinsPerLane; ++e) sh.hist[kBinsPerLane * tid + e] = 0;
       __syncthreads();
-      pick_bucket(sh, 1 << w, krem, prefix, shift);
-      prefix = sh.prefix;
-      krem = sh.krem;
-      count = __builtin_amdgcn_readfirstlane(sh.bucket);
-      lowbit = shift;
-      if (lowbit == 0 || count <= (uint32_t)kWave) break;
     }
-    if (lowbit == 0) {                                // the threshold key itself
-      thresh = prefix;
+    if constexpr (kRegs) {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i)
+        if (valid(i) && ((u[i] ^ prefix) & himask) == 0u)
+          atomicAdd(&sh.hist[(u[i] >> shift) & bmask], 1u);
     } else {
-      // 3. gather the bucket (at most 64 keys) into LDS; wave 0 ranks the
-      // (key, page) pairs in the 64-bit order and publishes the threshold
-      const uint32_t himask = 0xffffffffu << lowbit;  // 1 <= lowbit <= 31 here
-      auto gather = [&](uint32_t x, int j) {
-        if (((x ^ prefix) & himask) == 0u) {
-          const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
-          if (slot < (uint32_t)kWave) {
-            sh.cand_key[slot] = x;
-            sh.cand_idx[slot] = j;
-          }
-        }
-      };
-      if constexpr (kRegs) {
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i)
-          if (valid(i)) gather(u[i], wave * kRegSpan + i * kWave + lane);
-      } else {
-        for (int j = tid; j < n; j += kTopkThreads) gather(order_key(s[j]), j);
+      for (int j = tid; j < n; j += kTopkThreads) {
+        const uint32_t x = order_key(s[j]);
+        if (((x ^ prefix) & himask) == 0u) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
       }
-      __syncthreads();
-      if (wave == 0) {
-        const bool mine = (uint32_t)lane < count;
-        const uint32_t mkey = mine ? sh.cand_key[lane] : 0u;
-        const int32_t midx = mine ? sh.cand_idx[lane] : 0;
-        // rank = candidates before this one: a larger key, or the same key
-        // at a lower page
-        uint32_t rank = 0;
-        for (uint32_t m = 0; m < count; ++m) {
-          const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mkey, (int)m);
-          const int32_t oi = __builtin_amdgcn_readlane(midx, (int)m);
-          rank += (ok > mkey || (ok == mkey && oi < midx)) ? 1u : 0u;
-        }
-        const uint64_t hit = __ballot(mine && rank == krem - 1);
-        const int tl = (int)__ffsll((unsigned long long)hit) - 1;
-        const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)mkey, tl);
-        const int32_t tidx = __builtin_amdgcn_readlane(midx, tl);
-        // equal-key pairs at or above the threshold pair
-        const uint64_t eq = __ballot(mine && mkey == th && midx <= tidx);
-        if (lane == 0) {
-          sh.thresh = th;
-          sh.keq = (uint32_t)__popcll(eq);
-        }
-      }
-      __syncthreads();
-      thresh = sh.thresh;
-      krem = sh.keq;
     }
+    __syncthreads();
+    pick_bucket(sh, 1 << w, krem, prefix, shift);
+    prefix = sh.prefix;
+    krem = sh.krem;
+    count = __builtin_amdgcn_readfirstlane(sh.bucket);
+    lowbit = shift;
+    if (lowbit == 0 || count <= (uint32_t)kWave) break;
+  }
+  if (lowbit == 0) {                                  // the threshold key itself
+    thresh = prefix;
+  } else {
+    // 3. gather the bucket (at most 64 keys) into LDS; wave 0 ranks the
+    // (key, page) pairs in the 64-bit order and publishes the threshold pair.
+    // Register rows also count, per wave, the keys above the bucket: all of
+    // them are kept.
+    const uint32_t himask = 0xffffffffu << lowbit;    // 1 <= lowbit <= 31 here
+    const uint32_t bucket_top = prefix | ~himask;     // largest key of the bucket
+    auto gather = [&](uint32_t x, int j) {
+      if (((x ^ prefix) & himask) == 0u) {
+        const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
+        if (slot < (uint32_t)kWave) {
+          sh.cand_key[slot] = x;
+          sh.cand_idx[slot] = j;
+        }
+      }
+    };
+    if constexpr (kRegs) {
+      uint32_t above = 0;
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        if (valid(i)) gather(u[i], wave * kRegSpan + i * kWave + lane);
+        above += (uint32_t)__popcll(__ballot(valid(i) && u[i] > bucket_top));
+      }
+      if (lane == 0) sh.cnt_gt[wave] = above;
+    } else {
+      for (int j = tid; j < n; j += kTopkThreads) gather(order_key(s[j]), j);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const bool mine = (uint32_t)lane < count;
+      const uint32_t mkey = mine ? sh.cand_key[lane] : 0u;
+      const int32_t midx = mine ? sh.cand_idx[lane] : 0;
+      // rank = candidates before this one: a larger key, or the same key
+      // at a lower page
+      uint32_t rank = 0;
+      for (uint32_t m = 0; m < count; ++m) {
+        const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mkey, (int)m);
+        const int32_t oi = __builtin_amdgcn_readlane(midx, (int)m);
+        rank += (ok > mkey || (ok == mkey && oi < midx)) ? 1u : 0u;
+      }
+      const uint64_t hit = __ballot(mine && rank == krem - 1);
+      const int tl = (int)__ffsll((unsigned long long)hit) - 1;
+      const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)mkey, tl);
+      const int32_t tidx = __builtin_amdgcn_readlane(midx, tl);
+      // equal-key pairs at or above the threshold pair
+      const uint64_t eq = __ballot(mine && mkey == th && midx <= tidx);
+      if (lane == 0) {
+        sh.thresh = th;
+        sh.tidx = tidx;
+        sh.keq = (uint32_t)__popcll(eq);
+      }
+    }
+    __syncthreads();
+    thresh = sh.thresh;
+    if constexpr (kRegs) {
+      // 4a. ascending output in one pass.  A page is kept iff its (key, page)
+      // pair is at or above the threshold pair.  This wave's first position:
+      // the kept pages of earlier waves = their keys above the bucket plus
+      // the kept candidates at a lower page than this wave's range.
+      const int32_t tidx = (int32_t)sh.tidx;
+      const int w0 = wave * kRegSpan;
+      const bool cmine = (uint32_t)lane < count;
+      const uint32_t ck = cmine ? sh.cand_key[lane] : 0u;
+      const int32_t ci = cmine ? sh.cand_idx[lane] : 0;
+      const bool ckept = cmine && (ck > thresh || (ck == thresh && ci <= tidx));
+      uint32_t pos0 = sum_of_earlier_waves(sh.cnt_gt, wave) +
+                      (uint32_t)__popcll(__ballot(ckept && ci < w0));
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        const int j = w0 + i * kWave + lane;
+        const uint32_t x = u[i];
+        const bool kept = j < n && (x > thresh || (x == thresh && j <= tidx));
+        const uint64_t m = __ballot(kept);
+        if (kept) {
+          const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos0));
+          if (pos < (uint32_t)k) out[pos] = j;        // never past the row
+        }
+        pos0 += (uint32_t)__popcll(m);
+      }
+      return;
+    }
+    krem = sh.keq;
   }
 
-  // 4. ascending output.  Wave w owns pages [w*span, (w+1)*span), 64 at a
-  // time: a pass of ballots counts the wave's kept pages (above the
-  // threshold, and equal to it), one barrier exchanges the counts, and a
-  // second pass writes every kept page at its position, with lane prefixes
-  // of the ballot masks from v_mbcnt.  Register rows keep the masks from the
-  // first pass; long rows recompute them.
+  // 4b. ascending output for long rows, and for ties at a fully known key.
+  // Wave w owns pages [w*span, (w+1)*span), 64 at a time: a pass of ballots
+  // counts the wave's kept pages (above the threshold key, and equal to it),
+  // one barrier exchanges the counts, and a second pass writes every kept
+  // page at its position, with lane prefixes of the ballot masks from
+  // v_mbcnt.  Register rows keep the masks from the first pass; long rows
+  // recompute them.
   const int span = kRegs ? kRegSpan : ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
   const int w0 = wave * span;
   const int iters = kRegs ? kPerThread : span / kWave;
@@ -350,7 +400,7 @@ hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        const int32_t *ctx_lens, const int32_t *budget_tokens,
                        int max_k, int32_t *sel_pages, int32_t *num_sel,
                        hipStream_t stream) {
-  dim3 grid((unsigned)(batch * dm.Hkv));
+  dim3 grid((unsigned)dm.Hkv, (unsigned)batch);
   if (dm.max_pages <= kRegKeys)
     hipLaunchKernelGGL(topk_pages_kernel<true>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
                        dm.P, dm.max_pages, max_k, scores, ctx_lens, budget_tokens, sel_pages,

@@ -193,7 +193,7 @@ def _topk_rows(n_max, gen):
     return rows
 
 
-@pytest.mark.parametrize("n_max,P", [(64, 16), (300, 16), (2050, 32), (8008, 16)])
+@pytest.mark.parametrize("n_max,P", [(64, 16), (300, 16), (2050, 32), (8008, 16), (10000, 16)])
 def test_topk_exact(n_max, P, gpu_lib):
     gen = torch.Generator().manual_seed(5000 + n_max)
     rows = _topk_rows(n_max, gen)
