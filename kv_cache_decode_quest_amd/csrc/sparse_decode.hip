@@ -45,6 +45,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 __host__ __device__ constexpr int pages_per_wave(int P, int D) {
   return (P * D <= 2048) ? 4 : 2;
 }
+// Pages folded into the running softmax per update.  The loads of a round
+// are issued group by group (K then V of each group), so a group's update
+// can start while later groups are still in flight.
+constexpr int kPagesPerUpdate = 2;
 
 DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
   DecodePlan p{1, max_k > 0 ? max_k : 1};
@@ -65,6 +69,19 @@ size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A pair of fp32 weights as packed bf16 hi = RNE(p) and lo = RNE(p - hi),
+// each pair converted by one v_cvt_pk_bf16_f32 (round to nearest even).
+__device__ __forceinline__ void split_bf16x2(float p0, float p1, uint32_t &hi, uint32_t &lo) {
+  const bf16x2 h = {(__bf16)p0, (__bf16)p1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float r0 = p0 - __uint_as_float(hi << 16);
+  const float r1 = p1 - __uint_as_float(hi & 0xffff0000u);
+  const bf16x2 lw = {(__bf16)r0, (__bf16)r1};
+  lo = __builtin_bit_cast(uint32_t, lw);
+}
 
 // ---------------------------------------------------------------------------
 // bf16 matrix-core kernel
@@ -109,13 +126,19 @@ __device__ __forceinline__ void load_v(PageRegs<D, P> &pr, const uint16_t *__res
 // running max m and sum l, and accumulator channels nt*16 + 4*grp .. +3, so
 // the rescale needs no cross-lane traffic.  valid[u] is the number of tokens
 // of page u that take part (0 for an unused slot).
-template <int D, int P, int NPG>
-__device__ __forceinline__ void attend_round(PageRegs<D, P> (&pg)[NPG], const int (&valid)[NPG],
-                                             const bf16x8 *qop, float scale2, int grp,
+//
+// kPack (groups of at most 8 heads): columns 8..15 of the products carry no
+// head, so lane (col >= 8) takes over the logits of head col - 8 (one DPP
+// row shift) and feeds that head's lo weights to the second product while
+// lane col - 8 feeds the hi weights: one matrix-core step per tile instead of
+// two, and accumulator columns h and h + 8 add up to head h.
+template <int D, int P, int NPG, bool kPack>
+__device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *valid,
+                                             const bf16x8 *qop, float scale2, int col, int grp,
                                              float &m, float &l, f32x4 *acc) {
   using PR = PageRegs<D, P>;
   constexpr float kNegInf = -__builtin_huge_valf();
-  // logits: lane holds head `col`, tokens tt*16 + 4*grp + e
+  // logits: lane holds head `col` (kPack: head col mod 8), tokens tt*16 + 4*grp + e
   f32x4 s[NPG][PR::TT];
   float pmax = kNegInf;
 #pragma unroll
@@ -127,13 +150,23 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> (&pg)[NPG], const in
       for (int c = 0; c < PR::KC; ++c)
         c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pg[u].k[tt][c]),
                                                      qop[c], c4, 0, 0, 0);
+      if constexpr (kPack) {
+        // lanes 8..15 of each row take lanes 0..7's values; lanes 0..7 have
+        // no source 8 lanes below inside the row and keep their own
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = tt * 16 + 4 * grp + e;
-        const float x = tok < valid[u] ? c4[e] * scale2 : kNegInf;
-        s[u][tt][e] = x;
-        pmax = fmaxf(pmax, x);
+        for (int e = 0; e < 4; ++e)
+          c4[e] = __uint_as_float(dpp_row<kRowShr8>(__float_as_uint(c4[e]), __float_as_uint(c4[e])));
       }
+      if (valid[u] >= P) {                 // a full page (uniform branch)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[u][tt][e] = c4[e] * scale2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[u][tt][e] = tt * 16 + 4 * grp + e < valid[u] ? c4[e] * scale2 : kNegInf;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pmax = fmaxf(pmax, s[u][tt][e]);
     }
   }
   pmax = max_over_rows(pmax);
@@ -150,15 +183,17 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> (&pg)[NPG], const in
   for (int u = 0; u < NPG; ++u) {
 #pragma unroll
     for (int tt = 0; tt < PR::TT; ++tt) {
+      float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2_fast(s[u][tt][e] - m_sub);
-        const uint32_t hb = f32_to_bf16_bits(p);
-        const uint32_t lb = f32_to_bf16_bits(p - bf16_bits_to_f32(hb));
-        psum += p;
-        phi[u][tt][e] = (short)hb;
-        plo[u][tt][e] = (short)lb;
+        p[e] = exp2_fast(s[u][tt][e] - m_sub);
+        psum += p[e];
       }
+      uint32_t h01, l01, h23, l23;
+      split_bf16x2(p[0], p[1], h01, l01);
+      split_bf16x2(p[2], p[3], h23, l23);
+      phi[u][tt] = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
+      plo[u][tt] = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
     }
   }
   psum = sum_over_rows(psum);
@@ -193,14 +228,19 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> (&pg)[NPG], const in
 #pragma unroll
       for (int nt = 0; nt < PR::NT; ++nt) {
         const s16x4 vv = __builtin_bit_cast(s16x4, pg[u].v[tt][nt]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, phi[u][tt], acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, plo[u][tt], acc[nt], 0, 0, 0);
+        if constexpr (kPack) {
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, col < 8 ? phi[u][tt] : plo[u][tt],
+                                                              acc[nt], 0, 0, 0);
+        } else {
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, phi[u][tt], acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, plo[u][tt], acc[nt], 0, 0, 0);
+        }
       }
     }
   }
 }
 
-template <int D, int P>
+template <int D, int P, bool kPack>
 __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
     int Hkv, int G, int64_t pool, int max_pages, int max_k, int n_split, int pps,
     float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
@@ -288,17 +328,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
       phys[u] = ok ? ph : 0;
       valid[u] = (live && ok) ? min(P, ctx - j * P) : 0;
     }
-    // all K first, then all V: the logits of the round need only the K loads
+    // per update group: all K, then all V (the logits need only the K loads)
+    constexpr int UPG = kPagesPerUpdate < PPW ? kPagesPerUpdate : PPW;
     PR pg[PPW];
 #pragma unroll
-    for (int u = 0; u < PPW; ++u)
-      load_k<D, P>(pg[u], k_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+    for (int g0 = 0; g0 < PPW; g0 += UPG) {
 #pragma unroll
-    for (int u = 0; u < PPW; ++u)
-      load_v<D, P>(pg[u], v_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+      for (int u = g0; u < g0 + UPG; ++u)
+        load_k<D, P>(pg[u], k_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+#pragma unroll
+      for (int u = g0; u < g0 + UPG; ++u)
+        load_v<D, P>(pg[u], v_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+    }
     // keep every load of the round ahead of the first wait on any of them
     __builtin_amdgcn_sched_barrier(0);
-    attend_round<D, P, PPW>(pg, valid, qop, scale2, grp, m, l, acc);
+#pragma unroll
+    for (int g0 = 0; g0 < PPW; g0 += UPG)
+      attend_round<D, P, UPG, kPack>(pg + g0, valid + g0, qop, scale2, col, grp, m, l, acc);
   }
 
   // merge the waves of this work-group
@@ -321,7 +367,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
     for (int w = 0; w < kDecodeWaves; ++w) {
       const float mw = lds_m[w][h];
       const float f = (mw == -__builtin_huge_valf()) ? 0.f : exp2_fast(mw - M);
-      a += f * lds_acc[w][h][d];
+      const float aw = kPack ? lds_acc[w][h][d] + lds_acc[w][h + 8][d] : lds_acc[w][h][d];
+      a += f * aw;
       L += f * lds_l[w][h];
     }
     float *ph = out + h * (D + 2);
@@ -514,7 +561,12 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   const unsigned blocks = (unsigned)((long)batch * dm.Hkv * plan.n_split);
   if (dm.dtype == 1) {
 #define QUEST_DECODE(DD, PP)                                                              \
-  hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP>), dim3(blocks), dim3(kDecodeWaves * 64), 0, stream, \
+  do {                                                                                    \
+    if (dm.G <= 8) QUEST_DECODE_G(DD, PP, true);                                          \
+    else QUEST_DECODE_G(DD, PP, false);                                                   \
+  } while (0)
+#define QUEST_DECODE_G(DD, PP, PK)                                                        \
+  hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP, PK>), dim3(blocks), dim3(kDecodeWaves * 64), 0, stream, \
                      dm.Hkv, dm.G, dm.pool, dm.max_pages, max_k, plan.n_split,            \
                      plan.pages_per_split, scale2, (const uint16_t *)q,                   \
                      (const uint16_t *)k_cache, (const uint16_t *)v_cache, page_table,    \
@@ -524,6 +576,7 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
     else if (dm.D == 64 && dm.P == 16) QUEST_DECODE(64, 16);
     else QUEST_DECODE(64, 32);
 #undef QUEST_DECODE
+#undef QUEST_DECODE_G
   } else {
     const size_t lds = sizeof(float) * ((size_t)dm.G * dm.D + 2 * (size_t)dm.P * dm.D +
                                         (size_t)dm.G * dm.P + 3 * (size_t)dm.G);

@@ -39,6 +39,11 @@ SMALL = {
     "f32_g1": workloads.Workload("f32_g1", 2, 2, 2, 128, 32, "f32", ctx=2100,
                                  budget_tokens=300, steps=2, seed=79, permute_pages=True,
                                  poison=1e4),
+    # groups wider than 8 q heads (every head column of the matrix-core tiles in use)
+    "g16_p32": workloads.Workload("g16_p32", 3, 32, 2, 128, 32, "bf16", ctx=3000,
+                                  budget_tokens=600, steps=2, seed=80, poison=float("nan")),
+    "g12_d64": workloads.Workload("g12_d64", 2, 24, 2, 64, 16, "bf16", ctx_list=(500, 2000),
+                                  budget_tokens=256, steps=2, seed=81, permute_pages=True),
 }
 
 
