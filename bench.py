@@ -95,6 +95,48 @@ def run_step(layer, bufs, s, inp, ctx_before, ctx_after, budgets, sm, events=Non
         events[4].record()
 
 
+def dense_reference(layer, inputs, ctx_b, ctx_a, sm, evict, n_steps, dev):
+    """The vanilla decode step on the same pool, timed like the sparse step:
+    append one token per request, then the same decode kernel over every page
+    of every request (no scoring, no top-k).  Bytes = all valid K/V."""
+    w, L = layer.w, layer.L
+    B, H = w.batch, w.num_kv_heads
+    max_k = layer.lay.max_pages
+    bufs = quest.alloc_decode_buffers(L, B, max_k, dev)
+    bufs.sel_pages.copy_(torch.arange(max_k, dtype=torch.int32, device=dev).expand(B, H, max_k))
+    nsel = [((c.to(torch.int64) + w.page_size - 1) // w.page_size).to(torch.int32)
+            .view(B, 1).expand(B, H).contiguous().to(dev) for c in ctx_a[:n_steps]]
+
+    def step(s):
+        q, k_new, v_new = inputs[s]
+        quest.quest_append_kv(L, k_new, v_new, layer.cu1, ctx_b[s], 1, layer.pt, layer.k_cache,
+                              layer.v_cache, layer.kmeta)
+        quest.quest_sparse_decode(L, q, layer.k_cache, layer.v_cache, layer.pt, ctx_a[s],
+                                  bufs.sel_pages, nsel[s], max_k, sm, bufs.out, bufs.workspace)
+
+    for s in range(min(2, n_steps)):
+        step(s)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for s in range(n_steps):
+        evict()
+        ev[s][0].record()
+        step(s)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    total_s = sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3
+    elem = 2 if w.dtype == "bf16" else 4
+    kv_bytes = sum(int(c.sum()) for c in ctx_a[:n_steps]) * H * 2 * w.head_dim * elem
+    plan = quest.quest_sparse_decode_plan(L, B, max_k)
+    return {"what": "the same decode kernel over every page of every request (no scoring, no "
+                    "top-k), one token appended per request; cache evicted before each step",
+            "tokens_per_s": B * n_steps / total_s, "ms_per_step": total_s / n_steps * 1e3,
+            "steps": n_steps, "kv_bytes_per_step": kv_bytes / n_steps,
+            "hbm_gbps": kv_bytes / total_s / 1e9,
+            "hbm_frac_peak": kv_bytes / total_s / 1e9 / PEAK_HBM_GBPS,
+            "plan": plan}
+
+
 class Stepper:
     """Issues decode steps for the whole batch, split by request into
     contiguous chunks, one chunk per HIP stream (default priority).  Chunks
@@ -305,6 +347,9 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=24)
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense decode reference (every page, no selection)")
+    ap.add_argument("--dense-steps", type=int, default=16)
     ap.add_argument("--roofline-copies", type=int, default=8)
     ap.add_argument("--streams", type=int, default=1,
                     help="split the batch by request over this many HIP streams")
@@ -472,6 +517,14 @@ def main():
                 "note": "back-to-back steps without cache eviction: part of the metadata "
                         "is served from the Infinity Cache"}
 
+    dense = None
+    if not args.no_dense:
+        log(f"dense reference: {min(args.dense_steps, K)} steps over every page")
+        dense = dense_reference(layer, inputs, ctx_b, ctx_a, sm, evict,
+                                max(1, min(args.dense_steps, K)), dev)
+        dense["sparse_speedup"] = value / dense["tokens_per_s"]
+        restore()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, (layer.lay,) + layer.prefill, inputs,
@@ -513,6 +566,7 @@ def main():
                    "requests_per_stream": [r1 - r0 for r0, r1 in stepper.chunks]},
         "wall_s_timed_loop_incl_flush": t_wall,
         "warm": warm,
+        "dense_reference": dense,
         "cpu_baseline": cpu,
         "host": platform.node(),
     }

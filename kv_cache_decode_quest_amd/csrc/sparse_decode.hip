@@ -30,6 +30,8 @@
 // rounding error of hi), and both go through the matrix cores, so the weights
 // keep about 16 significant bits instead of bf16's 8.  Heads past G are zero
 // columns of q^T.
+#include <algorithm>
+
 #include "quest_device.h"
 #include "quest_launch.h"
 
@@ -50,12 +52,22 @@ __host__ __device__ constexpr int pages_per_wave(int P, int D) {
 // can start while later groups are still in flight.
 constexpr int kPagesPerUpdate = 2;
 
+// Work-groups the plan aims for: enough to keep every CU streaming (two
+// resident work-groups per CU at the decode's LDS size), few enough that long
+// rows take several rounds per split instead of multiplying the partials the
+// merge reads.
+constexpr long kTargetWorkGroups = 1024;
+
 DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
   DecodePlan p{1, max_k > 0 ? max_k : 1};
   if (batch <= 0 || max_k <= 0) return p;
   const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
+  const long rows = (long)batch * dm.Hkv;
+  const long want_splits = std::max(1L, (kTargetWorkGroups + rows - 1) / rows);
   long rounds = 1;
-  while ((max_k + per_round * rounds - 1) / (per_round * rounds) > kMaxSplits) ++rounds;
+  while ((max_k + per_round * rounds - 1) / (per_round * rounds) >
+         std::min((long)kMaxSplits, want_splits) && per_round * rounds < max_k)
+    ++rounds;
   const long pps = per_round * rounds;
   p.pages_per_split = (int)pps;
   p.n_split = (int)((max_k + pps - 1) / pps);

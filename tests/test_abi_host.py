@@ -159,7 +159,7 @@ def test_workspace_contract(lib):
 
 def test_plan_covers_every_page():
     """Splits cover max_k pages with no empty split, and never exceed the 256
-    splits the merge kernel holds in LDS."""
+    splits a plan may use."""
     for batch, hkv, max_k in [(1, 1, 1), (1, 1, 16), (8, 4, 256), (8, 4, 128), (32, 4, 409),
                               (64, 4, 128), (3, 2, 1000), (1, 1, 60000), (2, 4, 4097)]:
         for page_size in (16, 32):

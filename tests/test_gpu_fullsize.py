@@ -1,14 +1,15 @@
 """GPU parity at the full sizes of the ragged and 48-layer workloads, checked
 on sampled requests against the oracle (the benchmark shape itself is
-covered by test_full_bench_shape_sampled), plus hipGraph capture/replay of a
-decode step."""
+covered by test_full_bench_shape_sampled), dense decode over every page at
+the benchmark shape, plus hipGraph capture/replay of a decode step."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 import torch
 
-from helpers import to_f64
+import oracle
+from helpers import to_f64, to_oracle
 from kv_cache_decode_quest_amd import quest, workloads
 from kv_cache_decode_quest_amd.workloads import WORKLOADS, scaled
 from parity import Layer, check_kmeta, check_out, check_scores, compare_selection, log
@@ -82,6 +83,35 @@ def test_full_layers48_sampled(gpu_lib):
         q, bufs = results[li]
         flagged = check_requests(layers[li], q, bufs, sample)
         log(f"layers48: layer {li} ok, flagged {flagged}")
+
+
+def test_full_dense_sampled(gpu_lib):
+    """Dense flash-decode on the same pool (the vanilla method): every page of
+    every request selected, no scoring and no top-k, at the benchmark's shape
+    (batch 8 x 128000 + one appended token); requests 0 and 5 against the
+    oracle's dense attention over all their tokens."""
+    w = WORKLOADS["bench128k"]
+    sample = [0, 5]
+    lay = Layer(w, DEV, host_requests=sample)
+    q, k_new, v_new = lay.step_inputs(0)
+    lay.append_step(k_new, v_new)
+    B, H = w.batch, w.num_kv_heads
+    max_k = lay.lay.max_pages
+    bufs = quest.alloc_decode_buffers(lay.L, B, max_k, DEV)
+    bufs.sel_pages.copy_(torch.arange(max_k, dtype=torch.int32, device=DEV).expand(B, H, max_k))
+    n = (lay.ctx.to(torch.int64) + w.page_size - 1) // w.page_size
+    nsel = n.to(torch.int32).view(B, 1).expand(B, H).contiguous().to(DEV)
+    lay.attend(q, bufs, sel=bufs.sel_pages, nsel=nsel)
+    torch.cuda.synchronize()
+    out = to_f64(bufs.out)
+    sm = workloads.default_sm_scale(w)
+    for r in sample:
+        log(f"dense: oracle request {r} over {int(lay.ctx[r])} tokens")
+        qr = np.ascontiguousarray(to_oracle(q[r]))
+        ref = oracle.request_dense(lay.shape, qr, lay.host[0], lay.host[1], lay.pt_host[r],
+                                   int(lay.ctx[r]), sm)
+        check_out(out[r], ref, w.torch_dtype, f"dense r{r}")
+    log("dense: ok")
 
 
 def test_graph_capture_replay(gpu_lib):
