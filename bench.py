@@ -137,6 +137,55 @@ def dense_reference(layer, inputs, ctx_b, ctx_a, sm, evict, n_steps, dev):
             "plan": plan}
 
 
+def prefill_chunk_append(layer, chunk, n_calls, evict, dev):
+    """Bulk on_kv_stored at prefill-chunk granularity: each call stores one
+    `chunk`-token chunk of every request's prompt (positions c*chunk ..) with
+    quest_append_kv.  The chunks are the prompt's own tokens at their own
+    positions and start on a page boundary, so every call rewrites identical
+    bytes and leaves the cache as it was.  Bytes = new K/V read + K/V written
+    + the chunk pages' metadata written."""
+    w, L = layer.w, layer.L
+    B, H, D, P = w.batch, w.num_kv_heads, w.head_dim, w.page_size
+    k_all, v_all, cu = layer.prefill
+    cuh = cu.cpu().tolist()
+    lens = [cuh[r + 1] - cuh[r] for r in range(B)]
+    n_chunks = min(lens) // chunk
+    if n_chunks == 0 or chunk % P:
+        return None
+    calls = []
+    for i in range(min(n_calls, n_chunks)):
+        c = i * (n_chunks // min(n_calls, n_chunks))
+        idx = torch.cat([torch.arange(cuh[r] + c * chunk, cuh[r] + (c + 1) * chunk)
+                         for r in range(B)]).to(dev)
+        calls.append((k_all[idx].contiguous(), v_all[idx].contiguous(),
+                      torch.full((B,), c * chunk, dtype=torch.int32, device=dev)))
+    cu_c = torch.arange(0, B * chunk + 1, chunk, dtype=torch.int32, device=dev)
+
+    def call(i):
+        k, v, ctx0 = calls[i]
+        quest.quest_append_kv(L, k, v, cu_c, ctx0, chunk, layer.pt, layer.k_cache,
+                              layer.v_cache, layer.kmeta)
+
+    call(0)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
+    torch.cuda.synchronize()
+    for i in range(len(calls)):
+        evict()
+        ev[i][0].record()
+        call(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    total_s = sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3
+    elem = 2 if w.dtype == "bf16" else 4
+    tokens = B * chunk * len(calls)
+    nbytes = tokens * H * D * elem * 4 + (tokens // P) * H * 2 * D * elem
+    return {"what": f"quest_append_kv of one {chunk}-token chunk per request ({B} requests) "
+                    "per call, cache evicted before each call",
+            "chunk_tokens": chunk, "calls": len(calls), "us_per_call": total_s / len(calls) * 1e6,
+            "tokens_per_s": tokens / total_s, "bytes_per_call": nbytes / len(calls),
+            "hbm_gbps": nbytes / total_s / 1e9, "hbm_frac_peak": nbytes / total_s / 1e9 / PEAK_HBM_GBPS}
+
+
 class Stepper:
     """Issues decode steps for the whole batch, split by request into
     contiguous chunks, one chunk per HIP stream (default priority).  Chunks
@@ -350,6 +399,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense decode reference (every page, no selection)")
     ap.add_argument("--dense-steps", type=int, default=16)
+    ap.add_argument("--prefill-chunk", type=int, default=4096,
+                    help="chunk size of the prefill append leg (0 to skip)")
     ap.add_argument("--roofline-copies", type=int, default=8)
     ap.add_argument("--streams", type=int, default=1,
                     help="split the batch by request over this many HIP streams")
@@ -525,6 +576,12 @@ def main():
         dense["sparse_speedup"] = value / dense["tokens_per_s"]
         restore()
 
+    prefill = None
+    if args.prefill_chunk > 0:
+        log(f"prefill append: {args.prefill_chunk}-token chunks")
+        prefill = prefill_chunk_append(layer, args.prefill_chunk, 16, evict, dev)
+        restore()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, (layer.lay,) + layer.prefill, inputs,
@@ -567,6 +624,7 @@ def main():
         "wall_s_timed_loop_incl_flush": t_wall,
         "warm": warm,
         "dense_reference": dense,
+        "prefill_append": prefill,
         "cpu_baseline": cpu,
         "host": platform.node(),
     }

@@ -154,6 +154,58 @@ def test_incremental_append_equals_bulk(gpu_lib):
         assert torch.equal(km[phys].view(torch.int16), bulk.kmeta[phys].view(torch.int16))
 
 
+def test_unaligned_and_chunked_append_match(gpu_lib):
+    """The same tokens stored three ways give identical pools and metadata:
+    one bulk append (16-byte vector path), chunks of 37 tokens that start and
+    end inside pages, and one bulk append from source tensors shifted off
+    16-byte alignment (the scalar path)."""
+    w = scaled(WORKLOADS["ragged"], batch=3, ctx_range=(200, 900), steps=0)
+    ref = Layer(w, DEV, host=False)
+    k_new, v_new, cu, _ = workloads.prefill_tokens(w, ref.lay, DEV)
+    cuh = cu.cpu().tolist()
+    lens = [cuh[r + 1] - cuh[r] for r in range(w.batch)]
+
+    def fresh():
+        k_c, v_c = workloads.empty_pool(w, ref.lay, DEV)
+        return k_c, v_c, torch.full_like(ref.kmeta, -3.0)
+
+    def same(k_c, v_c, km):
+        assert torch.equal(k_c.view(torch.int16), ref.k_cache.view(torch.int16))
+        assert torch.equal(v_c.view(torch.int16), ref.v_cache.view(torch.int16))
+        for r in range(w.batch):
+            n = -(-lens[r] // w.page_size)
+            phys = ref.pt[r, :n].long()
+            assert torch.equal(km[phys].view(torch.int16), ref.kmeta[phys].view(torch.int16))
+
+    # chunks of 37 tokens per request
+    k_c, v_c, km = fresh()
+    step = 37
+    for t0 in range(0, max(lens), step):
+        counts = [max(0, min(step, n - t0)) for n in lens]
+        rows = [cuh[r] + t0 + i for r in range(w.batch) for i in range(counts[r])]
+        sub_cu = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int32, device=DEV)
+        ctx0 = torch.tensor([min(t0, n) for n in lens], dtype=torch.int32, device=DEV)
+        idx = torch.tensor(rows, dtype=torch.int64, device=DEV)
+        quest.quest_append_kv(ref.L, k_new[idx].contiguous(), v_new[idx].contiguous(), sub_cu,
+                              ctx0, step, ref.pt, k_c, v_c, km)
+    torch.cuda.synchronize()
+    same(k_c, v_c, km)
+
+    # source tensors one element off 16-byte alignment
+    k_c, v_c, km = fresh()
+    shape = tuple(k_new.shape)
+    k_buf = torch.empty(k_new.numel() + 1, dtype=k_new.dtype, device=DEV)
+    v_buf = torch.empty(v_new.numel() + 1, dtype=v_new.dtype, device=DEV)
+    k_off, v_off = k_buf[1:].view(shape), v_buf[1:].view(shape)
+    k_off.copy_(k_new)
+    v_off.copy_(v_new)
+    assert k_off.data_ptr() % 16 != 0
+    zero = torch.zeros(w.batch, dtype=torch.int32, device=DEV)
+    quest.quest_append_kv(ref.L, k_off, v_off, cu, zero, max(lens), ref.pt, k_c, v_c, km)
+    torch.cuda.synchronize()
+    same(k_c, v_c, km)
+
+
 def test_empty_and_one_token_requests(gpu_lib):
     """A request with no token selects nothing and outputs zeros; the others
     match the oracle (decode without a preceding append)."""
