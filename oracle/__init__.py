@@ -79,10 +79,11 @@ def load(path):
     L.qo_pages_for_budget.argtypes = [i32, i32, i32]
     L.qo_pages_for_budget.restype = i32
     L.qo_select.argtypes = [vp, i32, i32, vp]
+    L.qo_select_forced.argtypes = [vp, i32, i32, i32, i32, vp]
     L.qo_request_attend.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, i32, f64, vp]
     L.qo_request_dense.argtypes = [sp, vp, vp, vp, vp, i32, f64, vp]
     for fn in (L.qo_store_tokens, L.qo_request_bounds, L.qo_page_bounds,
-               L.qo_request_scores, L.qo_select, L.qo_request_attend,
+               L.qo_request_scores, L.qo_select, L.qo_select_forced, L.qo_request_attend,
                L.qo_request_dense):
         fn.restype = None
     return L
@@ -188,14 +189,19 @@ def pages_for_budget(budget_tokens, ctx, page_size) -> int:
     return int(lib().qo_pages_for_budget(int(budget_tokens), int(ctx), int(page_size)))
 
 
-def select(scores_row, k) -> np.ndarray:
-    """Ascending logical ids of the k best pages of one score row."""
+def select(scores_row, k, n_sink=0, n_recent=0) -> np.ndarray:
+    """Ascending logical ids of the k best pages of one score row; with
+    n_sink / n_recent, the first / last pages of the row are kept first."""
     scores_row = np.ascontiguousarray(scores_row, dtype=np.float64)
     n = scores_row.shape[0]
     if not 0 <= k <= n:
         raise ValueError("k outside [0, n]")
     out = np.empty(max(k, 1), np.int32)
-    lib().qo_select(_ptr(scores_row), n, int(k), _ptr(out))
+    if n_sink or n_recent:
+        lib().qo_select_forced(_ptr(scores_row), n, int(k), int(n_sink), int(n_recent),
+                               _ptr(out))
+    else:
+        lib().qo_select(_ptr(scores_row), n, int(k), _ptr(out))
     return out[:k].copy()
 
 
@@ -236,7 +242,7 @@ def request_dense(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, sm_scale) -> np.
 
 
 def decode_request(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, budget_tokens,
-                   sm_scale, reduce="max", bounds=None) -> dict:
+                   sm_scale, reduce="max", bounds=None, n_sink=0, n_recent=0) -> dict:
     """One request's decode view and output: bounds, scores, k, selection, out.
 
     ``bounds`` may be passed when already computed for the same pool state."""
@@ -244,7 +250,7 @@ def decode_request(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, budget_tokens,
         bounds = request_bounds(s, k_cache, pt_row, ctx)
     scores = request_scores(s, q_r, bounds, reduce)
     k = pages_for_budget(budget_tokens, ctx, s.P)
-    sel = [select(scores[g], k) for g in range(s.Hkv)]
+    sel = [select(scores[g], k, n_sink, n_recent) for g in range(s.Hkv)]
     out = request_attend(s, q_r, k_cache, v_cache, pt_row, ctx, sel, sm_scale)
     return {"bounds": bounds, "scores": scores, "k": k, "sel": sel, "out": out}
 

@@ -212,6 +212,41 @@ void qo_select(const double *scores, int32_t n, int32_t k, int32_t *sel) {
   free(all);
 }
 
+/* Forced pages (READING, a variant the pages leave open): the first n_sink
+ * and the last n_recent pages of a request are kept ahead of every scored
+ * page, the lower page first among themselves; the budget still fixes k, and
+ * the remaining slots follow qo_select's order.  The result is ascending. */
+static int forced_page(int32_t j, int32_t n, int32_t n_sink, int32_t n_recent) {
+  return j < n_sink || j >= n - n_recent;
+}
+
+typedef struct {
+  int forced;
+  scored_page sp;
+} ranked_page;
+
+static int forced_then_score(const void *pa, const void *pb) {
+  const ranked_page *a = (const ranked_page *)pa, *b = (const ranked_page *)pb;
+  if (a->forced != b->forced) return a->forced ? -1 : 1;
+  if (a->forced) return (a->sp.page > b->sp.page) - (a->sp.page < b->sp.page);
+  return by_score_then_page(&a->sp, &b->sp);
+}
+
+void qo_select_forced(const double *scores, int32_t n, int32_t k, int32_t n_sink,
+                      int32_t n_recent, int32_t *sel) {
+  if (k <= 0 || n <= 0) return;
+  ranked_page *all = (ranked_page *)malloc(sizeof(ranked_page) * (size_t)n);
+  for (int32_t j = 0; j < n; ++j) {
+    all[j].forced = forced_page(j, n, n_sink, n_recent);
+    all[j].sp.score = scores[j];
+    all[j].sp.page = j;
+  }
+  qsort(all, (size_t)n, sizeof(ranked_page), forced_then_score);
+  for (int32_t i = 0; i < k; ++i) sel[i] = all[i].sp.page;
+  qsort(sel, (size_t)k, sizeof sel[0], ascending_int);
+  free(all);
+}
+
 /* ---- attention over the selected view ----------------------------------- */
 
 /* For q head h (KV head g = h / G): logits l_t = sm_scale * q_h . k_t over the

@@ -67,6 +67,10 @@ int32_t qo_pages_for_budget(int32_t budget_tokens, int32_t ctx,
 /* Top-k pages of one score row; writes k logical ids in ascending order. */
 void qo_select(const double *scores, int32_t n, int32_t k, int32_t *sel);
 
+/* The same with the first n_sink and last n_recent pages kept first. */
+void qo_select_forced(const double *scores, int32_t n, int32_t k, int32_t n_sink,
+                      int32_t n_recent, int32_t *sel);
+
 /* Softmax attention of every q head over the valid tokens of the pages its KV
  * head selected.  sel is [Hkv][sel_stride], nsel is [Hkv]. */
 void qo_request_attend(const qo_shape *s, const void *q_r, const void *k_cache,

@@ -247,6 +247,35 @@ def pin_select_bruteforce():
     assert oracle.select(np.array([-0.0, 0.0, 5.0]), 2).tolist() == [0, 2]
 
 
+def pin_select_forced():
+    """Forced sink / recent pages reduce to the pinned plain selection: with
+    none forced it is the plain selection; when k covers the forced set F, the
+    result is F plus the plain selection of k - |F| pages among the others;
+    otherwise the k lowest pages of F."""
+    rng = np.random.default_rng(37)
+    for n in (1, 3, 10, 64, 200):
+        for levels in (3, 1000):
+            scores = rng.integers(0, levels, n).astype(np.float64) - levels / 2
+            for ns, nr in ((0, 0), (1, 0), (0, 1), (1, 1), (2, 3), (n, 0), (0, n + 2), (5, 5)):
+                forced = [j for j in range(n) if j < ns or j >= n - nr]
+                rest = [j for j in range(n) if not (j < ns or j >= n - nr)]
+                for k in sorted({0, 1, len(forced) - 1, len(forced), len(forced) + 1,
+                                 n // 2, n}):
+                    if not 0 <= k <= n:
+                        continue
+                    got = oracle.select(scores, k, ns, nr).tolist()
+                    if k <= len(forced):
+                        want = forced[:k]
+                    else:
+                        sub = oracle.select(scores[rest], k - len(forced)).tolist()
+                        want = sorted(forced + [rest[i] for i in sub])
+                    assert got == want, (n, levels, ns, nr, k)
+            if n > 2:
+                # a forced page outranks even the best scored page
+                best = int(np.argmax(scores[1:])) + 1
+                assert oracle.select(scores, 1, 1, 0).tolist() == [0], best
+
+
 # --------------------------------------------------------------------------
 # attention over the selected view
 # --------------------------------------------------------------------------
@@ -351,6 +380,7 @@ PINS = [
     pin_hand_example, pin_store_layout, pin_store_incremental_equals_bulk,
     pin_bounds_contain_and_attain, pin_score_is_box_maximum, pin_score_bounds_every_key,
     pin_score_closed_forms, pin_group_reduce, pin_budget_table, pin_select_bruteforce,
+    pin_select_forced,
     pin_dense_equals_sdpa, pin_sparse_equals_masked_sdpa, pin_attention_closed_forms,
     pin_permutation_invariance, pin_budget_covering_all_is_dense,
 ]
@@ -401,6 +431,10 @@ MUTANTS = {
                                                   "denom += exp(logit[t]);"),
     "store drops the page table": ("const int64_t phys = pt_row[pos / P];",
                                    "const int64_t phys = pos / P;"),
+    "recent pages counted from the front": ("return j < n_sink || j >= n - n_recent;",
+                                            "return j < n_sink || j < n_recent;"),
+    "forced pages not ranked first": ("if (a->forced != b->forced) return a->forced ? -1 : 1;",
+                                      ""),
 }
 
 
