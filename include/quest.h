@@ -23,6 +23,8 @@
  *     quest_page_scores    build_decode_view, part 1: per-page bounds from q
  *     quest_append_score   the two above fused into one pass
  *     quest_topk_pages     build_decode_view, part 2: top-k within the budget
+ *                          (quest_topk_pages_forced: with sink / recent pages
+ *                          always kept)
  *     quest_sparse_decode  attention over the selected explicit-KV view
  *
  * Conventions shared by every entry point
@@ -176,6 +178,21 @@ int quest_topk_pages(const quest_layout *layout, int32_t batch,
                      const float *scores, const int32_t *ctx_lens,
                      const int32_t *budget_tokens, int32_t max_k,
                      int32_t *sel_pages, int32_t *num_sel, void *stream);
+
+/* quest_topk_pages with forced pages, a variant the pages leave open (a
+ * selection that always keeps attention-sink and most-recent pages): for
+ * request r with n_r pages, the pages j < n_sink and j >= n_r - n_recent are
+ * ranked above every scored page, the lower page first among them; k_r is
+ * computed as in quest_topk_pages (the budget still decides how many pages
+ * are kept, forced ones included), so when k_r is smaller than the forced
+ * set the k_r lowest forced pages are kept.  Output as in quest_topk_pages;
+ * n_sink = n_recent = 0 is exactly quest_topk_pages.  n_sink or n_recent < 0
+ * returns QUEST_ERR_SHAPE. */
+int quest_topk_pages_forced(const quest_layout *layout, int32_t batch,
+                            const float *scores, const int32_t *ctx_lens,
+                            const int32_t *budget_tokens, int32_t max_k,
+                            int32_t n_sink, int32_t n_recent,
+                            int32_t *sel_pages, int32_t *num_sel, void *stream);
 
 /* Workspace bytes quest_sparse_decode needs for this batch and max_k (0 for
  * batch 0).  A pure function of its arguments; never calls HIP. */

@@ -130,18 +130,27 @@ int quest_append_score(const quest_layout *layout, int32_t batch, const void *q,
                                               (hipStream_t)stream));
 }
 
-int quest_topk_pages(const quest_layout *layout, int32_t batch, const float *scores,
-                     const int32_t *ctx_lens, const int32_t *budget_tokens, int32_t max_k,
-                     int32_t *sel_pages, int32_t *num_sel, void *stream) {
+int quest_topk_pages_forced(const quest_layout *layout, int32_t batch, const float *scores,
+                            const int32_t *ctx_lens, const int32_t *budget_tokens,
+                            int32_t max_k, int32_t n_sink, int32_t n_recent,
+                            int32_t *sel_pages, int32_t *num_sel, void *stream) {
   Dims dm;
   int st = check_layout(layout, dm);
   if (st != QUEST_OK) return st;
   if ((st = check_batch(batch, dm)) != QUEST_OK) return st;
-  if (max_k <= 0) return QUEST_ERR_SHAPE;
+  if (max_k <= 0 || n_sink < 0 || n_recent < 0) return QUEST_ERR_SHAPE;
   if (batch == 0) return QUEST_OK;
   if (!scores || !ctx_lens || !budget_tokens || !sel_pages || !num_sel) return QUEST_ERR_NULL;
   return launched(quest::launch_topk(dm, batch, scores, ctx_lens, budget_tokens, max_k,
-                                     sel_pages, num_sel, (hipStream_t)stream));
+                                     n_sink, n_recent, sel_pages, num_sel,
+                                     (hipStream_t)stream));
+}
+
+int quest_topk_pages(const quest_layout *layout, int32_t batch, const float *scores,
+                     const int32_t *ctx_lens, const int32_t *budget_tokens, int32_t max_k,
+                     int32_t *sel_pages, int32_t *num_sel, void *stream) {
+  return quest_topk_pages_forced(layout, batch, scores, ctx_lens, budget_tokens, max_k, 0, 0,
+                                 sel_pages, num_sel, stream);
 }
 
 size_t quest_sparse_decode_workspace_bytes(const quest_layout *layout, int32_t batch,

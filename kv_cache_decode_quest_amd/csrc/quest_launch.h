@@ -34,10 +34,11 @@ hipError_t launch_append_scores(const Dims &dm, int batch, const void *q, const 
                                 const int32_t *page_table, void *k_cache, void *v_cache,
                                 void *kmeta, int reduce, float *scores, hipStream_t stream);
 
+// n_sink / n_recent >= 0: the first / last pages of each request kept first.
 hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        const int32_t *ctx_lens, const int32_t *budget_tokens,
-                       int max_k, int32_t *sel_pages, int32_t *num_sel,
-                       hipStream_t stream);
+                       int max_k, int n_sink, int n_recent, int32_t *sel_pages,
+                       int32_t *num_sel, hipStream_t stream);
 
 struct DecodePlan {
   int n_split;          // splits per (request, KV head)

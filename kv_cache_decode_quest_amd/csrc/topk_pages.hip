@@ -129,11 +129,17 @@ constexpr int kRegKeys = 8192;
 constexpr int kPerThread = kRegKeys / kTopkThreads;
 constexpr int kRegSpan = kPerThread * kWave;              // pages per wave
 
+// Forced pages (the first n_sink and the last n_recent of a request) take the
+// largest key, above the key of any score but a NaN, so they are kept before
+// every scored page, the lower page first among them.
+constexpr uint32_t kForcedKey = 0xffffffffu;
+
 template <bool kRegs>
 __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
-    int Hkv, int P, int max_pages, int max_k, const float *__restrict__ scores,
-    const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ budget_tokens,
-    int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel) {
+    int Hkv, int P, int max_pages, int max_k, int n_sink, int n_recent,
+    const float *__restrict__ scores, const int32_t *__restrict__ ctx_lens,
+    const int32_t *__restrict__ budget_tokens, int32_t *__restrict__ sel_pages,
+    int32_t *__restrict__ num_sel) {
   __shared__ TopkShared sh;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   // grid (KV head, request): no division by runtime values
@@ -168,12 +174,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
   }
   // The thread's keys: registers, or global memory for long rows.  Invalid
   // slots (past the row) never count; their key is 0.
+  const int recent0 = n - n_recent;                   // first forced recent page
+  auto key_of = [&](float score, int j) -> uint32_t {
+    return (j < n_sink || j >= recent0) ? kForcedKey : order_key(score);
+  };
   uint32_t u[kRegs ? kPerThread : 1];
   if constexpr (kRegs) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int j = wave * kRegSpan + i * kWave + lane;
-      u[i] = j < n ? order_key(sv[i]) : 0u;
+      u[i] = j < n ? key_of(sv[i], j) : 0u;
     }
   }
   auto valid = [&](int i) { return wave * kRegSpan + i * kWave + lane < n; };
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
       }
   } else {
     for (int j = tid; j < n; j += kTopkThreads) {
-      const uint32_t x = order_key(s[j]);
+      const uint32_t x = key_of(s[j], j);
       lo = min(lo, x);
       hi = max(hi, x);
     }
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
           atomicAdd(&sh.hist[(u[i] >> shift) & bmask], 1u);
     } else {
       for (int j = tid; j < n; j += kTopkThreads) {
-        const uint32_t x = order_key(s[j]);
+        const uint32_t x = key_of(s[j], j);
         if (((x ^ prefix) & himask) == 0u) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
       }
     }
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
       }
       if (lane == 0) sh.cnt_gt[wave] = above;
     } else {
-      for (int j = tid; j < n; j += kTopkThreads) gather(order_key(s[j]), j);
+      for (int j = tid; j < n; j += kTopkThreads) gather(key_of(s[j], j), j);
     }
     __syncthreads();
     if (wave == 0) {
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
     const int j = w0 + i * kWave + lane;
     uint32_t x;
     if constexpr (kRegs) x = u[i];
-    else x = j < n ? order_key(s[j]) : 0u;
+    else x = j < n ? key_of(s[j], j) : 0u;
     mg = __ballot(j < n && x > thresh);
     me = __ballot(j < n && x == thresh);
   };
@@ -398,17 +408,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
 
 hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        const int32_t *ctx_lens, const int32_t *budget_tokens,
-                       int max_k, int32_t *sel_pages, int32_t *num_sel,
-                       hipStream_t stream) {
+                       int max_k, int n_sink, int n_recent, int32_t *sel_pages,
+                       int32_t *num_sel, hipStream_t stream) {
   dim3 grid((unsigned)dm.Hkv, (unsigned)batch);
   if (dm.max_pages <= kRegKeys)
     hipLaunchKernelGGL(topk_pages_kernel<true>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
-                       dm.P, dm.max_pages, max_k, scores, ctx_lens, budget_tokens, sel_pages,
-                       num_sel);
+                       dm.P, dm.max_pages, max_k, n_sink, n_recent, scores, ctx_lens,
+                       budget_tokens, sel_pages, num_sel);
   else
     hipLaunchKernelGGL(topk_pages_kernel<false>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
-                       dm.P, dm.max_pages, max_k, scores, ctx_lens, budget_tokens, sel_pages,
-                       num_sel);
+                       dm.P, dm.max_pages, max_k, n_sink, n_recent, scores, ctx_lens,
+                       budget_tokens, sel_pages, num_sel);
   return hipGetLastError();
 }
 

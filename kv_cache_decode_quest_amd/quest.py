@@ -23,8 +23,8 @@ REDUCE = {"max": 0, "sum": 1}
 
 # exported symbols declared in include/quest.h
 EXPORTS = ("quest_abi_version", "quest_status_string", "quest_append_kv", "quest_page_scores",
-           "quest_append_score", "quest_topk_pages", "quest_sparse_decode_workspace_bytes",
-           "quest_sparse_decode", "quest_sparse_decode_plan")
+           "quest_append_score", "quest_topk_pages", "quest_topk_pages_forced",
+           "quest_sparse_decode_workspace_bytes", "quest_sparse_decode", "quest_sparse_decode_plan")
 
 
 class QuestError(RuntimeError):
@@ -69,13 +69,14 @@ def load(path: str = LIB_PATH):
     L.quest_append_score.argtypes = [lp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
                                      vp]
     L.quest_topk_pages.argtypes = [lp, i32, vp, vp, vp, i32, vp, vp, vp]
+    L.quest_topk_pages_forced.argtypes = [lp, i32, vp, vp, vp, i32, i32, i32, vp, vp, vp]
     L.quest_sparse_decode_workspace_bytes.argtypes = [lp, i32, i32]
     L.quest_sparse_decode_workspace_bytes.restype = sz
     L.quest_sparse_decode.argtypes = [lp, i32, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp,
                                       sz, vp]
     L.quest_sparse_decode_plan.argtypes = [lp, i32, i32, ip, ip]
     for name in ("quest_append_kv", "quest_page_scores", "quest_append_score", "quest_topk_pages",
-                 "quest_sparse_decode", "quest_sparse_decode_plan"):
+                 "quest_topk_pages_forced", "quest_sparse_decode", "quest_sparse_decode_plan"):
         getattr(L, name).restype = ctypes.c_int
     if L.quest_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libquest ABI {L.quest_abi_version()} != binding ABI {ABI_VERSION}")
@@ -214,6 +215,18 @@ def quest_append_score(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, max_
 
 def quest_topk_pages(L: QuestLayout, scores, ctx_lens, budget_tokens, max_k, sel_pages, num_sel):
     """build_decode_view part 2: ascending top-k logical pages per (r, KV head)."""
+    _topk(L, scores, ctx_lens, budget_tokens, max_k, sel_pages, num_sel)
+
+
+def quest_topk_pages_forced(L: QuestLayout, scores, ctx_lens, budget_tokens, max_k, n_sink,
+                            n_recent, sel_pages, num_sel):
+    """quest_topk_pages with the first n_sink and last n_recent pages of each
+    request kept ahead of the scored ones."""
+    _topk(L, scores, ctx_lens, budget_tokens, max_k, sel_pages, num_sel, n_sink, n_recent)
+
+
+def _topk(L, scores, ctx_lens, budget_tokens, max_k, sel_pages, num_sel, n_sink=None,
+          n_recent=None):
     dev = scores.device
     batch = ctx_lens.shape[0]
     _check(scores, "scores", torch.float32, (batch, L.num_kv_heads, L.max_pages_per_seq), dev)
@@ -221,10 +234,17 @@ def quest_topk_pages(L: QuestLayout, scores, ctx_lens, budget_tokens, max_k, sel
     _check(budget_tokens, "budget_tokens", torch.int32, (batch,), dev)
     _check(sel_pages, "sel_pages", torch.int32, (batch, L.num_kv_heads, max_k), dev)
     _check(num_sel, "num_sel", torch.int32, (batch, L.num_kv_heads), dev)
-    st = load().quest_topk_pages(ctypes.byref(L), batch, _ptr(scores), _ptr(ctx_lens),
-                                 _ptr(budget_tokens), int(max_k), _ptr(sel_pages), _ptr(num_sel),
-                                 _stream(dev))
-    _raise("quest_topk_pages", st)
+    if n_sink is None:
+        st = load().quest_topk_pages(ctypes.byref(L), batch, _ptr(scores), _ptr(ctx_lens),
+                                     _ptr(budget_tokens), int(max_k), _ptr(sel_pages),
+                                     _ptr(num_sel), _stream(dev))
+        _raise("quest_topk_pages", st)
+    else:
+        st = load().quest_topk_pages_forced(ctypes.byref(L), batch, _ptr(scores),
+                                            _ptr(ctx_lens), _ptr(budget_tokens), int(max_k),
+                                            int(n_sink), int(n_recent), _ptr(sel_pages),
+                                            _ptr(num_sel), _stream(dev))
+        _raise("quest_topk_pages_forced", st)
 
 
 def quest_sparse_decode_workspace_bytes(L: QuestLayout, batch: int, max_k: int) -> int:

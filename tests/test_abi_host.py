@@ -103,6 +103,18 @@ def test_fused_append_score_rejections(lib):
                                   None, None, None, 0, None, None) == OK
 
 
+def test_forced_topk_rejections(lib):
+    L = layout()
+
+    def call(n_sink, n_recent, batch=1, scores=FAKE):
+        return lib.quest_topk_pages_forced(ctypes.byref(L), batch, scores, FAKE, FAKE, 8,
+                                           n_sink, n_recent, FAKE, FAKE, None)
+    assert call(-1, 0) == ERR_SHAPE
+    assert call(0, -2) == ERR_SHAPE
+    assert call(1, 1, scores=None) == ERR_NULL
+    assert call(1, 1, batch=0, scores=None) == OK
+
+
 def test_null_layout(lib):
     assert lib.quest_page_scores(None, 1, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == ERR_NULL
 

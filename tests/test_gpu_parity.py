@@ -282,6 +282,71 @@ def test_topk_exact(n_max, P, gpu_lib):
             assert np.all(sel[b, g, k:] == -1)
 
 
+@pytest.mark.parametrize("n_max,P", [(300, 16), (2050, 32), (10000, 16)])
+def test_topk_forced_exact(n_max, P, gpu_lib):
+    """Forced sink / recent pages: the same rows as test_topk_exact, every
+    (n_sink, n_recent) pair below, compared with the oracle's selection
+    (budgets include k smaller than the forced set)."""
+    gen = torch.Generator().manual_seed(6000 + n_max)
+    rows = _topk_rows(n_max, gen)
+    Hkv = 2
+    B = (len(rows) + 1) // 2
+    while len(rows) < B * Hkv:
+        rows.append(torch.randn(n_max, generator=gen))
+    scores = torch.stack(rows).reshape(B, Hkv, n_max).contiguous()
+    ctx_choices = [n_max * P, n_max * P - P + 1, 1, P + 1, (n_max // 2) * P, n_max * P - 3]
+    bud_choices = [3 * P, (n_max - 1) * P, 5, 0, n_max * P * 2, P * (n_max // 3) + 7]
+    ctx = torch.tensor([ctx_choices[b % 6] for b in range(B)], dtype=torch.int32)
+    bud = torch.tensor([bud_choices[(b + 1) % 6] for b in range(B)], dtype=torch.int32)
+    max_k = max(1, n_max - 2)
+    L = quest.make_layout(8 * Hkv, Hkv, 128, P, torch.bfloat16, 1, n_max)
+    s64 = scores.double().numpy()
+    for ns, nr in ((1, 0), (0, 1), (1, 2), (4, 4), (n_max, 0)):
+        sel = torch.full((B, Hkv, max_k), 12345, dtype=torch.int32, device=DEV)
+        nsel = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
+        quest.quest_topk_pages_forced(L, scores.to(DEV), ctx.to(DEV), bud.to(DEV), max_k, ns,
+                                      nr, sel, nsel)
+        torch.cuda.synchronize()
+        sel_h, nsel_h = sel.cpu().numpy(), nsel.cpu().numpy()
+        for b in range(B):
+            n = min(-(-int(ctx[b]) // P), n_max)
+            k = min(oracle.pages_for_budget(int(bud[b]), int(ctx[b]), P), max_k)
+            for g in range(Hkv):
+                want = oracle.select(np.ascontiguousarray(s64[b, g, :n]), k, ns, nr)
+                assert nsel_h[b, g] == k, (ns, nr, b, g)
+                assert np.array_equal(sel_h[b, g, :k], want), (ns, nr, b, g, n, k)
+                assert np.all(sel_h[b, g, k:] == -1)
+
+
+def test_forced_pages_decode(gpu_lib):
+    """One decode step with a sink page and two recent pages always kept:
+    selections and outputs against the oracle's decode with the same forcing."""
+    w = scaled(WORKLOADS["layer32k"], batch=3, ctx=4000, budget_tokens=512, steps=1)
+    lay = Layer(w, DEV)
+    q, k_new, v_new = lay.step_inputs(0)
+    lay.append_step(k_new, v_new)
+    bufs = lay.buffers()
+    quest.quest_page_scores(lay.L, q, lay.kmeta, lay.pt, lay.ctx, bufs.scores)
+    quest.quest_topk_pages_forced(lay.L, bufs.scores, lay.ctx, lay.budgets(), bufs.max_k, 1, 2,
+                                  bufs.sel_pages, bufs.num_sel)
+    lay.attend(q, bufs)
+    torch.cuda.synchronize()
+    sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+    out = to_f64(bufs.out)
+    for r in range(w.batch):
+        ref = oracle.decode_request(lay.shape, np.ascontiguousarray(to_oracle(q[r])), lay.host[0],
+                                    lay.host[1], lay.pt_host[r], int(lay.ctx[r]),
+                                    int(lay.budgets()[r]), workloads.default_sm_scale(w),
+                                    n_sink=1, n_recent=2)
+        n = -(-int(lay.ctx[r]) // w.page_size)
+        flags = [compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g], ref["scores"][g])
+                 for g in range(w.num_kv_heads)]
+        for g in range(w.num_kv_heads):
+            assert {0, n - 2, n - 1} <= set(sel[r, g, :nsel[r, g]].tolist())
+        if "flagged" not in flags:
+            check_out(out[r], ref["out"], torch.bfloat16, f"forced r{r}")
+
+
 def test_topk_empty_request(gpu_lib):
     L = quest.make_layout(8, 1, 128, 16, torch.bfloat16, 1, 10)
     scores = torch.randn((2, 1, 10), device=DEV)
