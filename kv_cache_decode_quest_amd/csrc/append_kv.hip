@@ -52,7 +52,6 @@ __device__ __forceinline__ void append_page_group(
     uint16_t *__restrict__ kmeta) {
   const int lo_pos = max(p0, page * P), hi_pos = min(p1, (page + 1) * P);
   const bool fresh = lo_pos == page * P;
-  const bool full = fresh && hi_pos == (page + 1) * P;
 
   float lo[8], hi[8];
   if (fresh) {
@@ -71,51 +70,60 @@ __device__ __forceinline__ void append_page_group(
       hi[c] = bf16_bits_to_f32((bw[c / 2] >> (16 * (c & 1))) & 0xffffu);
     }
   }
-  // all loads first (clamped rows for slots outside the new range)
-  uint4 kv[P], vv[P];
+  // The page in blocks of SB slots (bounded registers for large pages); in
+  // each block all loads first, clamped rows for slots outside the new range.
+  constexpr int SB = P < 16 ? P : 16;
+  for (int s0 = 0; s0 < P; s0 += SB) {
+    const int b_lo = page * P + s0;
+    if (b_lo + SB <= lo_pos || b_lo >= hi_pos) continue;  // no new slot here
+    const bool full = lo_pos <= b_lo && b_lo + SB <= hi_pos;
+    uint4 kv[SB], vv[SB];
 #pragma unroll
-  for (int s = 0; s < P; ++s) {
-    const int pos = min(max(page * P + s, lo_pos), hi_pos - 1);
-    const int64_t src = ((int64_t)(row0 + pos - p0) * Hkv + g) * D + d0;
-    kv[s] = *(const uint4 *)(k_new + src);
-    vv[s] = *(const uint4 *)(v_new + src);
-  }
+    for (int s = 0; s < SB; ++s) {
+      const int pos = min(max(b_lo + s, lo_pos), hi_pos - 1);
+      const int64_t src = ((int64_t)(row0 + pos - p0) * Hkv + g) * D + d0;
+      kv[s] = *(const uint4 *)(k_new + src);
+      vv[s] = *(const uint4 *)(v_new + src);
+    }
 #pragma unroll
-  for (int s = 0; s < P; ++s) {
-    const int pos = page * P + s;
-    if (pos < lo_pos || pos >= hi_pos) continue;
-    *(uint4 *)(k_cache + (head * P + s) * D + d0) = kv[s];
-    const uint32_t w[4] = {kv[s].x, kv[s].y, kv[s].z, kv[s].w};
+    for (int s = 0; s < SB; ++s) {
+      const int pos = b_lo + s;
+      if (pos < lo_pos || pos >= hi_pos) continue;
+      *(uint4 *)(k_cache + (head * P + s0 + s) * D + d0) = kv[s];
+      const uint32_t w[4] = {kv[s].x, kv[s].y, kv[s].z, kv[s].w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float x = bf16_bits_to_f32((w[c / 2] >> (16 * (c & 1))) & 0xffffu);
+        if (x < lo[c]) lo[c] = x;
+        if (x > hi[c]) hi[c] = x;
+      }
+    }
+    // V: channel d0 + c of the page is the row (head * D + d0 + c) of P slots;
+    // this block is its slots s0 .. s0 + SB - 1
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float x = bf16_bits_to_f32((w[c / 2] >> (16 * (c & 1))) & 0xffffu);
-      if (x < lo[c]) lo[c] = x;
-      if (x > hi[c]) hi[c] = x;
-    }
-  }
-  // V: channel d0 + c of the page is the row (head * D + d0 + c) of P slots
+      uint16_t *vrow = v_cache + (head * D + d0 + c) * P + s0;
+      const int sh = 16 * (c & 1);
+      if (full) {
+        uint32_t out[SB / 2];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint16_t *vrow = v_cache + (head * D + d0 + c) * P;
-    const int sh = 16 * (c & 1);
-    if (full) {
-      uint32_t out[P / 2];
+        for (int t = 0; t < SB / 2; ++t) {
+          const uint32_t *x0 = (const uint32_t *)&vv[2 * t];
+          const uint32_t *x1 = (const uint32_t *)&vv[2 * t + 1];
+          out[t] = ((x0[c / 2] >> sh) & 0xffffu) | (((x1[c / 2] >> sh) & 0xffffu) << 16);
+        }
 #pragma unroll
-      for (int t = 0; t < P / 2; ++t) {
-        const uint32_t* a = (const uint32_t *)&vv[2 * t];
-        const uint32_t* b = (const uint32_t *)&vv[2 * t + 1];
-        out[t] = ((a[c / 2] >> sh) & 0xffffu) | (((b[c / 2] >> sh) & 0xffffu) << 16);
-      }
+        for (int t = 0; t < SB / 8; ++t)
+          *(uint4 *)(vrow + 8 * t) =
+              make_uint4(out[4 * t], out[4 * t + 1], out[4 * t + 2], out[4 * t + 3]);
+      } else {
 #pragma unroll
-      for (int t = 0; t < P / 8; ++t)
-        *(uint4 *)(vrow + 8 * t) = make_uint4(out[4 * t], out[4 * t + 1], out[4 * t + 2], out[4 * t + 3]);
-    } else {
-#pragma unroll
-      for (int s = 0; s < P; ++s) {
-        const int pos = page * P + s;
-        if (pos < lo_pos || pos >= hi_pos) continue;
-        const uint32_t *a = (const uint32_t *)&vv[s];
-        vrow[s] = (uint16_t)((a[c / 2] >> sh) & 0xffffu);
+        for (int s = 0; s < SB; ++s) {
+          const int pos = b_lo + s;
+          if (pos < lo_pos || pos >= hi_pos) continue;
+          const uint32_t *x0 = (const uint32_t *)&vv[s];
+          vrow[s] = (uint16_t)((x0[c / 2] >> sh) & 0xffffu);
+        }
       }
     }
   }
@@ -190,16 +198,15 @@ hipError_t launch_append(const Dims &dm, int batch, const void *k_new,
              aligned16(v_cache) && aligned16(kmeta) && dm.D % 8 == 0) {
     const long units = pages * dm.Hkv * (dm.D / 8);
     dim3 vgrid((unsigned)((units + 255) / 256), (unsigned)batch);
-    if (dm.P == 16)
-      hipLaunchKernelGGL(append_pages_kernel<16>, vgrid, block, 0, stream, dm.Hkv, dm.D, dm.pool,
-                         dm.max_pages, (const uint16_t *)k_new, (const uint16_t *)v_new,
-                         cu_new, ctx_before, page_table, (uint16_t *)k_cache,
-                         (uint16_t *)v_cache, (uint16_t *)kmeta);
-    else
-      hipLaunchKernelGGL(append_pages_kernel<32>, vgrid, block, 0, stream, dm.Hkv, dm.D, dm.pool,
-                         dm.max_pages, (const uint16_t *)k_new, (const uint16_t *)v_new,
-                         cu_new, ctx_before, page_table, (uint16_t *)k_cache,
-                         (uint16_t *)v_cache, (uint16_t *)kmeta);
+#define QUEST_APPEND_PAGES(PP)                                                            \
+  hipLaunchKernelGGL(append_pages_kernel<PP>, vgrid, block, 0, stream, dm.Hkv, dm.D, dm.pool,   \
+                     dm.max_pages, (const uint16_t *)k_new, (const uint16_t *)v_new, cu_new,   \
+                     ctx_before, page_table, (uint16_t *)k_cache, (uint16_t *)v_cache,        \
+                     (uint16_t *)kmeta)
+    if (dm.P == 16) QUEST_APPEND_PAGES(16);
+    else if (dm.P == 32) QUEST_APPEND_PAGES(32);
+    else QUEST_APPEND_PAGES(64);
+#undef QUEST_APPEND_PAGES
   } else {
     hipLaunchKernelGGL(append_kv_kernel<uint16_t>, grid, block, 0, stream, dm.Hkv, dm.D,
                        dm.P, dm.pool, dm.max_pages, (const uint16_t *)k_new,

@@ -42,10 +42,10 @@ constexpr int kMaxSplits = 256;        // per (request, KV head); bounds the par
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Pages one wave loads at once (one round): 32 KB of K and V per wave in
-// flight for 16-token pages at D = 128 (fewer for 32-token pages at D = 128,
-// to fit the registers).
+// flight at D = 128 (4 pages of 16 tokens, 2 of 32, 1 of 64), so the page
+// registers stay within budget.
 __host__ __device__ constexpr int pages_per_wave(int P, int D) {
-  return (P * D <= 2048) ? 4 : 2;
+  return (P * D <= 2048) ? 4 : (P * D <= 4096 ? 2 : 1);
 }
 // Pages folded into the running softmax per update.  The loads of a round
 // are issued group by group (K then V of each group), so a group's update
@@ -585,8 +585,10 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
                      ctx_lens, sel_pages, num_sel, workspace)
     if (dm.D == 128 && dm.P == 16) QUEST_DECODE(128, 16);
     else if (dm.D == 128 && dm.P == 32) QUEST_DECODE(128, 32);
+    else if (dm.D == 128 && dm.P == 64) QUEST_DECODE(128, 64);
     else if (dm.D == 64 && dm.P == 16) QUEST_DECODE(64, 16);
-    else QUEST_DECODE(64, 32);
+    else if (dm.D == 64 && dm.P == 32) QUEST_DECODE(64, 32);
+    else QUEST_DECODE(64, 64);
 #undef QUEST_DECODE
 #undef QUEST_DECODE_G
   } else {

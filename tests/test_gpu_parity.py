@@ -44,6 +44,12 @@ SMALL = {
                                   budget_tokens=600, steps=2, seed=80, poison=float("nan")),
     "g12_d64": workloads.Workload("g12_d64", 2, 24, 2, 64, 16, "bf16", ctx_list=(500, 2000),
                                   budget_tokens=256, steps=2, seed=81, permute_pages=True),
+    # 64-token pages (one page per wave and round in the decode)
+    "p64_d128": workloads.Workload("p64_d128", 4, 32, 4, 128, 64, "bf16",
+                                   ctx_list=(1, 64, 1000, 6001), budget_tokens=640, steps=2,
+                                   seed=82, poison=float("nan"), permute_pages=True),
+    "p64_d64_f32": workloads.Workload("p64_d64_f32", 2, 8, 2, 64, 64, "f32", ctx=2100,
+                                      budget_tokens=500, steps=2, seed=83),
 }
 
 
@@ -154,12 +160,13 @@ def test_incremental_append_equals_bulk(gpu_lib):
         assert torch.equal(km[phys].view(torch.int16), bulk.kmeta[phys].view(torch.int16))
 
 
-def test_unaligned_and_chunked_append_match(gpu_lib):
+@pytest.mark.parametrize("page_size", [16, 32, 64])
+def test_unaligned_and_chunked_append_match(page_size, gpu_lib):
     """The same tokens stored three ways give identical pools and metadata:
     one bulk append (16-byte vector path), chunks of 37 tokens that start and
     end inside pages, and one bulk append from source tensors shifted off
     16-byte alignment (the scalar path)."""
-    w = scaled(WORKLOADS["ragged"], batch=3, ctx_range=(200, 900), steps=0)
+    w = scaled(WORKLOADS["ragged"], batch=3, ctx_range=(200, 900), steps=0, page_size=page_size)
     ref = Layer(w, DEV, host=False)
     k_new, v_new, cu, _ = workloads.prefill_tokens(w, ref.lay, DEV)
     cuh = cu.cpu().tolist()
@@ -250,7 +257,8 @@ def _topk_rows(n_max, gen):
     return rows
 
 
-@pytest.mark.parametrize("n_max,P", [(64, 16), (300, 16), (2050, 32), (8008, 16), (10000, 16)])
+@pytest.mark.parametrize("n_max,P", [(64, 16), (300, 16), (2050, 32), (8008, 16), (10000, 16),
+                                     (500, 64)])
 def test_topk_exact(n_max, P, gpu_lib):
     gen = torch.Generator().manual_seed(5000 + n_max)
     rows = _topk_rows(n_max, gen)
