@@ -78,12 +78,15 @@ def load(path):
     L.qo_request_scores.argtypes = [sp, vp, vp, i32, i32, vp]
     L.qo_pages_for_budget.argtypes = [i32, i32, i32]
     L.qo_pages_for_budget.restype = i32
+    L.qo_request_head_scores.argtypes = [sp, vp, vp, i32, vp]
+    L.qo_request_attend_heads.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, i32, f64, vp]
     L.qo_select.argtypes = [vp, i32, i32, vp]
     L.qo_select_forced.argtypes = [vp, i32, i32, i32, i32, vp]
     L.qo_request_attend.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, i32, f64, vp]
     L.qo_request_dense.argtypes = [sp, vp, vp, vp, vp, i32, f64, vp]
     for fn in (L.qo_store_tokens, L.qo_request_bounds, L.qo_page_bounds,
-               L.qo_request_scores, L.qo_select, L.qo_select_forced, L.qo_request_attend,
+               L.qo_request_scores, L.qo_request_head_scores, L.qo_request_attend_heads,
+               L.qo_select, L.qo_select_forced, L.qo_request_attend,
                L.qo_request_dense):
         fn.restype = None
     return L
@@ -185,6 +188,16 @@ def request_scores(s: Shape, q_r, bounds, reduce="max") -> np.ndarray:
     return out
 
 
+def request_head_scores(s: Shape, q_r, bounds) -> np.ndarray:
+    """fp64 [Hq][n_pages]: every q head's own page bound (no group reduction)."""
+    _check(q_r, s.storage_dtype(), (s.Hq, s.D), "q")
+    n = bounds.shape[0]
+    _check(bounds, np.float64, (n, s.Hkv, 2, s.D), "bounds")
+    out = np.empty((s.Hq, n), np.float64)
+    lib().qo_request_head_scores(s.c, _ptr(q_r), _ptr(bounds), n, _ptr(out))
+    return out
+
+
 def pages_for_budget(budget_tokens, ctx, page_size) -> int:
     return int(lib().qo_pages_for_budget(int(budget_tokens), int(ctx), int(page_size)))
 
@@ -205,6 +218,19 @@ def select(scores_row, k, n_sink=0, n_recent=0) -> np.ndarray:
     return out[:k].copy()
 
 
+def _page_table(sel, rows, n):
+    stride = max([len(x) for x in sel] + [1])
+    table = np.full((rows, stride), -1, np.int32)
+    nsel = np.zeros(rows, np.int32)
+    for g, pages in enumerate(sel):
+        pages = np.asarray(pages, np.int32)
+        if pages.size and (pages.min() < 0 or pages.max() >= n):
+            raise ValueError("selected page outside the request")
+        table[g, :pages.size] = pages
+        nsel[g] = pages.size
+    return table, nsel, stride
+
+
 def request_attend(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, sel, sm_scale) -> np.ndarray:
     """fp64 [Hq][D]: attention of one request over the pages in ``sel``.
 
@@ -214,19 +240,28 @@ def request_attend(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, sel, sm_scale) 
     n = _check_row(s, pt_row, ctx)
     if len(sel) != s.Hkv:
         raise ValueError("need one page list per KV head")
-    stride = max([len(x) for x in sel] + [1])
-    table = np.full((s.Hkv, stride), -1, np.int32)
-    nsel = np.zeros(s.Hkv, np.int32)
-    for g, pages in enumerate(sel):
-        pages = np.asarray(pages, np.int32)
-        if pages.size and (pages.min() < 0 or pages.max() >= n):
-            raise ValueError("selected page outside the request")
-        table[g, :pages.size] = pages
-        nsel[g] = pages.size
+    table, nsel, stride = _page_table(sel, s.Hkv, n)
     out = np.empty((s.Hq, s.D), np.float64)
     lib().qo_request_attend(s.c, _ptr(q_r), _ptr(k_cache), _ptr(v_cache), _ptr(pt_row),
                             int(ctx), _ptr(table), _ptr(nsel), stride, float(sm_scale),
                             _ptr(out))
+    return out
+
+
+def request_attend_heads(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, sel,
+                         sm_scale) -> np.ndarray:
+    """fp64 [Hq][D]: attention with one page list per q head (``sel`` has Hq
+    integer arrays of logical ids)."""
+    _check_pool(s, k_cache, v_cache)
+    _check(q_r, s.storage_dtype(), (s.Hq, s.D), "q")
+    n = _check_row(s, pt_row, ctx)
+    if len(sel) != s.Hq:
+        raise ValueError("need one page list per q head")
+    table, nsel, stride = _page_table(sel, s.Hq, n)
+    out = np.empty((s.Hq, s.D), np.float64)
+    lib().qo_request_attend_heads(s.c, _ptr(q_r), _ptr(k_cache), _ptr(v_cache), _ptr(pt_row),
+                                  int(ctx), _ptr(table), _ptr(nsel), stride, float(sm_scale),
+                                  _ptr(out))
     return out
 
 
@@ -242,14 +277,22 @@ def request_dense(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, sm_scale) -> np.
 
 
 def decode_request(s: Shape, q_r, k_cache, v_cache, pt_row, ctx, budget_tokens,
-                   sm_scale, reduce="max", bounds=None, n_sink=0, n_recent=0) -> dict:
+                   sm_scale, reduce="max", bounds=None, n_sink=0, n_recent=0,
+                   per_q_head=False) -> dict:
     """One request's decode view and output: bounds, scores, k, selection, out.
 
-    ``bounds`` may be passed when already computed for the same pool state."""
+    ``bounds`` may be passed when already computed for the same pool state.
+    per_q_head: every q head scores and selects its own pages (``reduce`` is
+    not used); scores and sel then have one row per q head."""
     if bounds is None:
         bounds = request_bounds(s, k_cache, pt_row, ctx)
-    scores = request_scores(s, q_r, bounds, reduce)
     k = pages_for_budget(budget_tokens, ctx, s.P)
+    if per_q_head:
+        scores = request_head_scores(s, q_r, bounds)
+        sel = [select(scores[h], k, n_sink, n_recent) for h in range(s.Hq)]
+        out = request_attend_heads(s, q_r, k_cache, v_cache, pt_row, ctx, sel, sm_scale)
+        return {"bounds": bounds, "scores": scores, "k": k, "sel": sel, "out": out}
+    scores = request_scores(s, q_r, bounds, reduce)
     sel = [select(scores[g], k, n_sink, n_recent) for g in range(s.Hkv)]
     out = request_attend(s, q_r, k_cache, v_cache, pt_row, ctx, sel, sm_scale)
     return {"bounds": bounds, "scores": scores, "k": k, "sel": sel, "out": out}

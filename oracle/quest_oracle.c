@@ -164,6 +164,30 @@ void qo_request_scores(const qo_shape *s, const void *q_r,
   }
 }
 
+/* Per-q-head scores (READING, a variant the pages leave open: the selection
+ * is not shared across a GQA group): U[h][j] of every q head h, which reads
+ * the bounds of its KV head h / G.  By definition this is the group score of
+ * a group of one head, so it is computed as exactly that. */
+void qo_request_head_scores(const qo_shape *s, const void *q_r,
+                            const double *bounds, int32_t n_pages, double *scores) {
+  const int32_t Hq = s->num_q_heads, H = s->num_kv_heads, D = s->head_dim;
+  const int32_t G = Hq / H;
+  const size_t esz = elem_bytes(s->elem);
+  qo_shape one = *s;
+  one.num_q_heads = 1;
+  one.num_kv_heads = 1;
+  double *b1 = (double *)malloc(sizeof(double) * ((size_t)n_pages * 2 * D + 1));
+  for (int32_t h = 0; h < Hq; ++h) {
+    const int32_t kvh = h / G;
+    for (int32_t j = 0; j < n_pages; ++j)
+      memcpy(b1 + (int64_t)j * 2 * D, bounds + ((int64_t)j * H + kvh) * 2 * D,
+             sizeof(double) * 2 * (size_t)D);
+    qo_request_scores(&one, (const char *)q_r + (size_t)h * D * esz, b1, n_pages,
+                      QO_REDUCE_MAX, scores + (int64_t)h * n_pages);
+  }
+  free(b1);
+}
+
 /* ---- build_decode_view: top-k within the token budget ------------------- */
 
 /* READING: a budget of B tokens buys floor(B / P) whole pages, at least one
@@ -309,6 +333,17 @@ void qo_request_attend(const qo_shape *s, const void *q_r, const void *k_cache,
                     sel + (int64_t)g * sel_stride, nsel[g], h, sm_scale,
                     out + (int64_t)h * s->head_dim);
   }
+}
+
+/* Attention with one selection per q head: head h attends the pages in
+ * sel[h][0 .. nsel[h]-1] of its KV head. */
+void qo_request_attend_heads(const qo_shape *s, const void *q_r, const void *k_cache,
+                             const void *v_cache, const int32_t *pt_row, int32_t ctx,
+                             const int32_t *sel, const int32_t *nsel,
+                             int32_t sel_stride, double sm_scale, double *out) {
+  for (int32_t h = 0; h < s->num_q_heads; ++h)
+    attend_one_head(s, q_r, k_cache, v_cache, pt_row, ctx, sel + (int64_t)h * sel_stride,
+                    nsel[h], h, sm_scale, out + (int64_t)h * s->head_dim);
 }
 
 /* Dense attention is the view that holds every page (the vanilla method). */

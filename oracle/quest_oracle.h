@@ -60,6 +60,11 @@ void qo_request_scores(const qo_shape *s, const void *q_r,
                        const double *bounds, int32_t n_pages, int32_t reduce,
                        double *scores);
 
+/* Per-q-head page scores [Hq][n_pages]: each head's own bound, no group
+ * reduction. */
+void qo_request_head_scores(const qo_shape *s, const void *q_r,
+                            const double *bounds, int32_t n_pages, double *scores);
+
 /* Number of pages a token budget buys for a request of ctx tokens. */
 int32_t qo_pages_for_budget(int32_t budget_tokens, int32_t ctx,
                             int32_t page_size);
@@ -77,6 +82,12 @@ void qo_request_attend(const qo_shape *s, const void *q_r, const void *k_cache,
                        const void *v_cache, const int32_t *pt_row, int32_t ctx,
                        const int32_t *sel, const int32_t *nsel,
                        int32_t sel_stride, double sm_scale, double *out);
+
+/* Attention with one selection per q head: sel is [Hq][sel_stride], nsel [Hq]. */
+void qo_request_attend_heads(const qo_shape *s, const void *q_r, const void *k_cache,
+                             const void *v_cache, const int32_t *pt_row, int32_t ctx,
+                             const int32_t *sel, const int32_t *nsel,
+                             int32_t sel_stride, double sm_scale, double *out);
 
 /* Dense attention: every valid token of the request. */
 void qo_request_dense(const qo_shape *s, const void *q_r, const void *k_cache,

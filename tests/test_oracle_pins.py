@@ -218,6 +218,35 @@ def pin_group_reduce(dtype):
                        rtol=1e-13, atol=1e-12)
 
 
+def pin_per_head_selection(dtype):
+    """Per-q-head selection reduces to the pinned grouped path on a pool with
+    one KV head per q head (KV head h // G copied to slot h, G = 1 there):
+    each head's own scores are that pool's group scores, and attention with
+    one page list per q head is that pool's attention with the same lists."""
+    gen = torch.Generator().manual_seed(25)
+    Hq, Hkv, D, P, ctx = 8, 2, 8, 4, 37
+    G = Hq // Hkv
+    s, pt, _, _, k_pool, v_pool, q = _request(gen, Hq, Hkv, D, P, ctx, dtype)
+    b = oracle.request_bounds(s, k_pool, pt, ctx)
+    s1 = shape_of(Hq, Hq, D, P, s.pool, dtype)
+    k1 = np.ascontiguousarray(np.repeat(k_pool, G, axis=1))
+    v1 = np.ascontiguousarray(np.repeat(v_pool, G, axis=1))
+    b1 = oracle.request_bounds(s1, k1, pt, ctx)
+    heads = oracle.request_head_scores(s, q, b)
+    assert np.array_equal(heads, oracle.request_scores(s1, q, b1, "max"))
+    for budget in (4, 13, 40):
+        r = oracle.decode_request(s, q, k_pool, v_pool, pt, ctx, budget, 0.3, per_q_head=True)
+        k = oracle.pages_for_budget(budget, ctx, P)
+        assert len(r["sel"]) == Hq
+        assert all(np.array_equal(r["sel"][h], oracle.select(heads[h], k)) for h in range(Hq))
+        want = oracle.request_attend(s1, q, k1, v1, pt, ctx, r["sel"], 0.3)
+        assert np.array_equal(r["out"], want)
+    # with every page selected, per-head and shared selection are both dense
+    full = oracle.decode_request(s, q, k_pool, v_pool, pt, ctx, 10 ** 6, 0.3, per_q_head=True)
+    assert np.array_equal(full["out"],
+                          oracle.request_dense(s, q, k_pool, v_pool, pt, ctx, 0.3))
+
+
 # --------------------------------------------------------------------------
 # budget and selection
 # --------------------------------------------------------------------------
@@ -379,8 +408,8 @@ def pin_budget_covering_all_is_dense(dtype):
 PINS = [
     pin_hand_example, pin_store_layout, pin_store_incremental_equals_bulk,
     pin_bounds_contain_and_attain, pin_score_is_box_maximum, pin_score_bounds_every_key,
-    pin_score_closed_forms, pin_group_reduce, pin_budget_table, pin_select_bruteforce,
-    pin_select_forced,
+    pin_score_closed_forms, pin_group_reduce, pin_per_head_selection, pin_budget_table,
+    pin_select_bruteforce, pin_select_forced,
     pin_dense_equals_sdpa, pin_sparse_equals_masked_sdpa, pin_attention_closed_forms,
     pin_permutation_invariance, pin_budget_covering_all_is_dense,
 ]
@@ -435,6 +464,11 @@ MUTANTS = {
                                             "return j < n_sink || j < n_recent;"),
     "forced pages not ranked first": ("if (a->forced != b->forced) return a->forced ? -1 : 1;",
                                       ""),
+    "head scores read KV head h mod Hkv": ("const int32_t kvh = h / G;",
+                                           "const int32_t kvh = h % H;"),
+    "per-head attention uses the group's first list": (
+        "sel + (int64_t)h * sel_stride,",
+        "sel + (int64_t)(h - h % (s->num_q_heads / s->num_kv_heads)) * sel_stride,"),
 }
 
 
