@@ -80,6 +80,14 @@ typedef enum { QUEST_F32 = 0, QUEST_BF16 = 1 } quest_dtype;
  * every q head of the group; SUM bounds the group-summed logit. */
 typedef enum { QUEST_REDUCE_MAX = 0, QUEST_REDUCE_SUM = 1 } quest_group_reduce;
 
+/* Whose pages are selected (a variant the pages leave open).  PER_KV_HEAD:
+ * the q heads of a KV head share one selection from the group score (the
+ * layout's R = Hkv selection rows per request).  PER_Q_HEAD: every q head
+ * scores and selects its own pages from its own bound, with no group
+ * reduction (R = Hq rows per request); each q head then attends its own
+ * pages, so the selected K/V bytes grow with the group size. */
+typedef enum { QUEST_SELECT_PER_KV_HEAD = 0, QUEST_SELECT_PER_Q_HEAD = 1 } quest_selection;
+
 /* Shape of one attention layer's paged cache.
  *   num_q_heads (Hq) and num_kv_heads (Hkv): Hq % Hkv == 0, G = Hq/Hkv <= 16;
  *     q head h reads KV head h / G.
@@ -87,7 +95,10 @@ typedef enum { QUEST_REDUCE_MAX = 0, QUEST_REDUCE_SUM = 1 } quest_group_reduce;
  *   fp32 only at D = 64).
  *   dtype: quest_dtype of q, K, V, metadata and output.
  *   num_pool_pages: physical pages in the pool shared by all requests.
- *   max_pages_per_seq: row stride of the page table and of the score array. */
+ *   max_pages_per_seq: row stride of the page table and of the score array.
+ *   selection: quest_selection; it fixes R, the selection rows per request
+ *     (R = Hkv per KV head, R = Hq per q head).  Other values return
+ *     QUEST_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t abi_version;
   int32_t num_q_heads;
@@ -97,7 +108,7 @@ typedef struct {
   int32_t dtype;
   int64_t num_pool_pages;
   int32_t max_pages_per_seq;
-  int32_t reserved;           /* set to 0 */
+  int32_t selection;          /* quest_selection (0: per KV head) */
 } quest_layout;
 
 /* Device layouts (row-major, contiguous):
@@ -110,9 +121,11 @@ typedef struct {
  *              p % P.  Only entries j < ceil(ctx/P) are read.
  *   ctx_lens   int32 [batch]: valid tokens of each request.
  *   q, out     [batch][Hq][D]
- *   scores     fp32 [batch][Hkv][max_pages_per_seq]
+ *   scores     fp32 [batch][R][max_pages_per_seq]
  *   budget_tokens int32 [batch]
- *   sel_pages  int32 [batch][Hkv][max_k]; num_sel int32 [batch][Hkv] */
+ *   sel_pages  int32 [batch][R][max_k]; num_sel int32 [batch][R]
+ * (R = Hkv with the default per-KV-head selection; below, "row g" is KV head
+ * g then, or q head g with per-q-head selection.) */
 
 /* Returns QUEST_ABI_VERSION of the loaded library. */
 int quest_abi_version(void);
@@ -146,6 +159,8 @@ int quest_append_kv(const quest_layout *layout, int32_t batch,
  *   U[h][j] = sum_d max(q[r][h][d]*min[j][g][d], q[r][h][d]*max[j][g][d])
  * for each q head h of group g (q unscaled), and
  *   scores[r][g][j] = max_h U[h][j]   (group_reduce MAX) or sum_h (SUM).
+ * With per-q-head selection there is no reduction: scores[r][h][j] = U[h][j]
+ * for every q head h (group_reduce is still validated but has no effect).
  * Products of bf16 values are exact in fp32; sums are fp32 in an unspecified
  * order.  Entries j >= ceil(ctx/P) are not written. */
 int quest_page_scores(const quest_layout *layout, int32_t batch,
@@ -169,7 +184,7 @@ int quest_append_score(const quest_layout *layout, int32_t batch, const void *q,
                        void *kmeta, int32_t group_reduce, float *scores, void *stream);
 
 /* build_decode_view, part 2: k_r = min(max_k, clamp(floor(budget_tokens[r] /
- * P), 1, n_r)) pages per (request, KV head), n_r = ceil(ctx_lens[r]/P);
+ * P), 1, n_r)) pages per (request, selection row), n_r = ceil(ctx_lens[r]/P);
  * k_r = 0 when ctx_lens[r] == 0.  The k_r pages with the largest scores are
  * selected; equal scores go to the lower logical page (-0.0 equals +0.0).
  * sel_pages[r][g][0..k_r-1] receives their logical ids in ascending order,
@@ -203,8 +218,9 @@ size_t quest_sparse_decode_workspace_bytes(const quest_layout *layout,
 /* Attention over the explicit-KV view (SparseEngine digest, Method key
  * points, AttentionView): for q head h of request r, with g = h / G,
  *   out[r][h] = sum_t softmax_t(sm_scale * q[r][h].k_t) v_t
- * over the valid tokens t (< ctx_lens[r]) of the pages sel_pages[r][g][0 ..
- * num_sel[r][g]-1].  A head with no token in its view outputs zeros.
+ * over the valid tokens t (< ctx_lens[r]) of KV head g in the pages
+ * sel_pages[r][x][0 .. num_sel[r][x]-1] of its selection row x (x = g per KV
+ * head, x = h per q head).  A head with no token in its view outputs zeros.
  * Split-K: pages are spread over work-groups, each keeps a running max, sum
  * and fp32 accumulator, and a second kernel merges the partials.  The bf16
  * path feeds each fp32 softmax weight to the matrix-core P*V product as the
@@ -219,7 +235,7 @@ int quest_sparse_decode(const quest_layout *layout, int32_t batch,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Launch plan quest_sparse_decode uses (for reports): number of KV splits per
- * (request, KV head) and pages per split.  Never calls HIP. */
+ * (request, selection row) and pages per split.  Never calls HIP. */
 int quest_sparse_decode_plan(const quest_layout *layout, int32_t batch,
                              int32_t max_k, int32_t *num_splits,
                              int32_t *pages_per_split);

@@ -60,9 +60,11 @@ struct FusedAppend {
   uint16_t *k_cache, *v_cache;
 };
 
+// per_head: no group reduction; q head h of KV head g writes its own score
+// row r * Hq + g * G + h (selection per q head).
 template <int D, bool kAppend>
 __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
-    int Hkv, int G, int64_t pool, int P, int max_pages, int reduce,
+    int Hkv, int G, int per_head, int64_t pool, int P, int max_pages, int reduce,
     const uint16_t *__restrict__ q, uint16_t *kmeta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
     FusedAppend fa, float *__restrict__ scores) {
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
   if (base >= n) return;
 
   const int32_t *pt = page_table + (int64_t)r * max_pages;
-  float *out = scores + ((int64_t)r * Hkv + g) * max_pages;
+  float *out = scores + (per_head ? (int64_t)(r * Hkv + g) * G : (int64_t)r * Hkv + g) *
+                            max_pages;
 
   // Metadata row of this lane's page in each of the wave's tiles; pages past
   // the request (or with an id outside the pool) read physical page 0 and are
@@ -173,7 +176,14 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], as_bf16x8(b[t][c]), acc, 0, 0, 0);
-    // lane holds page `col`, heads 4*grp .. 4*grp+3: combine the group.
+    // lane holds page `col`, heads 4*grp .. 4*grp+3
+    if (per_head) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * grp + i < G && page[t] < n) out[(int64_t)(4 * grp + i) * max_pages + page[t]] = acc[i];
+      continue;
+    }
+    // combine the group
     float v = reduce == 0 ? -__builtin_huge_valf() : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
 // With cu_new non-null the request length is ctx_before + its new tokens
 // (the fused path, after a separate append launch), else ctx_lens.
 __global__ __launch_bounds__(256) void page_scores_valu_kernel(
-    int Hkv, int G, int D, int64_t pool, int P, int max_pages, int reduce,
+    int Hkv, int G, int per_head, int D, int64_t pool, int P, int max_pages, int reduce,
     const float *__restrict__ q, const float *__restrict__ kmeta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
     const int32_t *__restrict__ cu_new, const int32_t *__restrict__ ctx_before,
@@ -218,9 +228,11 @@ __global__ __launch_bounds__(256) void page_scores_valu_kernel(
       const float qd = q_lds[h * D + d];
       u += qd >= 0.f ? qd * hi[d] : qd * lo[d];
     }
+    if (per_head)
+      scores[((int64_t)(r * Hkv + g) * G + h) * max_pages + j] = u;
     v = reduce == 0 ? fmaxf(v, u) : v + u;
   }
-  scores[((int64_t)r * Hkv + g) * max_pages + j] = v;
+  if (!per_head) scores[((int64_t)r * Hkv + g) * max_pages + j] = v;
 }
 
 static hipError_t launch_scores(const Dims &dm, int batch, const void *q, void *kmeta,
@@ -233,6 +245,7 @@ static hipError_t launch_scores(const Dims &dm, int batch, const void *q, void *
     dim3 block(64 * kScoreWaves);
 #define QUEST_SCORES(DD, AA)                                                                \
   hipLaunchKernelGGL((page_scores_mfma_kernel<DD, AA>), grid, block, 0, stream, dm.Hkv, dm.G, \
+                     (int)dm.per_head(),                                                    \
                      dm.pool, dm.P, dm.max_pages, reduce, (const uint16_t *)q,              \
                      (uint16_t *)kmeta, page_table, ctx_lens, fa, scores)
     if (dm.D == 128) {
@@ -244,7 +257,8 @@ static hipError_t launch_scores(const Dims &dm, int batch, const void *q, void *
   } else {
     dim3 grid((unsigned)((dm.max_pages + 255) / 256), (unsigned)dm.Hkv, (unsigned)batch);
     hipLaunchKernelGGL(page_scores_valu_kernel, grid, dim3(256),
-                       (size_t)dm.G * dm.D * sizeof(float), stream, dm.Hkv, dm.G, dm.D,
+                       (size_t)dm.G * dm.D * sizeof(float), stream, dm.Hkv, dm.G,
+                       (int)dm.per_head(), dm.D,
                        dm.pool, dm.P, dm.max_pages, reduce, (const float *)q,
                        (const float *)kmeta, page_table, ctx_lens,
                        fused ? fa.cu_new : nullptr, fused ? fa.ctx_before : nullptr, scores);

@@ -40,9 +40,20 @@ int check_layout(const quest_layout *L, Dims &dm) {
   if (G > 16) return QUEST_ERR_UNSUPPORTED;
   // keep per-request token counts inside int32 arithmetic
   if ((int64_t)L->max_pages_per_seq * L->page_size > INT32_MAX) return QUEST_ERR_SHAPE;
+  if (L->selection != QUEST_SELECT_PER_KV_HEAD && L->selection != QUEST_SELECT_PER_Q_HEAD)
+    return QUEST_ERR_UNSUPPORTED;
   dm.Hq = L->num_q_heads;
   dm.Hkv = L->num_kv_heads;
   dm.G = G;
+  if (L->selection == QUEST_SELECT_PER_Q_HEAD) {
+    dm.R = dm.Hq;
+    dm.Gcols = 1;
+    dm.gdiv = G;
+  } else {
+    dm.R = dm.Hkv;
+    dm.Gcols = G;
+    dm.gdiv = 1;
+  }
   dm.D = L->head_dim;
   dm.P = L->page_size;
   dm.dtype = L->dtype;
@@ -53,7 +64,7 @@ int check_layout(const quest_layout *L, Dims &dm) {
 
 int check_batch(int32_t batch, const Dims &dm) {
   if (batch < 0 || batch > 65535) return QUEST_ERR_SHAPE;
-  if ((int64_t)batch * dm.Hkv > INT32_MAX / 16) return QUEST_ERR_SHAPE;
+  if ((int64_t)batch * dm.Hq > INT32_MAX / 16) return QUEST_ERR_SHAPE;
   return QUEST_OK;
 }
 

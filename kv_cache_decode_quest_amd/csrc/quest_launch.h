@@ -13,6 +13,12 @@ struct Dims {
   int dtype;          // 0 fp32, 1 bf16
   int64_t pool;       // physical pages
   int max_pages;      // page-table row stride
+  // Selection rows: a request has R rows of scores / selections, row x holds
+  // q heads x*Gcols .. x*Gcols+Gcols-1 and reads KV head x / gdiv.  Shared
+  // per KV head: R = Hkv, Gcols = G, gdiv = 1; per q head: R = Hq, Gcols = 1,
+  // gdiv = G.
+  int R, Gcols, gdiv;
+  bool per_head() const { return R != Hkv || Gcols != G; }
 };
 
 hipError_t launch_append(const Dims &dm, int batch, const void *k_new,

@@ -62,7 +62,7 @@ DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
   DecodePlan p{1, max_k > 0 ? max_k : 1};
   if (batch <= 0 || max_k <= 0) return p;
   const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
-  const long rows = (long)batch * dm.Hkv;
+  const long rows = (long)batch * dm.R;
   const long want_splits = std::max(1L, (kTargetWorkGroups + rows - 1) / rows);
   long rounds = 1;
   while ((max_k + per_round * rounds - 1) / (per_round * rounds) >
@@ -77,7 +77,7 @@ DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
 size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k) {
   if (batch <= 0) return 0;
   const DecodePlan p = decode_plan(dm, batch, max_k);
-  return (size_t)batch * dm.Hkv * p.n_split * dm.G * (dm.D + 2) * sizeof(float);
+  return (size_t)batch * dm.R * p.n_split * dm.Gcols * (dm.D + 2) * sizeof(float);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -254,8 +254,8 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *vali
 
 template <int D, int P, bool kPack>
 __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
-    int Hkv, int G, int64_t pool, int max_pages, int max_k, int n_split, int pps,
-    float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
+    int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k, int n_split,
+    int pps, float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
     const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
@@ -272,7 +272,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
   const int col = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x % n_split;
   const int row = blockIdx.x / n_split;
-  const int r = row / Hkv, g = row - r * Hkv;
+  // selection row `row` = request r, row hr of the request: q heads
+  // hr*G .. hr*G+G-1 of the request, reading KV head hr / gdiv
+  const int r = row / R, hr = row - r * R, g = hr / gdiv;
   const int first = split * pps;
   const int32_t *sel = sel_pages + (int64_t)row * max_k;
   const int32_t *pt = page_table + (int64_t)r * max_pages;
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
   // outstanding load at the join.
   bf16x8 qop[PR::KC];
   {
-    const uint16_t *qh = q + ((int64_t)r * Hkv * G + (int64_t)g * G + (col < G ? col : 0)) * D;
+    const uint16_t *qh = q + ((int64_t)r * R * G + (int64_t)hr * G + (col < G ? col : 0)) * D;
     uint4 w[PR::KC];
 #pragma unroll
     for (int c = 0; c < PR::KC; ++c) w[c] = *(const uint4 *)(qh + c * 32 + grp * 8);
@@ -397,8 +399,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
 // staging each K and V page in LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
-    int Hkv, int G, int D, int P, int64_t pool, int max_pages, int max_k, int n_split,
-    int pps, float scale2, const float *__restrict__ q, const float *__restrict__ k_cache,
+    int R, int G, int Hkv, int gdiv, int D, int P, int64_t pool, int max_pages, int max_k,
+    int n_split, int pps, float scale2, const float *__restrict__ q,
+    const float *__restrict__ k_cache,
     const float *__restrict__ v_cache, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
     const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
 
   const int split = blockIdx.x % n_split;
   const int row = blockIdx.x / n_split;
-  const int r = row / Hkv, g = row - r * Hkv;
+  const int r = row / R, hr = row - r * R, g = hr / gdiv;
   const int nsel = min(num_sel[row], max_k);
   const int first = split * pps;
   if (first >= nsel) {                             // no page in this split:
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
   const int32_t *sel = sel_pages + (int64_t)row * max_k;
   const int32_t *pt = page_table + (int64_t)r * max_pages;
 
-  const float *qg = q + ((int64_t)r * Hkv * G + (int64_t)g * G) * D;
+  const float *qg = q + ((int64_t)r * R * G + (int64_t)hr * G) * D;
   for (int x = threadIdx.x; x < G * D; x += blockDim.x) q_s[x] = qg[x];
   for (int h = threadIdx.x; h < G; h += blockDim.x) {
     m_s[h] = -__builtin_huge_valf();
@@ -516,14 +519,14 @@ constexpr int kMergeChunk = 16;
 // Every split writes a partial (an empty one has max -inf and sum 0), so the
 // merge reads all n_split of them without waiting for the selection count.
 template <typename T>
-__global__ __launch_bounds__(128) void merge_kernel(int Hkv, int G, int D, int n_split,
+__global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_split,
                                                     const float *__restrict__ partial,
                                                     T *__restrict__ out) {
   const int hq = blockIdx.x;                 // r * Hq + h
-  const int Hq = Hkv * G;
+  const int Hq = R * G;
   const int r = hq / Hq, h = hq - r * Hq;
   const int g = h / G, hl = h - g * G;
-  const int row = r * Hkv + g;
+  const int row = r * R + g;
   const int live = n_split;
   const int64_t stride = (int64_t)G * (D + 2);
   const float *base = partial + (int64_t)row * n_split * stride + (int64_t)hl * (D + 2);
@@ -570,16 +573,17 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
                          float *workspace, hipStream_t stream) {
   const DecodePlan plan = decode_plan(dm, batch, max_k);
   const float scale2 = sm_scale * kLog2e;
-  const unsigned blocks = (unsigned)((long)batch * dm.Hkv * plan.n_split);
+  const unsigned blocks = (unsigned)((long)batch * dm.R * plan.n_split);
   if (dm.dtype == 1) {
 #define QUEST_DECODE(DD, PP)                                                              \
   do {                                                                                    \
-    if (dm.G <= 8) QUEST_DECODE_G(DD, PP, true);                                          \
+    if (dm.Gcols <= 8) QUEST_DECODE_G(DD, PP, true);                                      \
     else QUEST_DECODE_G(DD, PP, false);                                                   \
   } while (0)
 #define QUEST_DECODE_G(DD, PP, PK)                                                        \
   hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP, PK>), dim3(blocks), dim3(kDecodeWaves * 64), 0, stream, \
-                     dm.Hkv, dm.G, dm.pool, dm.max_pages, max_k, plan.n_split,            \
+                     dm.R, dm.Gcols, dm.Hkv, dm.gdiv, dm.pool, dm.max_pages, max_k,       \
+                     plan.n_split,                                                        \
                      plan.pages_per_split, scale2, (const uint16_t *)q,                   \
                      (const uint16_t *)k_cache, (const uint16_t *)v_cache, page_table,    \
                      ctx_lens, sel_pages, num_sel, workspace)
@@ -592,23 +596,24 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
 #undef QUEST_DECODE
 #undef QUEST_DECODE_G
   } else {
-    const size_t lds = sizeof(float) * ((size_t)dm.G * dm.D + 2 * (size_t)dm.P * dm.D +
-                                        (size_t)dm.G * dm.P + 3 * (size_t)dm.G);
+    const size_t lds = sizeof(float) * ((size_t)dm.Gcols * dm.D + 2 * (size_t)dm.P * dm.D +
+                                        (size_t)dm.Gcols * dm.P + 3 * (size_t)dm.Gcols);
     hipLaunchKernelGGL(sparse_decode_valu_kernel, dim3(blocks), dim3(256), lds, stream,
-                       dm.Hkv, dm.G, dm.D, dm.P, dm.pool, dm.max_pages, max_k, plan.n_split,
+                       dm.R, dm.Gcols, dm.Hkv, dm.gdiv, dm.D, dm.P, dm.pool, dm.max_pages,
+                       max_k, plan.n_split,
                        plan.pages_per_split, scale2, (const float *)q, (const float *)k_cache,
                        (const float *)v_cache, page_table, ctx_lens, sel_pages, num_sel,
                        workspace);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned mblocks = (unsigned)((long)batch * dm.Hkv * dm.G);
+  const unsigned mblocks = (unsigned)((long)batch * dm.Hq);
   if (dm.dtype == 1)
-    hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.Hkv,
-                       dm.G, dm.D, plan.n_split, workspace, (uint16_t *)out);
+    hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.R,
+                       dm.Gcols, dm.D, plan.n_split, workspace, (uint16_t *)out);
   else
-    hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.Hkv,
-                       dm.G, dm.D, plan.n_split, workspace, (float *)out);
+    hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.R,
+                       dm.Gcols, dm.D, plan.n_split, workspace, (float *)out);
   return hipGetLastError();
 }
 

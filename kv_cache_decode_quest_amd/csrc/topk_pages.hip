@@ -136,15 +136,15 @@ constexpr uint32_t kForcedKey = 0xffffffffu;
 
 template <bool kRegs>
 __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
-    int Hkv, int P, int max_pages, int max_k, int n_sink, int n_recent,
+    int R, int P, int max_pages, int max_k, int n_sink, int n_recent,
     const float *__restrict__ scores, const int32_t *__restrict__ ctx_lens,
     const int32_t *__restrict__ budget_tokens, int32_t *__restrict__ sel_pages,
     int32_t *__restrict__ num_sel) {
   __shared__ TopkShared sh;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  // grid (KV head, request): no division by runtime values
+  // grid (selection row, request): no division by runtime values
   const int r = blockIdx.y;
-  const int row = r * Hkv + (int)blockIdx.x;
+  const int row = r * R + (int)blockIdx.x;
   const int log2p = __builtin_ctz(P);                 // the page size is a power of two
   const float *s = scores + (int64_t)row * max_pages;
   // Register rows: the whole score row is loaded in the same round trip as
@@ -410,13 +410,13 @@ hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        const int32_t *ctx_lens, const int32_t *budget_tokens,
                        int max_k, int n_sink, int n_recent, int32_t *sel_pages,
                        int32_t *num_sel, hipStream_t stream) {
-  dim3 grid((unsigned)dm.Hkv, (unsigned)batch);
+  dim3 grid((unsigned)dm.R, (unsigned)batch);        // one work-group per selection row
   if (dm.max_pages <= kRegKeys)
-    hipLaunchKernelGGL(topk_pages_kernel<true>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
+    hipLaunchKernelGGL(topk_pages_kernel<true>, grid, dim3(kTopkThreads), 0, stream, dm.R,
                        dm.P, dm.max_pages, max_k, n_sink, n_recent, scores, ctx_lens,
                        budget_tokens, sel_pages, num_sel);
   else
-    hipLaunchKernelGGL(topk_pages_kernel<false>, grid, dim3(kTopkThreads), 0, stream, dm.Hkv,
+    hipLaunchKernelGGL(topk_pages_kernel<false>, grid, dim3(kTopkThreads), 0, stream, dm.R,
                        dm.P, dm.max_pages, max_k, n_sink, n_recent, scores, ctx_lens,
                        budget_tokens, sel_pages, num_sel);
   return hipGetLastError();

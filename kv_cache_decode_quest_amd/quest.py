@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libquest.so")
 ABI_VERSION = 1
 QUEST_F32, QUEST_BF16 = 0, 1
 REDUCE = {"max": 0, "sum": 1}
+QUEST_SELECT_PER_KV_HEAD, QUEST_SELECT_PER_Q_HEAD = 0, 1
 
 # exported symbols declared in include/quest.h
 EXPORTS = ("quest_abi_version", "quest_status_string", "quest_append_kv", "quest_page_scores",
@@ -43,7 +44,7 @@ class QuestLayout(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("num_pool_pages", ctypes.c_int64),
         ("max_pages_per_seq", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("selection", ctypes.c_int32),
     ]
 
 
@@ -105,10 +106,18 @@ def _dtype_code(dtype) -> int:
 
 
 def make_layout(num_q_heads, num_kv_heads, head_dim, page_size, dtype, num_pool_pages,
-                max_pages_per_seq, abi_version=ABI_VERSION) -> QuestLayout:
+                max_pages_per_seq, abi_version=ABI_VERSION, per_q_head=False) -> QuestLayout:
+    """per_q_head: every q head selects its own pages (no GQA sharing)."""
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    sel = QUEST_SELECT_PER_Q_HEAD if per_q_head else QUEST_SELECT_PER_KV_HEAD
     return QuestLayout(abi_version, num_q_heads, num_kv_heads, head_dim, page_size, code,
-                       int(num_pool_pages), int(max_pages_per_seq), 0)
+                       int(num_pool_pages), int(max_pages_per_seq), sel)
+
+
+def selection_rows(L: QuestLayout) -> int:
+    """Rows of scores / selections per request: KV heads, or q heads when
+    every q head selects its own pages."""
+    return L.num_q_heads if L.selection == QUEST_SELECT_PER_Q_HEAD else L.num_kv_heads
 
 
 def _layout_dtype(L: QuestLayout):
@@ -180,7 +189,7 @@ def quest_page_scores(L: QuestLayout, q, kmeta, page_table, ctx_lens, scores, gr
     _check(kmeta, "kmeta", dt, _pool_shapes(L)[2], dev)
     _check(page_table, "page_table", torch.int32, (batch, L.max_pages_per_seq), dev)
     _check(ctx_lens, "ctx_lens", torch.int32, (batch,), dev)
-    _check(scores, "scores", torch.float32, (batch, L.num_kv_heads, L.max_pages_per_seq), dev)
+    _check(scores, "scores", torch.float32, (batch, selection_rows(L), L.max_pages_per_seq), dev)
     st = load().quest_page_scores(ctypes.byref(L), batch, _ptr(q), _ptr(kmeta), _ptr(page_table),
                                   _ptr(ctx_lens), REDUCE[group_reduce], _ptr(scores), _stream(dev))
     _raise("quest_page_scores", st)
@@ -203,7 +212,7 @@ def quest_append_score(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, max_
     _check(cu_new, "cu_new", torch.int32, (batch + 1,), dev)
     _check(ctx_before, "ctx_before", torch.int32, (batch,), dev)
     _check(page_table, "page_table", torch.int32, (batch, L.max_pages_per_seq), dev)
-    _check(scores, "scores", torch.float32, (batch, L.num_kv_heads, L.max_pages_per_seq), dev)
+    _check(scores, "scores", torch.float32, (batch, selection_rows(L), L.max_pages_per_seq), dev)
     if T == 0:                       # nothing to store: a plain scoring pass
         k_new = v_new = torch.empty((1, L.num_kv_heads, L.head_dim), dtype=dt, device=dev)
     st = load().quest_append_score(ctypes.byref(L), batch, _ptr(q), _ptr(k_new), _ptr(v_new),
@@ -229,11 +238,11 @@ def _topk(L, scores, ctx_lens, budget_tokens, max_k, sel_pages, num_sel, n_sink=
           n_recent=None):
     dev = scores.device
     batch = ctx_lens.shape[0]
-    _check(scores, "scores", torch.float32, (batch, L.num_kv_heads, L.max_pages_per_seq), dev)
+    _check(scores, "scores", torch.float32, (batch, selection_rows(L), L.max_pages_per_seq), dev)
     _check(ctx_lens, "ctx_lens", torch.int32, (batch,), dev)
     _check(budget_tokens, "budget_tokens", torch.int32, (batch,), dev)
-    _check(sel_pages, "sel_pages", torch.int32, (batch, L.num_kv_heads, max_k), dev)
-    _check(num_sel, "num_sel", torch.int32, (batch, L.num_kv_heads), dev)
+    _check(sel_pages, "sel_pages", torch.int32, (batch, selection_rows(L), max_k), dev)
+    _check(num_sel, "num_sel", torch.int32, (batch, selection_rows(L)), dev)
     if n_sink is None:
         st = load().quest_topk_pages(ctypes.byref(L), batch, _ptr(scores), _ptr(ctx_lens),
                                      _ptr(budget_tokens), int(max_k), _ptr(sel_pages),
@@ -270,8 +279,8 @@ def quest_sparse_decode(L: QuestLayout, q, k_cache, v_cache, page_table, ctx_len
     _check(v_cache, "v_cache", dt, vshape, dev)
     _check(page_table, "page_table", torch.int32, (batch, L.max_pages_per_seq), dev)
     _check(ctx_lens, "ctx_lens", torch.int32, (batch,), dev)
-    _check(sel_pages, "sel_pages", torch.int32, (batch, L.num_kv_heads, max_k), dev)
-    _check(num_sel, "num_sel", torch.int32, (batch, L.num_kv_heads), dev)
+    _check(sel_pages, "sel_pages", torch.int32, (batch, selection_rows(L), max_k), dev)
+    _check(num_sel, "num_sel", torch.int32, (batch, selection_rows(L)), dev)
     _check(out, "out", dt, (batch, L.num_q_heads, L.head_dim), dev)
     _check(workspace, "workspace", None, None, dev)
     nbytes = workspace.numel() * workspace.element_size()
@@ -297,10 +306,11 @@ def alloc_decode_buffers(L: QuestLayout, batch: int, max_k: int, device) -> Deco
     dt = _layout_dtype(L)
     ws = max(quest_sparse_decode_workspace_bytes(L, batch, max_k), 16)
     return DecodeBuffers(
-        scores=torch.empty((batch, L.num_kv_heads, L.max_pages_per_seq), dtype=torch.float32,
+        scores=torch.empty((batch, selection_rows(L), L.max_pages_per_seq), dtype=torch.float32,
                            device=device),
-        sel_pages=torch.empty((batch, L.num_kv_heads, max_k), dtype=torch.int32, device=device),
-        num_sel=torch.empty((batch, L.num_kv_heads), dtype=torch.int32, device=device),
+        sel_pages=torch.empty((batch, selection_rows(L), max_k), dtype=torch.int32,
+                              device=device),
+        num_sel=torch.empty((batch, selection_rows(L)), dtype=torch.int32, device=device),
         out=torch.empty((batch, L.num_q_heads, L.head_dim), dtype=dt, device=device),
         workspace=torch.empty((ws + 3) // 4, dtype=torch.float32, device=device),
         max_k=max_k)

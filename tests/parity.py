@@ -133,13 +133,14 @@ class Layer:
         return quest.alloc_decode_buffers(self.L, self.w.batch, max_k, self.device)
 
     # ----- oracle side -------------------------------------------------------
-    def oracle_request(self, q, r, reduce="max", sm_scale=None):
+    def oracle_request(self, q, r, reduce="max", sm_scale=None, per_q_head=False):
         sm = workloads.default_sm_scale(self.w) if sm_scale is None else sm_scale
         qr = np.ascontiguousarray(to_oracle(q[r]))
         ctx = int(self.ctx[r])
         budget = int(self.budgets()[r])
         return oracle.decode_request(self.shape, qr, self.host[0], self.host[1],
-                                     self.pt_host[r], ctx, budget, sm, reduce)
+                                     self.pt_host[r], ctx, budget, sm, reduce,
+                                     per_q_head=per_q_head)
 
 
 # ----- comparisons -----------------------------------------------------------

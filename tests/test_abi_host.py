@@ -50,9 +50,11 @@ def layout(**kw):
                 num_pool_pages=1000, max_pages_per_seq=100)
     base.update(kw)
     abi = base.pop("abi_version", 1)
-    return quest.make_layout(base["num_q_heads"], base["num_kv_heads"], base["head_dim"],
-                             base["page_size"], base["dtype"], base["num_pool_pages"],
-                             base["max_pages_per_seq"], abi_version=abi)
+    L = quest.make_layout(base["num_q_heads"], base["num_kv_heads"], base["head_dim"],
+                          base["page_size"], base["dtype"], base["num_pool_pages"],
+                          base["max_pages_per_seq"], abi_version=abi)
+    L.selection = base.get("selection", 0)
+    return L
 
 
 def scores_call(lib, L, batch=1, reduce=0, q=FAKE, kmeta=FAKE, out=FAKE):
@@ -77,6 +79,8 @@ def decode_call(lib, L, batch=1, max_k=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, sc
     (dict(page_size=64, dtype=0), ERR_UNSUPPORTED),
     (dict(dtype=7), ERR_UNSUPPORTED),
     (dict(num_q_heads=68), ERR_UNSUPPORTED),           # G = 17 > 16
+    (dict(selection=2), ERR_UNSUPPORTED),
+    (dict(selection=-1), ERR_UNSUPPORTED),
 ])
 def test_layout_rejections(lib, kw, want):
     L = layout(**kw)
@@ -157,6 +161,18 @@ def test_argument_rejections(lib):
     # bf16 vector loads need 16-byte alignment
     assert scores_call(lib, L, q=ctypes.c_void_p(0x100002)) == ERR_SHAPE
     assert decode_call(lib, L, q=ctypes.c_void_p(0x100008)) == ERR_SHAPE
+
+
+def test_per_q_head_rows(lib):
+    """Per-q-head selection: one selection row per q head, each a single head,
+    in the plan's rows and the workspace size."""
+    shared, per_head = layout(), layout(selection=1)
+    assert quest.selection_rows(shared) == 4 and quest.selection_rows(per_head) == 32
+    p = quest.quest_sparse_decode_plan(per_head, 8, 256)
+    need = lib.quest_sparse_decode_workspace_bytes(ctypes.byref(per_head), 8, 256)
+    assert need == 8 * 32 * p["num_splits"] * 1 * (128 + 2) * 4
+    q = quest.make_layout(32, 4, 128, 16, 1, 1000, 100, per_q_head=True)
+    assert q.selection == quest.QUEST_SELECT_PER_Q_HEAD
 
 
 def test_workspace_contract(lib):

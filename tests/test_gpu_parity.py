@@ -355,6 +355,47 @@ def test_forced_pages_decode(gpu_lib):
             check_out(out[r], ref["out"], torch.bfloat16, f"forced r{r}")
 
 
+@pytest.mark.parametrize("name,fused", [("layer32k_small", False), ("layer32k_small", True),
+                                        ("edges_d64_p32", True), ("f32_g1", False)])
+def test_per_q_head_selection(name, fused, gpu_lib):
+    """Every q head scores and selects its own pages (no GQA sharing):
+    per-head scores within the fp32 summation bound, per-head selections
+    exact, and outputs against the oracle's per-q-head decode."""
+    w = SMALL[name]
+    lay = Layer(w, DEV)
+    lay.L = quest.make_layout(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                              w.torch_dtype, lay.lay.num_pool_pages, lay.lay.max_pages,
+                              per_q_head=True)
+    q, k_new, v_new = lay.step_inputs(0)
+    bufs = lay.buffers(extra=1)
+    assert tuple(bufs.scores.shape[:2]) == (w.batch, w.num_q_heads)
+    if fused:
+        lay.append_score_step(q, k_new, v_new, bufs)
+    else:
+        lay.append_step(k_new, v_new)
+        lay.view(q, bufs)
+    lay.attend(q, bufs)
+    torch.cuda.synchronize()
+    scores = bufs.scores.cpu().numpy().astype(np.float64)
+    sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+    out = to_f64(bufs.out)
+    qh = to_f64(q)
+    G = w.num_q_heads // w.num_kv_heads
+    for r in range(w.batch):
+        ref = lay.oracle_request(q, r, per_q_head=True)
+        n = ref["scores"].shape[1]
+        if n:
+            mag = np.maximum(np.abs(ref["bounds"][:, :, 0, :]), np.abs(ref["bounds"][:, :, 1, :]))
+            kv_of = np.arange(w.num_q_heads) // G
+            tol = 2.0 * (w.head_dim + 2) * 2.0 ** -24 * np.einsum(
+                "hd,jhd->hj", np.abs(qh[r]), mag[:, kv_of, :]) + 1e-30
+            assert np.all(np.abs(scores[r, :, :n] - ref["scores"]) <= tol)
+        flags = [compare_selection(sel[r, h], int(nsel[r, h]), ref["sel"][h], ref["scores"][h])
+                 for h in range(w.num_q_heads)]
+        if "flagged" not in flags:
+            check_out(out[r], ref["out"], w.torch_dtype, f"{name} per-head r{r}")
+
+
 def test_topk_empty_request(gpu_lib):
     L = quest.make_layout(8, 1, 128, 16, torch.bfloat16, 1, 10)
     scores = torch.randn((2, 1, 10), device=DEV)
