@@ -91,8 +91,8 @@ typedef enum { QUEST_SELECT_PER_KV_HEAD = 0, QUEST_SELECT_PER_Q_HEAD = 1 } quest
 /* Shape of one attention layer's paged cache.
  *   num_q_heads (Hq) and num_kv_heads (Hkv): Hq % Hkv == 0, G = Hq/Hkv <= 16;
  *     q head h reads KV head h / G.
- *   head_dim (D): 64 or 128.   page_size (P): 16, 32 or 64 tokens (64 with
- *   fp32 only at D = 64).
+ *   head_dim (D): 64 or 128.   page_size (P): 8, 16, 32 or 64 tokens (64
+ *   with fp32 only at D = 64).
  *   dtype: quest_dtype of q, K, V, metadata and output.
  *   num_pool_pages: physical pages in the pool shared by all requests.
  *   max_pages_per_seq: row stride of the page table and of the score array.

@@ -203,7 +203,8 @@ hipError_t launch_append(const Dims &dm, int batch, const void *k_new,
                      dm.max_pages, (const uint16_t *)k_new, (const uint16_t *)v_new, cu_new,   \
                      ctx_before, page_table, (uint16_t *)k_cache, (uint16_t *)v_cache,        \
                      (uint16_t *)kmeta)
-    if (dm.P == 16) QUEST_APPEND_PAGES(16);
+    if (dm.P == 8) QUEST_APPEND_PAGES(8);
+    else if (dm.P == 16) QUEST_APPEND_PAGES(16);
     else if (dm.P == 32) QUEST_APPEND_PAGES(32);
     else QUEST_APPEND_PAGES(64);
 #undef QUEST_APPEND_PAGES

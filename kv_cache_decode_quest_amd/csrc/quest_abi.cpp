@@ -30,7 +30,7 @@ int check_layout(const quest_layout *L, Dims &dm) {
   if (L->num_q_heads % L->num_kv_heads != 0) return QUEST_ERR_SHAPE;
   if (L->dtype != QUEST_F32 && L->dtype != QUEST_BF16) return QUEST_ERR_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return QUEST_ERR_UNSUPPORTED;
-  if (L->page_size != 16 && L->page_size != 32 && L->page_size != 64)
+  if (L->page_size != 8 && L->page_size != 16 && L->page_size != 32 && L->page_size != 64)
     return QUEST_ERR_UNSUPPORTED;
   // fp32 pages of 64 tokens at D = 128 would need more than 64 KB of LDS in
   // the fp32 decode kernel's staging

@@ -44,8 +44,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Pages one wave loads at once (one round): 32 KB of K and V per wave in
 // flight at D = 128 (4 pages of 16 tokens, 2 of 32, 1 of 64), so the page
 // registers stay within budget.
+// 8-token pages go two to a 16-token tile (twice the pages of 16-token ones).
 __host__ __device__ constexpr int pages_per_wave(int P, int D) {
-  return (P * D <= 2048) ? 4 : (P * D <= 4096 ? 2 : 1);
+  return P < 16 ? 2 * pages_per_wave(16, D) : ((P * D <= 2048) ? 4 : (P * D <= 4096 ? 2 : 1));
 }
 // Pages folded into the running softmax per update.  The loads of a round
 // are issued group by group (K then V of each group), so a group's update
@@ -131,6 +132,28 @@ __device__ __forceinline__ void load_v(PageRegs<D, P> &pr, const uint16_t *__res
       pr.v[tt][nt] = *(const uint2 *)(vp + (nt * 16 + col) * P + tt * 16 + grp * 4);
 }
 
+// 8-token pages: a 16-token tile holds page a in tokens 0..7 and page b in
+// tokens 8..15.  K rows: lane (col, grp) takes token col of the tile; V: lane
+// (col, grp) takes tokens 4*grp .. +3, i.e. slots 4*(grp & 1) .. +3 of page a
+// (grp < 2) or b.
+template <int D>
+__device__ __forceinline__ void load_k_half(PageRegs<D, 16> &pr, const uint16_t *__restrict__ kpa,
+                                            const uint16_t *__restrict__ kpb, int col, int grp) {
+  const uint16_t *kp = (col < 8 ? kpa : kpb) + (col & 7) * D;
+#pragma unroll
+  for (int c = 0; c < PageRegs<D, 16>::KC; ++c)
+    pr.k[0][c] = *(const uint4 *)(kp + c * 32 + grp * 8);
+}
+
+template <int D>
+__device__ __forceinline__ void load_v_half(PageRegs<D, 16> &pr, const uint16_t *__restrict__ vpa,
+                                            const uint16_t *__restrict__ vpb, int col, int grp) {
+  const uint16_t *vp = (grp < 2 ? vpa : vpb) + (grp & 1) * 4;
+#pragma unroll
+  for (int nt = 0; nt < PageRegs<D, 16>::NT; ++nt)
+    pr.v[0][nt] = *(const uint2 *)(vp + (nt * 16 + col) * 8);
+}
+
 // One round of the online softmax over the NPG pages a wave holds, for all
 // heads of the group at once: the logits of every page on the matrix cores,
 // one running-max / running-sum update for the whole round, then
@@ -144,10 +167,14 @@ __device__ __forceinline__ void load_v(PageRegs<D, P> &pr, const uint16_t *__res
 // row shift) and feeds that head's lo weights to the second product while
 // lane col - 8 feeds the hi weights: one matrix-core step per tile instead of
 // two, and accumulator columns h and h + 8 add up to head h.
+//
+// Validity: token tt*16 + tok0 + e of the lane takes part iff it is below
+// lim[u]; full[u] (uniform) says every token of tile-page u does.
 template <int D, int P, int NPG, bool kPack>
-__device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *valid,
-                                             const bf16x8 *qop, float scale2, int col, int grp,
-                                             float &m, float &l, f32x4 *acc) {
+__device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
+                                             const bool *full, int tok0, const bf16x8 *qop,
+                                             float scale2, int col, int grp, float &m, float &l,
+                                             f32x4 *acc) {
   using PR = PageRegs<D, P>;
   constexpr float kNegInf = -__builtin_huge_valf();
   // logits: lane holds head `col` (kPack: head col mod 8), tokens tt*16 + 4*grp + e
@@ -169,13 +196,13 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *vali
         for (int e = 0; e < 4; ++e)
           c4[e] = __uint_as_float(dpp_row<kRowShr8>(__float_as_uint(c4[e]), __float_as_uint(c4[e])));
       }
-      if (valid[u] >= P) {                 // a full page (uniform branch)
+      if (full[u]) {                        // a full page (uniform branch)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[u][tt][e] = c4[e] * scale2;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s[u][tt][e] = tt * 16 + 4 * grp + e < valid[u] ? c4[e] * scale2 : kNegInf;
+          s[u][tt][e] = tt * 16 + tok0 + e < lim[u] ? c4[e] * scale2 : kNegInf;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) pmax = fmaxf(pmax, s[u][tt][e]);
@@ -220,14 +247,14 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *vali
     // The slots of a partial page past its valid tokens may hold anything
     // (NaN included): zero their V values, since a zero weight times NaN is
     // still NaN.
-    if (valid[u] < P) {
+    if (!full[u]) {
 #pragma unroll
       for (int tt = 0; tt < PR::TT; ++tt) {
-        const int t0 = tt * 16 + 4 * grp;
-        const uint32_t mx = (t0 + 0 < valid[u] ? 0x0000ffffu : 0u) |
-                            (t0 + 1 < valid[u] ? 0xffff0000u : 0u);
-        const uint32_t my = (t0 + 2 < valid[u] ? 0x0000ffffu : 0u) |
-                            (t0 + 3 < valid[u] ? 0xffff0000u : 0u);
+        const int t0 = tt * 16 + tok0;
+        const uint32_t mx = (t0 + 0 < lim[u] ? 0x0000ffffu : 0u) |
+                            (t0 + 1 < lim[u] ? 0xffff0000u : 0u);
+        const uint32_t my = (t0 + 2 < lim[u] ? 0x0000ffffu : 0u) |
+                            (t0 + 3 < lim[u] ? 0xffff0000u : 0u);
 #pragma unroll
         for (int nt = 0; nt < PR::NT; ++nt) {
           pg[u].v[tt][nt].x &= mx;
@@ -259,8 +286,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
     const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
-  using PR = PageRegs<D, P>;
+  // 8-token pages are attended two to a 16-token tile ("tile page")
+  constexpr bool kHalf = P < 16;
+  constexpr int TP = kHalf ? 16 : P;
+  constexpr int SUB = kHalf ? 2 : 1;    // pages per tile page
+  using PR = PageRegs<D, TP>;
   constexpr int PPW = pages_per_wave(P, D);
+  constexpr int NV = PPW / SUB;         // tile pages per wave and round
   constexpr int kLdsRow = D + 4;       // padded so the 16-byte stores below spread over banks
   __shared__ float lds_m[kDecodeWaves][16];
   __shared__ float lds_l[kDecodeWaves][16];
@@ -343,22 +375,44 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
       valid[u] = (live && ok) ? min(P, ctx - j * P) : 0;
     }
     // per update group: all K, then all V (the logits need only the K loads)
-    constexpr int UPG = kPagesPerUpdate < PPW ? kPagesPerUpdate : PPW;
-    PR pg[PPW];
+    constexpr int UPG = kPagesPerUpdate < NV ? kPagesPerUpdate : NV;
+    PR pg[NV];
+    auto kbase = [&](int u) { return k_cache + (phys[u] * Hkv + g) * page_elems; };
+    auto vbase = [&](int u) { return v_cache + (phys[u] * Hkv + g) * page_elems; };
 #pragma unroll
-    for (int g0 = 0; g0 < PPW; g0 += UPG) {
+    for (int g0 = 0; g0 < NV; g0 += UPG) {
 #pragma unroll
-      for (int u = g0; u < g0 + UPG; ++u)
-        load_k<D, P>(pg[u], k_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+      for (int v = g0; v < g0 + UPG; ++v) {
+        if constexpr (kHalf) load_k_half<D>(pg[v], kbase(2 * v), kbase(2 * v + 1), col, grp);
+        else load_k<D, TP>(pg[v], kbase(v), col, grp);
+      }
 #pragma unroll
-      for (int u = g0; u < g0 + UPG; ++u)
-        load_v<D, P>(pg[u], v_cache + (phys[u] * Hkv + g) * page_elems, col, grp);
+      for (int v = g0; v < g0 + UPG; ++v) {
+        if constexpr (kHalf) load_v_half<D>(pg[v], vbase(2 * v), vbase(2 * v + 1), col, grp);
+        else load_v<D, TP>(pg[v], vbase(v), col, grp);
+      }
     }
     // keep every load of the round ahead of the first wait on any of them
     __builtin_amdgcn_sched_barrier(0);
+    // validity per tile page: this lane's tokens 4*grp .. +3 lie in page
+    // 2v + (grp >> 1) of a half tile, as slots 4*(grp & 1) .. +3
+    int lim[NV];
+    bool full[NV];
 #pragma unroll
-    for (int g0 = 0; g0 < PPW; g0 += UPG)
-      attend_round<D, P, UPG, kPack>(pg + g0, valid + g0, qop, scale2, col, grp, m, l, acc);
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (kHalf) {
+        lim[v] = grp < 2 ? valid[2 * v] : valid[2 * v + 1];
+        full[v] = valid[2 * v] >= P && valid[2 * v + 1] >= P;
+      } else {
+        lim[v] = valid[v];
+        full[v] = valid[v] >= P;
+      }
+    }
+    const int tok0 = kHalf ? 4 * (grp & 1) : 4 * grp;
+#pragma unroll
+    for (int g0 = 0; g0 < NV; g0 += UPG)
+      attend_round<D, TP, UPG, kPack>(pg + g0, lim + g0, full + g0, tok0, qop, scale2, col, grp,
+                                      m, l, acc);
   }
 
   // merge the waves of this work-group
@@ -590,6 +644,8 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
     if (dm.D == 128 && dm.P == 16) QUEST_DECODE(128, 16);
     else if (dm.D == 128 && dm.P == 32) QUEST_DECODE(128, 32);
     else if (dm.D == 128 && dm.P == 64) QUEST_DECODE(128, 64);
+    else if (dm.D == 128 && dm.P == 8) QUEST_DECODE(128, 8);
+    else if (dm.D == 64 && dm.P == 8) QUEST_DECODE(64, 8);
     else if (dm.D == 64 && dm.P == 16) QUEST_DECODE(64, 16);
     else if (dm.D == 64 && dm.P == 32) QUEST_DECODE(64, 32);
     else QUEST_DECODE(64, 64);

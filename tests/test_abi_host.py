@@ -74,7 +74,7 @@ def decode_call(lib, L, batch=1, max_k=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, sc
     (dict(num_pool_pages=0), ERR_SHAPE),
     (dict(max_pages_per_seq=0), ERR_SHAPE),
     (dict(head_dim=96), ERR_UNSUPPORTED),
-    (dict(page_size=8), ERR_UNSUPPORTED),
+    (dict(page_size=12), ERR_UNSUPPORTED),
     (dict(page_size=128), ERR_UNSUPPORTED),
     (dict(page_size=64, dtype=0), ERR_UNSUPPORTED),
     (dict(dtype=7), ERR_UNSUPPORTED),
@@ -192,7 +192,7 @@ def test_plan_covers_every_page():
     splits a plan may use."""
     for batch, hkv, max_k in [(1, 1, 1), (1, 1, 16), (8, 4, 256), (8, 4, 128), (32, 4, 409),
                               (64, 4, 128), (3, 2, 1000), (1, 1, 60000), (2, 4, 4097)]:
-        for page_size in (16, 32, 64):
+        for page_size in (8, 16, 32, 64):
             L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8, page_size=page_size)
             p = quest.quest_sparse_decode_plan(L, batch, max_k)
             assert p["pages_per_split"] >= 1

@@ -50,6 +50,15 @@ SMALL = {
                                    seed=82, poison=float("nan"), permute_pages=True),
     "p64_d64_f32": workloads.Workload("p64_d64_f32", 2, 8, 2, 64, 64, "f32", ctx=2100,
                                       budget_tokens=500, steps=2, seed=83),
+    # 8-token pages (two to a 16-token matrix-core tile in the decode); odd
+    # page budgets leave the second half of a tile empty
+    "p8_d128": workloads.Workload("p8_d128", 4, 32, 4, 128, 8, "bf16",
+                                  ctx_list=(1, 9, 1001, 5003), budget_tokens=200, steps=2,
+                                  seed=84, poison=float("nan"), permute_pages=True),
+    "p8_d64": workloads.Workload("p8_d64", 3, 12, 4, 64, 8, "bf16", ctx_list=(7, 800, 3000),
+                                 budget_tokens=88, steps=2, seed=85),
+    "p8_f32": workloads.Workload("p8_f32", 2, 8, 2, 128, 8, "f32", ctx=700, budget_tokens=136,
+                                 steps=2, seed=86),
 }
 
 
@@ -160,7 +169,7 @@ def test_incremental_append_equals_bulk(gpu_lib):
         assert torch.equal(km[phys].view(torch.int16), bulk.kmeta[phys].view(torch.int16))
 
 
-@pytest.mark.parametrize("page_size", [16, 32, 64])
+@pytest.mark.parametrize("page_size", [8, 16, 32, 64])
 def test_unaligned_and_chunked_append_match(page_size, gpu_lib):
     """The same tokens stored three ways give identical pools and metadata:
     one bulk append (16-byte vector path), chunks of 37 tokens that start and
@@ -258,7 +267,7 @@ def _topk_rows(n_max, gen):
 
 
 @pytest.mark.parametrize("n_max,P", [(64, 16), (300, 16), (2050, 32), (8008, 16), (10000, 16),
-                                     (500, 64)])
+                                     (500, 64), (900, 8)])
 def test_topk_exact(n_max, P, gpu_lib):
     gen = torch.Generator().manual_seed(5000 + n_max)
     rows = _topk_rows(n_max, gen)
