@@ -419,7 +419,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the Quest decode path here is built and timed "
-              "on a single MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
+              "on a single MI355X (requests and KV heads are independent, so it would shard "
+              "by request or by KV head with no exchange); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

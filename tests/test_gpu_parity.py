@@ -110,9 +110,9 @@ def run_and_check(w, layer=0, reduce="max", fused=False):
                 check_scores(scores[r], ref["scores"], qh[r], ref["bounds"], w.group)
             row_flag = False
             for g in range(w.num_kv_heads):
-                verdict = compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g],
+                outcome = compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g],
                                             ref["scores"][g])
-                row_flag |= verdict == "flagged"
+                row_flag |= outcome == "flagged"
             check_out(out2[r], ref["out"], w.torch_dtype, f"{w.name} r{r} (oracle selection)")
             if row_flag:
                 flagged += 1
