@@ -137,6 +137,55 @@ def dense_reference(layer, inputs, ctx_b, ctx_a, sm, evict, n_steps, dev):
             "plan": plan}
 
 
+def per_q_head_reference(layer, inputs, ctx_b, ctx_a, budgets, sm, evict, n_steps, dev):
+    """The same decode step with per-q-head selection (every q head scores,
+    selects and attends its own pages; no sharing across the GQA group),
+    timed like the sparse step.  Bytes = metadata + each q head's selected
+    valid K/V."""
+    w = layer.w
+    B, Hq, P = w.batch, w.num_q_heads, w.page_size
+    L = quest.make_layout(Hq, w.num_kv_heads, w.head_dim, P, w.torch_dtype,
+                          layer.lay.num_pool_pages, layer.lay.max_pages, per_q_head=True)
+    max_k = max(1, max(int((b // P).max()) for b in budgets[:n_steps]))
+    bufs = quest.alloc_decode_buffers(L, B, max_k, dev)
+    sels = torch.empty((n_steps,) + tuple(bufs.sel_pages.shape), dtype=torch.int32, device=dev)
+    nsels = torch.empty((n_steps,) + tuple(bufs.num_sel.shape), dtype=torch.int32, device=dev)
+
+    def step(s):
+        q, k_new, v_new = inputs[s]
+        quest.quest_append_score(L, q, k_new, v_new, layer.cu1, ctx_b[s], 1, layer.pt,
+                                 layer.k_cache, layer.v_cache, layer.kmeta, bufs.scores)
+        quest.quest_topk_pages(L, bufs.scores, ctx_a[s], budgets[s], max_k, bufs.sel_pages,
+                               bufs.num_sel)
+        quest.quest_sparse_decode(L, q, layer.k_cache, layer.v_cache, layer.pt, ctx_a[s],
+                                  bufs.sel_pages, bufs.num_sel, max_k, sm, bufs.out,
+                                  bufs.workspace)
+
+    step(0)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for s in range(n_steps):
+        evict()
+        ev[s][0].record()
+        step(s)
+        ev[s][1].record()
+        sels[s].copy_(bufs.sel_pages)
+        nsels[s].copy_(bufs.num_sel)
+    torch.cuda.synchronize()
+    total_s = sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3
+    meta_b = kv_b = 0
+    for s in range(n_steps):
+        m, kv = step_bytes(w, ctx_a[s], sels[s], nsels[s])
+        meta_b += m
+        kv_b += kv
+    return {"what": "the same step with every q head scoring, selecting and attending its "
+                    "own pages (no sharing across the GQA group); cache evicted before each step",
+            "tokens_per_s": B * n_steps / total_s, "ms_per_step": total_s / n_steps * 1e3,
+            "steps": n_steps, "selected_kv_bytes_per_step": kv_b / n_steps,
+            "hbm_gbps": (meta_b + kv_b) / total_s / 1e9,
+            "hbm_frac_peak": (meta_b + kv_b) / total_s / 1e9 / PEAK_HBM_GBPS}
+
+
 def prefill_chunk_append(layer, chunk, n_calls, evict, dev):
     """Bulk on_kv_stored at prefill-chunk granularity: each call stores one
     `chunk`-token chunk of every request's prompt (positions c*chunk ..) with
@@ -399,6 +448,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense decode reference (every page, no selection)")
     ap.add_argument("--dense-steps", type=int, default=16)
+    ap.add_argument("--no-per-head", action="store_true",
+                    help="skip the per-q-head selection reference")
     ap.add_argument("--prefill-chunk", type=int, default=4096,
                     help="chunk size of the prefill append leg (0 to skip)")
     ap.add_argument("--roofline-copies", type=int, default=8)
@@ -577,6 +628,14 @@ def main():
         dense["sparse_speedup"] = value / dense["tokens_per_s"]
         restore()
 
+    per_head = None
+    if not args.no_per_head:
+        log(f"per-q-head selection: {min(args.dense_steps, K)} steps")
+        per_head = per_q_head_reference(layer, inputs, ctx_b, ctx_a, budgets, sm, evict,
+                                        max(1, min(args.dense_steps, K)), dev)
+        per_head["shared_speedup"] = value / per_head["tokens_per_s"]
+        restore()
+
     prefill = None
     if args.prefill_chunk > 0:
         log(f"prefill append: {args.prefill_chunk}-token chunks")
@@ -625,6 +684,7 @@ def main():
         "wall_s_timed_loop_incl_flush": t_wall,
         "warm": warm,
         "dense_reference": dense,
+        "per_q_head_reference": per_head,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
         "host": platform.node(),
