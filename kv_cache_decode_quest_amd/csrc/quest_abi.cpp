@@ -40,6 +40,10 @@ int check_layout(const quest_layout *L, Dims &dm) {
   if (G > 16) return QUEST_ERR_UNSUPPORTED;
   // keep per-request token counts inside int32 arithmetic
   if ((int64_t)L->max_pages_per_seq * L->page_size > INT32_MAX) return QUEST_ERR_SHAPE;
+  // the scoring grid (64 pages x one KV head per 256-thread work-group) stays
+  // under 2^32 work-items per dimension
+  if ((int64_t)L->max_pages_per_seq * L->num_kv_heads >= ((int64_t)1 << 30))
+    return QUEST_ERR_SHAPE;
   if (L->selection != QUEST_SELECT_PER_KV_HEAD && L->selection != QUEST_SELECT_PER_Q_HEAD)
     return QUEST_ERR_UNSUPPORTED;
   dm.Hq = L->num_q_heads;
@@ -62,9 +66,13 @@ int check_layout(const quest_layout *L, Dims &dm) {
   return QUEST_OK;
 }
 
+// batch <= 65535 (grid y of the scoring, top-k and append kernels) and
+// batch * Hq <= 2^22, which keeps the decode (at most about max(rows, 1024)
+// work-groups of 512 threads) and merge (batch * Hq work-groups of 128)
+// grids under 2^32 work-items.
 int check_batch(int32_t batch, const Dims &dm) {
   if (batch < 0 || batch > 65535) return QUEST_ERR_SHAPE;
-  if ((int64_t)batch * dm.Hq > INT32_MAX / 16) return QUEST_ERR_SHAPE;
+  if ((int64_t)batch * dm.Hq > ((int64_t)1 << 22)) return QUEST_ERR_SHAPE;
   return QUEST_OK;
 }
 

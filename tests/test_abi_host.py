@@ -129,6 +129,12 @@ def test_batch_bounds_and_empty_batch(lib):
     L = layout()
     assert scores_call(lib, L, batch=-1) == ERR_SHAPE
     assert scores_call(lib, L, batch=70000) == ERR_SHAPE
+    # batch * Hq <= 2^22 keeps the decode and merge grids within 2^32 work-items
+    wide = layout(num_q_heads=1024, num_kv_heads=64)
+    assert decode_call(lib, wide, batch=4097) == ERR_SHAPE
+    assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(wide), 4097, 8) == 0
+    # max_pages_per_seq * Hkv < 2^30 keeps the scoring grid within 2^32 work-items
+    assert scores_call(lib, layout(max_pages_per_seq=1 << 28, num_pool_pages=1 << 28)) == ERR_SHAPE
     # batch 0: nothing to do, no pointer needed, nothing launched
     assert lib.quest_page_scores(ctypes.byref(L), 0, None, None, None, None, 0, None, None) == OK
     assert lib.quest_topk_pages(ctypes.byref(L), 0, None, None, None, 4, None, None, None) == OK
