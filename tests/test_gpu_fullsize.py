@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the ragged and 48-layer workloads, checked
+"""GPU parity at the full sizes of the one-layer 32k, ragged and 48-layer workloads, checked
 on sampled requests against the oracle (the benchmark shape itself is
 covered by test_full_bench_shape_sampled), dense decode over every page at
 the benchmark shape, plus hipGraph capture/replay of a decode step."""
@@ -37,6 +37,21 @@ def check_requests(lay, q, bufs, requests):
         else:
             check_out(out[r], ref["out"], lay.w.torch_dtype, f"{lay.w.name} r{r}")
     return flagged
+
+
+def test_full_layer32k_sampled(gpu_lib):
+    """The one-layer Qwen3-30B-A3B-like configuration at full size: batch 8 x
+    32768 tokens, budget 2048, one decode step through the fused append +
+    scores path; requests 0, 3 and 7 against the oracle."""
+    w = WORKLOADS["layer32k"]
+    sample = [0, 3, 7]
+    lay = Layer(w, DEV, host_requests=sample)
+    q, k_new, v_new = lay.step_inputs(0)
+    bufs = lay.buffers(extra=1)
+    lay.append_score_step(q, k_new, v_new, bufs)
+    lay.attend(q, bufs)
+    flagged = check_requests(lay, q, bufs, sample)
+    log(f"layer32k: ok, flagged {flagged}")
 
 
 def test_full_ragged_sampled(gpu_lib):
