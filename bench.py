@@ -8,20 +8,24 @@ and min/max refresh fused with the page scores), quest_topk_pages and
 quest_sparse_decode (split-K attention + merge).  Inputs are seeded synthetic
 tensors already resident in HBM.
 
-Timing: W warm-up steps, then K timed steps.  Before each timed step an
-untimed read of a 2 GiB scratch buffer evicts the 256 MB Infinity Cache, so
-the metadata and KV are read from HBM as they would be between layers (a read
-sweep, like the other layers' KV reads, leaves no dirty lines whose write-back
-would compete with the step); a HIP event pair on the library's stream
-brackets each step.  value =
-batch * K / (sum of step times).  A warm number (back-to-back steps, no
-eviction) is reported separately and labelled as cache-assisted.
+Timing: the layer's cache is resident in several copies (own K/V pools and
+metadata per copy, one shared page table, as a model's layers share one block
+table), and the K timed steps rotate over the copies, so a step's metadata
+and KV were last touched several layers earlier and are read from HBM, not
+from the 256 MB Infinity Cache.  The steps run back to back from one
+captured HIP graph (decode steps are replayed from graphs in serving), after
+W eager warm-up steps, one eager pass over the sequence and one untimed
+replay; a HIP event pair brackets the timed replay.  value = batch * K /
+replay time.  Also reported: the same steps launched eagerly one at a time,
+the cache evicted before each by an untimed 2 GiB read sweep (each step then
+pays its own dispatch latency).
 
 Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -46,6 +50,16 @@ def log(msg):
 
 class BenchLayer:
     """The layer's caller-owned buffers (the cache-manager role)."""
+
+    def resident_copy(self):
+        """Another layer of the same shape and contents: its own K/V pools and
+        metadata, the same page table and context lengths."""
+        c = object.__new__(BenchLayer)
+        c.__dict__.update(self.__dict__)
+        c.k_cache, c.v_cache = self.k_cache.clone(), self.v_cache.clone()
+        c.kmeta = self.kmeta.clone()
+        c.prefill = None
+        return c
 
     def __init__(self, w: workloads.Workload, capacity: int, device):
         self.w, self.device = w, device
@@ -235,64 +249,6 @@ def prefill_chunk_append(layer, chunk, n_calls, evict, dev):
             "hbm_gbps": nbytes / total_s / 1e9, "hbm_frac_peak": nbytes / total_s / 1e9 / PEAK_HBM_GBPS}
 
 
-class Stepper:
-    """Issues decode steps for the whole batch, split by request into
-    contiguous chunks, one chunk per HIP stream (default priority).  Chunks
-    are independent requests, so the latency-bound kernels of one chunk
-    (append, top-k, merge) overlap the HBM-bound kernels of another."""
-
-    def __init__(self, layer, max_k, n_streams, dev):
-        B = layer.w.batch
-        n_streams = max(1, min(n_streams, B))
-        edges = [round(i * B / n_streams) for i in range(n_streams + 1)]
-        self.chunks = [(edges[i], edges[i + 1]) for i in range(n_streams)]
-        self.layer = layer
-        self.streams = [None] + [torch.cuda.Stream(device=dev) for _ in range(n_streams - 1)]
-        self.bufs = [quest.alloc_decode_buffers(layer.L, r1 - r0, max_k, dev)
-                     for r0, r1 in self.chunks]
-        self.cu1 = [torch.arange(r1 - r0 + 1, dtype=torch.int32, device=dev)
-                    for r0, r1 in self.chunks]
-        self.start = torch.cuda.Event()
-        self.done = [torch.cuda.Event() for _ in self.chunks]
-        self.max_k = max_k
-
-    def _chunk(self, c, inp, ctx_before, ctx_after, budgets, sm):
-        r0, r1 = self.chunks[c]
-        lay, L, b = self.layer, self.layer.L, self.bufs[c]
-        q, k_new, v_new = (x[r0:r1] for x in inp)
-        pt = lay.pt[r0:r1]
-        ca, cb, bud = ctx_after[r0:r1], ctx_before[r0:r1], budgets[r0:r1]
-        quest.quest_append_score(L, q, k_new, v_new, self.cu1[c], cb, 1, pt, lay.k_cache,
-                                 lay.v_cache, lay.kmeta, b.scores)
-        quest.quest_topk_pages(L, b.scores, ca, bud, b.max_k, b.sel_pages, b.num_sel)
-        quest.quest_sparse_decode(L, q, lay.k_cache, lay.v_cache, pt, ca, b.sel_pages,
-                                  b.num_sel, b.max_k, sm, b.out, b.workspace)
-
-    def step(self, inp, ctx_before, ctx_after, budgets, sm):
-        if len(self.chunks) == 1:
-            self._chunk(0, inp, ctx_before, ctx_after, budgets, sm)
-            return
-        main = torch.cuda.current_stream()
-        self.start.record(main)
-        for c in range(len(self.chunks)):
-            st = main if c == 0 else self.streams[c]
-            if c > 0:
-                st.wait_event(self.start)
-            with torch.cuda.stream(st):
-                self._chunk(c, inp, ctx_before, ctx_after, budgets, sm)
-            if c > 0:
-                self.done[c].record(st)
-        for c in range(1, len(self.chunks)):
-            main.wait_event(self.done[c])
-
-    def record_selection(self, sels, nsels):
-        """Copy the last step's selections into full-batch tensors (main stream,
-        after step() has joined the chunk streams)."""
-        for (r0, r1), b in zip(self.chunks, self.bufs):
-            sels[r0:r1].copy_(b.sel_pages)
-            nsels[r0:r1].copy_(b.num_sel)
-
-
 def step_bytes(w, ctx_after, sel, nsel):
     """Algorithmic HBM bytes of one step: every live page's metadata row plus
     the valid tokens of every selected page (K and V)."""
@@ -444,7 +400,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=24)
-    ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--resident-layers", type=int, default=8,
+                    help="copies of the layer the timed steps rotate over")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense decode reference (every page, no selection)")
     ap.add_argument("--dense-steps", type=int, default=16)
@@ -453,8 +410,6 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=4096,
                     help="chunk size of the prefill append leg (0 to skip)")
     ap.add_argument("--roofline-copies", type=int, default=8)
-    ap.add_argument("--streams", type=int, default=1,
-                    help="split the batch by request over this many HIP streams")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain copy of this size (counter calibration)")
     ap.add_argument("--traffic-from-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
@@ -514,43 +469,75 @@ def main():
     touched = torch.tensor(sorted(set(touched)), dtype=torch.int64, device=dev)
     saved = layer.kmeta[touched].clone()
 
-    stepper = Stepper(layer, max_k, args.streams, dev)
-    log(f"warm-up: {W} steps ({len(stepper.chunks)} stream(s))")
-    for s in range(W):
-        stepper.step(inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
-    torch.cuda.synchronize()
-    layer.kmeta[touched] = saved
-    torch.cuda.synchronize()
-
     def restore():
         layer.kmeta[touched] = saved
 
-    # 1. the timed steps: one event pair per step, the cache evicted before each
-    log(f"timed: {K} steps")
-    ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    # 1. the timed steps: step s runs on copy s % NL at decode position s // NL
+    NL = max(1, args.resident_layers)
+    log(f"resident copies of the layer: {NL}")
+    layers = [layer] + [layer.resident_copy() for _ in range(NL - 1)]
     sels = torch.empty((K,) + tuple(bufs.sel_pages.shape), dtype=torch.int32, device=dev)
     nsels = torch.empty((K,) + tuple(bufs.num_sel.shape), dtype=torch.int32, device=dev)
+    per_copy = [quest.alloc_decode_buffers(layer.L, w.batch, max_k, dev) for _ in range(NL)]
+    step_bufs = [dataclasses.replace(per_copy[s % NL], sel_pages=sels[s], num_sel=nsels[s])
+                 for s in range(K)]
+
+    def rot_step(s):
+        m = s // NL
+        run_step(layers[s % NL], step_bufs[s], s, inputs[s], ctx_b[m], ctx_a[m], budgets[m], sm)
+
+    log(f"warm-up: {W} steps, then one eager pass over the {K} steps")
+    for s in range(W):
+        rot_step(s % K)
+    for s in range(K):
+        rot_step(s)
+    torch.cuda.synchronize()
+    eager_sel, eager_nsel = sels.clone(), nsels.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(K):
+            rot_step(s)
+    graph.replay()
+    torch.cuda.synchronize()
+    same = [torch.equal(sels, eager_sel) and torch.equal(nsels, eager_nsel)]
+    log(f"timed: {K} steps replayed")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    evict()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    for s in range(K):
-        evict()
-        ev_step[s][0].record()
-        stepper.step(inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
-        ev_step[s][1].record()
-        stepper.record_selection(sels[s], nsels[s])
+    ev[0].record()
+    graph.replay()
+    ev[1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    step_ms = [e[0].elapsed_time(e[1]) for e in ev_step]
-    total_s = sum(step_ms) / 1e3
+    total_s = ev[0].elapsed_time(ev[1]) / 1e3
+    same.append(torch.equal(sels, eager_sel) and torch.equal(nsels, eager_nsel))
     value = w.batch * K / total_s
 
     meta_b, kv_b = 0, 0
     for s in range(K):
-        m, kv = step_bytes(w, ctx_a[s], sels[s], nsels[s])
+        m, kv = step_bytes(w, ctx_a[s // NL], sels[s], nsels[s])
         meta_b += m
         kv_b += kv
     gbps = (meta_b + kv_b) / total_s / 1e9
+    del graph, step_bufs, per_copy, layers
+    torch.cuda.empty_cache()
 
+    # 1b. the same steps on one copy, launched eagerly one at a time, the
+    #     cache evicted before each (one event pair per step)
+    restore()
+    torch.cuda.synchronize()
+    ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for s in range(K):
+        evict()
+        ev_step[s][0].record()
+        run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+        ev_step[s][1].record()
+    torch.cuda.synchronize()
+    eager_ms = sum(e[0].elapsed_time(e[1]) for e in ev_step) / K
+    eager = {"tokens_per_s": w.batch / (eager_ms / 1e3), "ms_per_step": eager_ms,
+             "note": "one copy of the layer, steps launched one at a time from Python, "
+                     "a 2 GiB read sweep before each step, one event pair per step"}
     # 2. per-kernel breakdown: the same steps again, an event between kernels
     #    (each event adds a few microseconds of dispatch gap to its interval)
     restore()
@@ -604,28 +591,13 @@ def main():
         del src, dst
     del copies
 
-    warm = None
-    if not args.no_warm:
-        # the same steps back to back without evicting the cache
-        restore()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for s in range(K):
-            stepper.step(inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
-        ev[1].record()
-        torch.cuda.synchronize()
-        warm_s = ev[0].elapsed_time(ev[1]) / 1e3
-        warm = {"tokens_per_s": w.batch * K / warm_s, "ms_per_step": warm_s / K * 1e3,
-                "note": "back-to-back steps without cache eviction: part of the metadata "
-                        "is served from the Infinity Cache"}
-
     dense = None
     if not args.no_dense:
         log(f"dense reference: {min(args.dense_steps, K)} steps over every page")
         dense = dense_reference(layer, inputs, ctx_b, ctx_a, sm, evict,
                                 max(1, min(args.dense_steps, K)), dev)
-        dense["sparse_speedup"] = value / dense["tokens_per_s"]
+        # both timed the same way: eager launches, cache evicted before each step
+        dense["sparse_speedup"] = eager["tokens_per_s"] / dense["tokens_per_s"]
         restore()
 
     per_head = None
@@ -633,7 +605,7 @@ def main():
         log(f"per-q-head selection: {min(args.dense_steps, K)} steps")
         per_head = per_q_head_reference(layer, inputs, ctx_b, ctx_a, budgets, sm, evict,
                                         max(1, min(args.dense_steps, K)), dev)
-        per_head["shared_speedup"] = value / per_head["tokens_per_s"]
+        per_head["shared_speedup"] = eager["tokens_per_s"] / per_head["tokens_per_s"]
         restore()
 
     prefill = None
@@ -654,7 +626,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": sum(step_ms) / K,
+        "ms_per_step": total_s / K * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -679,10 +651,10 @@ def main():
                      "metadata_copies": R},
         "kernels_us_event_bracketed": {k: sum(v) / K * 1e3 for k, v in phase_ms.items()},
         "decode_kernel": {"achieved_gbps": decode_gbps, "plan": plan},
-        "launch": {"streams": len(stepper.chunks),
-                   "requests_per_stream": [r1 - r0 for r0, r1 in stepper.chunks]},
-        "wall_s_timed_loop_incl_flush": t_wall,
-        "warm": warm,
+        "launch": {"hip_graph": True, "resident_layer_copies": NL,
+                   "steps_per_replay": K, "selections_equal_eager": all(same)},
+        "wall_s_timed_replay": t_wall,
+        "eager_evicted": eager,
         "dense_reference": dense,
         "per_q_head_reference": per_head,
         "prefill_append": prefill,
