@@ -4,8 +4,9 @@ Workload (default "bench128k"): one Qwen3-30B-A3B-class attention layer
 (32 q / 4 KV heads, head_dim 128, bf16), batch 8, 128000-token contexts in a
 paged cache (page 16), token budget 4096 (256 pages per KV head).  A step is
 the whole hot path for one new token per request: quest_append_score (KV store
-and min/max refresh fused with the page scores), quest_topk_pages and
-quest_sparse_decode (split-K attention + merge).  Inputs are seeded synthetic
+and min/max refresh fused with the page scores) and quest_topk_sparse_decode
+(the top-k selection and the split-K attention in one kernel at this shape,
+then the merge).  Inputs are seeded synthetic
 tensors already resident in HBM.
 
 Timing: the layer's cache is resident in several copies (own K/V pools and
@@ -97,16 +98,11 @@ def run_step(layer, bufs, s, inp, ctx_before, ctx_after, budgets, sm, events=Non
                              layer.k_cache, layer.v_cache, layer.kmeta, bufs.scores)
     if events:
         events[1].record()
+    quest.quest_topk_sparse_decode(L, q, layer.k_cache, layer.v_cache, layer.pt, ctx_after,
+                                   bufs.scores, budgets, bufs.max_k, sm, bufs.sel_pages,
+                                   bufs.num_sel, bufs.out, bufs.workspace)
+    if events:
         events[2].record()
-    quest.quest_topk_pages(L, bufs.scores, ctx_after, budgets, bufs.max_k, bufs.sel_pages,
-                           bufs.num_sel)
-    if events:
-        events[3].record()
-    quest.quest_sparse_decode(L, q, layer.k_cache, layer.v_cache, layer.pt, ctx_after,
-                              bufs.sel_pages, bufs.num_sel, bufs.max_k, sm, bufs.out,
-                              bufs.workspace)
-    if events:
-        events[4].record()
 
 
 def dense_reference(layer, inputs, ctx_b, ctx_a, sm, evict, n_steps, dev):
@@ -541,15 +537,15 @@ def main():
     # 2. per-kernel breakdown: the same steps again, an event between kernels
     #    (each event adds a few microseconds of dispatch gap to its interval)
     restore()
-    ev_k = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    ev_k = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     for s in range(K):
         evict()
         run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm, ev_k[s])
     torch.cuda.synchronize()
     phase_ms = {name: [e[i].elapsed_time(e[i + 1]) for e in ev_k]
-                for i, name in [(0, "append_score"), (2, "topk"), (3, "decode")]}
-    decode_us = sum(phase_ms["decode"]) / K * 1e3
+                for i, name in [(0, "append_score"), (1, "topk_decode")]}
+    decode_us = sum(phase_ms["topk_decode"]) / K * 1e3
     decode_gbps = (kv_b / K) / (decode_us * 1e-6) / 1e9
 
     # 3. the dominant kernel alone: the fused append + page-scoring kernel over
@@ -650,7 +646,9 @@ def main():
                      "avg_launch_us": score_us, "launches": n_launch,
                      "metadata_copies": R},
         "kernels_us_event_bracketed": {k: sum(v) / K * 1e3 for k, v in phase_ms.items()},
-        "decode_kernel": {"achieved_gbps": decode_gbps, "plan": plan},
+        "topk_decode": {"selected_kv_gbps": decode_gbps, "plan": plan,
+                        "one_kernel": quest.quest_topk_sparse_decode_fused(layer.L, w.batch,
+                                                                           max_k)},
         "launch": {"hip_graph": True, "resident_layer_copies": NL,
                    "steps_per_replay": K, "selections_equal_eager": all(same)},
         "wall_s_timed_replay": t_wall,

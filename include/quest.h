@@ -237,6 +237,33 @@ int quest_sparse_decode(const quest_layout *layout, int32_t batch,
                         int32_t max_k, float sm_scale, void *out,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* quest_topk_pages_forced followed by quest_sparse_decode on its selection,
+ * in fewer launches where the shape allows (one kernel for the selection and
+ * the attention, then the merge).  Arguments as in those two calls; the
+ * selection and counts written are exactly those of quest_topk_pages_forced.
+ * The outputs equal the two calls' up to the order of the fp32 sums inside a
+ * work-group (the fused kernel merges 16 waves of half the pages each): the
+ * same tolerance against exact attention holds.  In the fused kernel every
+ * split of a row repeats the row's selection, which pays while the grid fits
+ * one resident work-group per CU (bf16, rows of at most 8192 pages, D = 64,
+ * or D = 128 with 16-token pages, at most 256 work-groups and 256 pages per
+ * split); other shapes take the two kernels in sequence.  Errors: those of
+ * both calls. */
+int quest_topk_sparse_decode(const quest_layout *layout, int32_t batch,
+                             const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *page_table, const int32_t *ctx_lens,
+                             const float *scores, const int32_t *budget_tokens,
+                             int32_t max_k, int32_t n_sink, int32_t n_recent,
+                             float sm_scale, int32_t *sel_pages, int32_t *num_sel,
+                             void *out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* 1 if quest_topk_sparse_decode runs the fused kernel for this batch and
+ * max_k, 0 if it runs the two kernels (or batch is 0), a negative
+ * quest_status for invalid arguments.  Never calls HIP. */
+int quest_topk_sparse_decode_fused(const quest_layout *layout, int32_t batch,
+                                   int32_t max_k);
+
 /* Launch plan quest_sparse_decode uses (for reports): number of KV splits per
  * (request, selection row) and pages per split.  Never calls HIP. */
 int quest_sparse_decode_plan(const quest_layout *layout, int32_t batch,

@@ -225,4 +225,42 @@ int quest_sparse_decode(const quest_layout *layout, int32_t batch, const void *q
                                        (float *)workspace, (hipStream_t)stream));
 }
 
+int quest_topk_sparse_decode(const quest_layout *layout, int32_t batch, const void *q,
+                             const void *k_cache, const void *v_cache,
+                             const int32_t *page_table, const int32_t *ctx_lens,
+                             const float *scores, const int32_t *budget_tokens, int32_t max_k,
+                             int32_t n_sink, int32_t n_recent, float sm_scale,
+                             int32_t *sel_pages, int32_t *num_sel, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  Dims dm;
+  int st = check_layout(layout, dm);
+  if (st != QUEST_OK) return st;
+  if ((st = check_batch(batch, dm)) != QUEST_OK) return st;
+  if (max_k <= 0 || n_sink < 0 || n_recent < 0) return QUEST_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return QUEST_ERR_SHAPE;
+  if (batch == 0) return QUEST_OK;
+  if (!q || !k_cache || !v_cache || !page_table || !ctx_lens || !scores || !budget_tokens ||
+      !sel_pages || !num_sel || !out)
+    return QUEST_ERR_NULL;
+  if (dm.dtype == QUEST_BF16 &&
+      (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)))
+    return QUEST_ERR_SHAPE;
+  const size_t need = quest::decode_workspace_bytes(dm, batch, max_k);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return QUEST_ERR_WORKSPACE;
+  return launched(quest::launch_topk_decode(dm, batch, q, k_cache, v_cache, page_table,
+                                            ctx_lens, scores, budget_tokens, max_k, n_sink,
+                                            n_recent, sm_scale, sel_pages, num_sel, out,
+                                            (float *)workspace, (hipStream_t)stream));
+}
+
+int quest_topk_sparse_decode_fused(const quest_layout *layout, int32_t batch, int32_t max_k) {
+  Dims dm;
+  int st = check_layout(layout, dm);
+  if (st != QUEST_OK) return st;
+  if ((st = check_batch(batch, dm)) != QUEST_OK) return st;
+  if (max_k <= 0) return QUEST_ERR_SHAPE;
+  return batch > 0 && quest::topk_decode_fused(dm, batch, max_k) ? 1 : 0;
+}
+
 }  // extern "C"

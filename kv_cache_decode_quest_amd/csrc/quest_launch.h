@@ -62,4 +62,16 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
                          int max_k, float sm_scale, void *out,
                          float *workspace, hipStream_t stream);
 
+// Top-k (forced pages as in launch_topk) then the decode of the selection;
+// one kernel where topk_decode_fused() says so, else launch_topk +
+// launch_decode.  Pure host test, no HIP call.
+bool topk_decode_fused(const Dims &dm, int batch, int max_k);
+hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *page_table,
+                              const int32_t *ctx_lens, const float *scores,
+                              const int32_t *budget_tokens, int max_k, int n_sink,
+                              int n_recent, float sm_scale, int32_t *sel_pages,
+                              int32_t *num_sel, void *out, float *workspace,
+                              hipStream_t stream);
+
 }  // namespace quest

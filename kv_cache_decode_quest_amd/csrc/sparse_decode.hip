@@ -34,6 +34,7 @@
 
 #include "quest_device.h"
 #include "quest_launch.h"
+#include "topk_select.h"
 
 namespace quest {
 
@@ -279,50 +280,54 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
   }
 }
 
-template <int D, int P, bool kPack>
-__global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
-    int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k, int n_split,
-    int pps, float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
-    const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
+// One split of one selection row on a work-group of kWaves waves (8, or 16
+// with half the pages per wave: the same pages per round).  ids(i) is the
+// row's i-th selected page (read for some i past the split or the count,
+// whose value is then ignored); count() the row's selected count, at most
+// max_k.  Writes the split's partial (acc, m, l) per head.
+template <int D, int P, bool kPack, int kWaves, typename Ids, typename Count>
+__device__ __forceinline__ void decode_split(
+    int row, int split, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages,
+    int max_k, int n_split, int pps, float scale2, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens, Ids ids,
+    Count count, float *__restrict__ partial) {
+  static_assert(kWaves == kDecodeWaves || kWaves == 2 * kDecodeWaves, "wave count");
   // 8-token pages are attended two to a 16-token tile ("tile page")
   constexpr bool kHalf = P < 16;
   constexpr int TP = kHalf ? 16 : P;
   constexpr int SUB = kHalf ? 2 : 1;    // pages per tile page
   using PR = PageRegs<D, TP>;
-  constexpr int PPW = pages_per_wave(P, D);
+  constexpr int PPW = pages_per_wave(P, D) * kDecodeWaves / kWaves;
+  static_assert(PPW >= SUB, "at least one tile page per wave");
   constexpr int NV = PPW / SUB;         // tile pages per wave and round
   constexpr int kLdsRow = D + 4;       // padded so the 16-byte stores below spread over banks
-  __shared__ float lds_m[kDecodeWaves][16];
-  __shared__ float lds_l[kDecodeWaves][16];
-  __shared__ __align__(16) float lds_acc[kDecodeWaves][16][kLdsRow];
+  __shared__ float lds_m[kWaves][16];
+  __shared__ float lds_l[kWaves][16];
+  __shared__ __align__(16) float lds_acc[kWaves][16][kLdsRow];
 
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: the page lookups below become scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int split = blockIdx.x % n_split;
-  const int row = blockIdx.x / n_split;
   // selection row `row` = request r, row hr of the request: q heads
   // hr*G .. hr*G+G-1 of the request, reading KV head hr / gdiv
   const int r = row / R, hr = row - r * R, g = hr / gdiv;
   const int first = split * pps;
-  const int32_t *sel = sel_pages + (int64_t)row * max_k;
   const int32_t *pt = page_table + (int64_t)r * max_pages;
   const int64_t page_elems = (int64_t)P * D;
   // The first round of page ids is read together with the row's count and
   // length (ids past the count are ignored below), so the chain to the first
   // K/V load is ids -> page table -> K/V.
-  constexpr int kRound = kDecodeWaves * PPW;
+  constexpr int kRound = kWaves * PPW;
   int sel0[PPW];
 #pragma unroll
   for (int u = 0; u < PPW; ++u) {
     const int i = first + wave * PPW + u;
-    sel0[u] = sel[i < max_k ? i : max_k - 1];
+    sel0[u] = ids(i < max_k ? i : max_k - 1);
   }
-  const int jfirst = sel[first < max_k ? first : max_k - 1];
-  const int nsel = min(num_sel[row], max_k);
+  const int jfirst = ids(first < max_k ? first : max_k - 1);
+  const int nsel = count();
   const int ctx = ctx_lens[r];
   if (first >= nsel) {                             // no page in this split:
     float *mine = partial + ((int64_t)row * n_split + split) * G * (D + 2);
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
       const int i = p0 + u;
-      const int j = (base == first) ? sel0[u] : sel[i < last ? i : last - 1];
+      const int j = (base == first) ? sel0[u] : ids(i < last ? i : last - 1);
       // slots past the split, or with an id outside the request, re-read the
       // split's first page (a cache hit) with no valid token
       const bool live = i < last && j >= 0 && j < n;
@@ -429,10 +434,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
     const int h = idx / D, d = idx - h * D;
     float M = -__builtin_huge_valf();
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, lds_m[w][h]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][h]);
     float a = 0.f, L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float mw = lds_m[w][h];
       const float f = (mw == -__builtin_huge_valf()) ? 0.f : exp2_fast(mw - M);
       const float aw = kPack ? lds_acc[w][h][d] + lds_acc[w][h + 8][d] : lds_acc[w][h][d];
@@ -446,6 +451,87 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
       ph[D + 1] = L;
     }
   }
+}
+
+template <int D, int P, bool kPack>
+__global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
+    int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k, int n_split,
+    int pps, float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ ctx_lens, const int32_t *__restrict__ sel_pages,
+    const int32_t *__restrict__ num_sel, float *__restrict__ partial) {
+  const int split = blockIdx.x % n_split;
+  const int row = blockIdx.x / n_split;
+  const int32_t *sel = sel_pages + (int64_t)row * max_k;
+  decode_split<D, P, kPack, kDecodeWaves>(
+      row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
+      v_cache, page_table, ctx_lens, [&](int i) { return sel[i]; },
+      [&] { return min(num_sel[row], max_k); }, partial);
+}
+
+// ---------------------------------------------------------------------------
+// Fused top-k + decode (bf16).  Every work-group of a row runs the row's
+// selection itself (1024 threads, the row's scores read from global memory),
+// keeps the page ids of its own split in LDS, then attends them with 16
+// waves of half the pages each (the same pages per round as the 8-wave
+// kernel, so the plan and the partials are the same).  Split 0 also writes
+// the row's selection and count.  The selection is repeated by every split
+// of a row: it pays where the grid fits in one wave of resident work-groups
+// (one per CU at this kernel's LDS size), so the repeats run side by side
+// instead of one launch before the decode.
+// ---------------------------------------------------------------------------
+constexpr int kFusedWaves = 2 * kDecodeWaves;
+static_assert(kFusedWaves * kWave == kTopkThreads, "the fused kernel runs the 1024-thread selection");
+constexpr int kMaxFusedPages = 256;          // pages per split the LDS list holds
+constexpr long kFusedMaxWorkGroups = 256;    // the CU count of an MI355X
+
+template <int D, int P, bool kPack>
+__global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
+    int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k, int n_split,
+    int pps, int n_sink, int n_recent, float scale2, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
+    const float *__restrict__ scores, const int32_t *__restrict__ budget_tokens,
+    int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel,
+    float *__restrict__ partial) {
+  __shared__ TopkShared sh;
+  __shared__ int32_t split_pages[kMaxFusedPages];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int split = blockIdx.x % n_split;
+  const int row = blockIdx.x / n_split;
+  const int r = row / R;
+  const int log2p = __builtin_ctz(P);                 // the page size is a power of two
+  const float *s = scores + (int64_t)row * max_pages;
+  float sv[kPerThread];                               // the row fits in registers
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int j = wave * kRegSpan + i * kWave + lane;
+    sv[i] = s[j < max_pages ? j : 0];
+  }
+  int n, k;
+  row_size(ctx_lens[r], budget_tokens[r], log2p, max_pages, max_k, n, k);
+  const int first = split * pps;
+  int32_t *out = sel_pages + (int64_t)row * max_k;
+  if (split == 0) {
+    if (tid == 0) num_sel[row] = k;
+    for (int i = k + tid; i < max_k; i += kTopkThreads) out[i] = -1;
+  }
+  select_row<true>(sh, s, sv, n, k, n_sink, n_recent, [&](int pos, int j) {
+    if (split == 0) out[pos] = j;
+    const unsigned x = (unsigned)(pos - first);
+    if (x < (unsigned)pps) split_pages[x] = j;
+  });
+  __syncthreads();
+  // positions of the split that hold no kept page are never live in the
+  // decode; any index is clamped into the list
+  decode_split<D, P, kPack, kFusedWaves>(
+      row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
+      v_cache, page_table, ctx_lens,
+      [&](int i) {
+        const int x = i - first;
+        return split_pages[x < 0 ? 0 : (x < pps ? x : pps - 1)];
+      },
+      [&] { return k; }, partial);
 }
 
 // ---------------------------------------------------------------------------
@@ -619,6 +705,18 @@ __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_s
   }
 }
 
+static hipError_t launch_merge(const Dims &dm, int batch, const DecodePlan &plan,
+                               const float *workspace, void *out, hipStream_t stream) {
+  const unsigned mblocks = (unsigned)((long)batch * dm.Hq);
+  if (dm.dtype == 1)
+    hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.R,
+                       dm.Gcols, dm.D, plan.n_split, workspace, (uint16_t *)out);
+  else
+    hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.R,
+                       dm.Gcols, dm.D, plan.n_split, workspace, (float *)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const Dims &dm, int batch, const void *q,
                          const void *k_cache, const void *v_cache,
                          const int32_t *page_table, const int32_t *ctx_lens,
@@ -663,14 +761,60 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned mblocks = (unsigned)((long)batch * dm.Hq);
-  if (dm.dtype == 1)
-    hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, workspace, (uint16_t *)out);
-  else
-    hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, workspace, (float *)out);
-  return hipGetLastError();
+  return launch_merge(dm, batch, plan, workspace, out, stream);
+}
+
+// Shapes whose 16-wave decode fits the 128 registers a 1024-thread
+// work-group leaves each lane (the others spill, and stay two launches).
+static bool fused_shape(int P, int D) { return D == 64 || (D == 128 && P == 16); }
+
+bool topk_decode_fused(const Dims &dm, int batch, int max_k) {
+  if (dm.dtype != 1 || dm.max_pages > kRegKeys || !fused_shape(dm.P, dm.D)) return false;
+  const DecodePlan p = decode_plan(dm, batch, max_k);
+  return p.pages_per_split <= kMaxFusedPages &&
+         (long)batch * dm.R * p.n_split <= kFusedMaxWorkGroups;
+}
+
+hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *page_table,
+                              const int32_t *ctx_lens, const float *scores,
+                              const int32_t *budget_tokens, int max_k, int n_sink,
+                              int n_recent, float sm_scale, int32_t *sel_pages,
+                              int32_t *num_sel, void *out, float *workspace,
+                              hipStream_t stream) {
+  if (!topk_decode_fused(dm, batch, max_k)) {
+    const hipError_t err = launch_topk(dm, batch, scores, ctx_lens, budget_tokens, max_k,
+                                       n_sink, n_recent, sel_pages, num_sel, stream);
+    if (err != hipSuccess) return err;
+    return launch_decode(dm, batch, q, k_cache, v_cache, page_table, ctx_lens, sel_pages,
+                         num_sel, max_k, sm_scale, out, workspace, stream);
+  }
+  const DecodePlan plan = decode_plan(dm, batch, max_k);
+  const float scale2 = sm_scale * kLog2e;
+  const unsigned blocks = (unsigned)((long)batch * dm.R * plan.n_split);
+#define QUEST_FUSED(DD, PP)                                                               \
+  do {                                                                                    \
+    if (dm.Gcols <= 8) QUEST_FUSED_G(DD, PP, true);                                       \
+    else QUEST_FUSED_G(DD, PP, false);                                                    \
+  } while (0)
+#define QUEST_FUSED_G(DD, PP, PK)                                                         \
+  hipLaunchKernelGGL((topk_decode_mfma_kernel<DD, PP, PK>), dim3(blocks), dim3(kTopkThreads), \
+                     0, stream, dm.R, dm.Gcols, dm.Hkv, dm.gdiv, dm.pool, dm.max_pages,    \
+                     max_k, plan.n_split, plan.pages_per_split, n_sink, n_recent, scale2,  \
+                     (const uint16_t *)q, (const uint16_t *)k_cache,                      \
+                     (const uint16_t *)v_cache, page_table, ctx_lens, scores,             \
+                     budget_tokens, sel_pages, num_sel, workspace)
+  if (dm.D == 128 && dm.P == 16) QUEST_FUSED(128, 16);
+  else if (dm.D == 64 && dm.P == 8) QUEST_FUSED(64, 8);
+  else if (dm.D == 64 && dm.P == 16) QUEST_FUSED(64, 16);
+  else if (dm.D == 64 && dm.P == 32) QUEST_FUSED(64, 32);
+  else if (dm.D == 64 && dm.P == 64) QUEST_FUSED(64, 64);
+  else return hipErrorInvalidValue;
+#undef QUEST_FUSED
+#undef QUEST_FUSED_G
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_merge(dm, batch, plan, workspace, out, stream);
 }
 
 }  // namespace quest

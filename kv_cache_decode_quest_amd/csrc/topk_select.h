@@ -1,0 +1,399 @@
+// topk_select.h -- build_decode_view, part 2: the top-k pages of every
+// (request, KV head) row within the request's token budget, as device code
+// shared by the top-k kernel and the fused top-k + decode kernel.
+//
+// k = min(max_k, clamp(floor(budget / P), 1, n)) pages of the row's n are
+// kept: the largest scores, equal scores to the lower logical page.  That
+// order is the order of the unique 64-bit key
+//     (orderable(score) << 32) | (0xffffffff - page),
+// so the selected set is unique and any exact top-k algorithm returns it.
+//
+// One 1024-thread work-group per row, radix select on the 32-bit orderable
+// score keys (held in registers for rows of up to 8192 pages).  The work is a
+// handful of barrier-separated phases, each short; wave-level scans and
+// reductions use the DPP network and ballots, not LDS round trips, and
+// cross-wave sums read one LDS word per lane.
+//  1. min and max key: every key shares the bits above the highest bit where
+//     they differ;
+//  2. refinement: an (up to) 11-bit histogram of the keys matching the known
+//     prefix, on the next bits, gives the bucket holding the k-th largest key
+//     and the count kept above it; repeated until the bucket holds at most 64
+//     keys (usually twice) or the key is fully known;
+//  3. the bucket's keys are gathered into LDS and one wave ranks the
+//     (key, page) pairs in the 64-bit order, which fixes the threshold;
+//  4. each wave walks a contiguous range of pages with ballots: a count pass,
+//     one barrier to exchange the per-wave counts, then a write pass that puts
+//     every page above the threshold, and the lowest-index pages equal to it
+//     up to the count still needed, at its ascending position (lane prefixes
+//     of the ballot masks by v_mbcnt).
+#pragma once
+#include "quest_device.h"
+
+namespace quest {
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kBinsPerLane = kBins / kTopkThreads;   // each lane owns this many buckets
+constexpr int kBinsPerWave = kBinsPerLane * kWave;
+static_assert(kBinsPerLane * kTopkThreads == kBins && kTopkWaves <= 16, "bucket ownership");
+
+// Larger score <-> larger key; -0.0 and +0.0 map to the same key.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct TopkShared {
+  uint32_t hist[kBins];
+  uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves];
+  uint32_t cand_key[kWave];
+  int32_t cand_idx[kWave];
+  uint32_t cnt_gt[kTopkWaves], cnt_eq[kTopkWaves];   // per-wave output counts
+  uint32_t cand_count;
+  uint32_t prefix;     // known high bits of the threshold key
+  uint32_t krem;       // keys still to take at or below the known prefix
+  uint32_t bucket;     // keys in the chosen bucket
+  uint32_t thresh;     // the threshold pair (key, page), once ranked
+  int32_t tidx;
+  uint32_t keq;        // keys equal to the threshold key that are kept
+};
+
+// Sum of vals[w] over the waves w before `wave` (vals: kTopkWaves entries in
+// LDS): lane l < 16 reads vals[l], masked by l < wave, and row 0 sums its 16
+// lanes on the DPP network.  Uniform result.
+__device__ __forceinline__ uint32_t sum_of_earlier_waves(const uint32_t *vals, int wave) {
+  const int lane = lane_id();
+  uint32_t x = lane < wave ? vals[lane & (kTopkWaves - 1)] : 0u;
+  x += dpp_row<kRowShr1>(0u, x);
+  x += dpp_row<kRowShr2>(0u, x);
+  x += dpp_row<kRowShr4>(0u, x);
+  x += dpp_row<kRowShr8>(0u, x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+}
+
+// min and max of vals_lo[w] / vals_hi[w] over all waves, the same way.
+__device__ __forceinline__ void minmax_over_waves(const uint32_t *vals_lo,
+                                                  const uint32_t *vals_hi, uint32_t &lo,
+                                                  uint32_t &hi) {
+  const int lane = lane_id() & (kTopkWaves - 1);
+  uint32_t a = vals_lo[lane], b = vals_hi[lane];
+  a = min(a, dpp_row<kRowShr1>(a, a));
+  a = min(a, dpp_row<kRowShr2>(a, a));
+  a = min(a, dpp_row<kRowShr4>(a, a));
+  a = min(a, dpp_row<kRowShr8>(a, a));
+  b = max(b, dpp_row<kRowShr1>(b, b));
+  b = max(b, dpp_row<kRowShr2>(b, b));
+  b = max(b, dpp_row<kRowShr4>(b, b));
+  b = max(b, dpp_row<kRowShr8>(b, b));
+  lo = (uint32_t)__builtin_amdgcn_readlane((int)a, 15);
+  hi = (uint32_t)__builtin_amdgcn_readlane((int)b, 15);
+}
+
+// The bucket (of `bins` <= kBins) holding the krem-th largest counted key,
+// buckets ranked from the top: wave w owns the kBinsPerWave buckets below the
+// top kBinsPerWave*w, lane l kBinsPerLane of them.  Results in sh.prefix /
+// sh.krem / sh.bucket.
+__device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t krem,
+                                            uint32_t prefix, int shift) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int top = bins - 1 - kBinsPerWave * wave - kBinsPerLane * lane;
+  uint32_t c[kBinsPerLane], total = 0;
+#pragma unroll
+  for (int e = 0; e < kBinsPerLane; ++e) {
+    c[e] = top - e >= 0 ? sh.hist[top - e] : 0u;
+    total += c[e];
+  }
+  const uint32_t incl = wave_incl_sum(total);
+  if (lane == kWave - 1) sh.wave_a[wave] = incl;
+  __syncthreads();
+  uint32_t run = sum_of_earlier_waves(sh.wave_a, wave) + incl - total;   // keys above `top`
+#pragma unroll
+  for (int e = 0; e < kBinsPerLane; ++e) {
+    if (run < krem && krem <= run + c[e]) {
+      sh.prefix = prefix | ((uint32_t)(top - e) << shift);
+      sh.krem = krem - run;
+      sh.bucket = c[e];
+    }
+    run += c[e];
+  }
+  __syncthreads();
+}
+
+// Rows of up to kRegKeys pages are read from HBM once, into registers: wave w
+// holds pages [S w, S w + S) with S = kRegSpan, lane l pages S w + 64 i + l
+// (i < kPerThread), the same wave-contiguous order the output pass needs, so
+// no pass re-reads memory.  Longer rows read their scores from global memory in every pass.
+constexpr int kRegKeys = 8192;
+constexpr int kPerThread = kRegKeys / kTopkThreads;
+constexpr int kRegSpan = kPerThread * kWave;              // pages per wave
+
+// Forced pages (the first n_sink and the last n_recent of a request) take the
+// largest key, above the key of any score but a NaN, so they are kept before
+// every scored page, the lower page first among them.
+constexpr uint32_t kForcedKey = 0xffffffffu;
+
+// k = min(max_k, clamp(floor(budget / P), 1, n)) of the row's n pages (n =
+// 0 and k = 0 for a request with no token); P a power of two.
+__device__ __forceinline__ void row_size(int ctx, int budget, int log2p, int max_pages,
+                                         int max_k, int &n, int &k) {
+  n = ctx <= 0 ? 0 : min((ctx + (1 << log2p) - 1) >> log2p, max_pages);
+  k = 0;
+  if (n > 0) {
+    k = budget >> log2p;                              // floor; negatives clamp to 1 below
+    k = k < 1 ? 1 : (k > n ? n : k);
+    k = k < max_k ? k : max_k;
+  }
+}
+
+// The selection of one row by a kTopkThreads work-group; every thread calls
+// it.  s: the row's scores in global memory; sv: this thread's scores of a
+// register row (wave w, lane l, slot i holds page kRegSpan w + 64 i + l);
+// n pages, k of them kept (0 <= k <= n).  emit(pos, page) is called once for
+// each kept page with its position pos in [0, k) of the ascending page list.
+template <bool kRegs, typename Emit>
+__device__ __forceinline__ void select_row(TopkShared &sh, const float *__restrict__ s,
+                                           const float (&sv)[kRegs ? kPerThread : 1], int n,
+                                           int k, int n_sink, int n_recent, Emit emit) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  if (k == n) {                                       // the whole row (or nothing)
+    for (int i = tid; i < n; i += kTopkThreads) emit(i, i);
+    return;
+  }
+  // The thread's keys: registers, or global memory for long rows.  Invalid
+  // slots (past the row) never count; their key is 0.
+  const int recent0 = n - n_recent;                   // first forced recent page
+  auto key_of = [&](float score, int j) -> uint32_t {
+    return (j < n_sink || j >= recent0) ? kForcedKey : order_key(score);
+  };
+  uint32_t u[kRegs ? kPerThread : 1];
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int j = wave * kRegSpan + i * kWave + lane;
+      u[i] = j < n ? key_of(sv[i], j) : 0u;
+    }
+  }
+  auto valid = [&](int i) { return wave * kRegSpan + i * kWave + lane < n; };
+
+  // 1. min and max key
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      if (valid(i)) {
+        lo = min(lo, u[i]);
+        hi = max(hi, u[i]);
+      }
+  } else {
+    for (int j = tid; j < n; j += kTopkThreads) {
+      const uint32_t x = key_of(s[j], j);
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    sh.wave_a[wave] = lo;
+    sh.wave_b[wave] = hi;
+  }
+#pragma unroll
+  for (int e = 0; e < kBinsPerLane; ++e) sh.hist[kBinsPerLane * tid + e] = 0;
+  if (tid == 0) sh.cand_count = 0;
+  __syncthreads();
+  minmax_over_waves(sh.wave_a, sh.wave_b, lo, hi);
+
+  uint32_t thresh, krem = (uint32_t)k;
+  if (lo == hi) {                                     // every key equal: the first k pages
+    for (int i = tid; i < k; i += kTopkThreads) emit(i, i);
+    return;
+  }
+  // 2. refine the threshold key, 11 bits at a time
+  const int hb = 31 - __builtin_clz(lo ^ hi);
+  int lowbit = hb + 1;                                // bits >= lowbit are known
+  uint32_t prefix = (uint32_t)(((uint64_t)hi >> lowbit) << lowbit);
+  uint32_t count;
+  for (bool first_pass = true;; first_pass = false) {
+    const int w = lowbit < kDigitBits ? lowbit : kDigitBits;
+    const int shift = lowbit - w;
+    const uint32_t bmask = (1u << w) - 1u;
+    const uint32_t himask = lowbit >= 32 ? 0u : (0xffffffffu << lowbit);
+    if (!first_pass) {
+#pragma unroll
+      for (int e = 0; e < kBinsPerLane; ++e) sh.hist[kBinsPerLane * tid + e] = 0;
+      __syncthreads();
+    }
+    if constexpr (kRegs) {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i)
+        if (valid(i) && ((u[i] ^ prefix) & himask) == 0u)
+          atomicAdd(&sh.hist[(u[i] >> shift) & bmask], 1u);
+    } else {
+      for (int j = tid; j < n; j += kTopkThreads) {
+        const uint32_t x = key_of(s[j], j);
+        if (((x ^ prefix) & himask) == 0u) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
+      }
+    }
+    __syncthreads();
+    pick_bucket(sh, 1 << w, krem, prefix, shift);
+    prefix = sh.prefix;
+    krem = sh.krem;
+    count = __builtin_amdgcn_readfirstlane(sh.bucket);
+    lowbit = shift;
+    if (lowbit == 0 || count <= (uint32_t)kWave) break;
+  }
+  if (lowbit == 0) {                                  // the threshold key itself
+    thresh = prefix;
+  } else {
+    // 3. gather the bucket (at most 64 keys) into LDS; wave 0 ranks the
+    // (key, page) pairs in the 64-bit order and publishes the threshold pair.
+    // Register rows also count, per wave, the keys above the bucket: all of
+    // them are kept.
+    const uint32_t himask = 0xffffffffu << lowbit;    // 1 <= lowbit <= 31 here
+    const uint32_t bucket_top = prefix | ~himask;     // largest key of the bucket
+    auto gather = [&](uint32_t x, int j) {
+      if (((x ^ prefix) & himask) == 0u) {
+        const uint32_t slot = atomicAdd(&sh.cand_count, 1u);
+        if (slot < (uint32_t)kWave) {
+          sh.cand_key[slot] = x;
+          sh.cand_idx[slot] = j;
+        }
+      }
+    };
+    if constexpr (kRegs) {
+      uint32_t above = 0;
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        if (valid(i)) gather(u[i], wave * kRegSpan + i * kWave + lane);
+        above += (uint32_t)__popcll(__ballot(valid(i) && u[i] > bucket_top));
+      }
+      if (lane == 0) sh.cnt_gt[wave] = above;
+    } else {
+      for (int j = tid; j < n; j += kTopkThreads) gather(key_of(s[j], j), j);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const bool mine = (uint32_t)lane < count;
+      const uint32_t mkey = mine ? sh.cand_key[lane] : 0u;
+      const int32_t midx = mine ? sh.cand_idx[lane] : 0;
+      // rank = candidates before this one: a larger key, or the same key
+      // at a lower page
+      uint32_t rank = 0;
+      for (uint32_t m = 0; m < count; ++m) {
+        const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mkey, (int)m);
+        const int32_t oi = __builtin_amdgcn_readlane(midx, (int)m);
+        rank += (ok > mkey || (ok == mkey && oi < midx)) ? 1u : 0u;
+      }
+      const uint64_t hit = __ballot(mine && rank == krem - 1);
+      const int tl = (int)__ffsll((unsigned long long)hit) - 1;
+      const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)mkey, tl);
+      const int32_t tidx = __builtin_amdgcn_readlane(midx, tl);
+      // equal-key pairs at or above the threshold pair
+      const uint64_t eq = __ballot(mine && mkey == th && midx <= tidx);
+      if (lane == 0) {
+        sh.thresh = th;
+        sh.tidx = tidx;
+        sh.keq = (uint32_t)__popcll(eq);
+      }
+    }
+    __syncthreads();
+    thresh = sh.thresh;
+    if constexpr (kRegs) {
+      // 4a. ascending output in one pass.  A page is kept iff its (key, page)
+      // pair is at or above the threshold pair.  This wave's first position:
+      // the kept pages of earlier waves = their keys above the bucket plus
+      // the kept candidates at a lower page than this wave's range.
+      const int32_t tidx = (int32_t)sh.tidx;
+      const int w0 = wave * kRegSpan;
+      const bool cmine = (uint32_t)lane < count;
+      const uint32_t ck = cmine ? sh.cand_key[lane] : 0u;
+      const int32_t ci = cmine ? sh.cand_idx[lane] : 0;
+      const bool ckept = cmine && (ck > thresh || (ck == thresh && ci <= tidx));
+      uint32_t pos0 = sum_of_earlier_waves(sh.cnt_gt, wave) +
+                      (uint32_t)__popcll(__ballot(ckept && ci < w0));
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        const int j = w0 + i * kWave + lane;
+        const uint32_t x = u[i];
+        const bool kept = j < n && (x > thresh || (x == thresh && j <= tidx));
+        const uint64_t m = __ballot(kept);
+        if (kept) {
+          const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos0));
+          if (pos < (uint32_t)k) emit((int)pos, j);   // never past the row
+        }
+        pos0 += (uint32_t)__popcll(m);
+      }
+      return;
+    }
+    krem = sh.keq;
+  }
+
+  // 4b. ascending output for long rows, and for ties at a fully known key.
+  // Wave w owns pages [w*span, (w+1)*span), 64 at a time: a pass of ballots
+  // counts the wave's kept pages (above the threshold key, and equal to it),
+  // one barrier exchanges the counts, and a second pass writes every kept
+  // page at its position, with lane prefixes of the ballot masks from
+  // v_mbcnt.  Register rows keep the masks from the first pass; long rows
+  // recompute them.
+  const int span = kRegs ? kRegSpan : ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
+  const int w0 = wave * span;
+  const int iters = kRegs ? kPerThread : span / kWave;
+  auto masks = [&](int i, uint64_t &mg, uint64_t &me) {
+    const int j = w0 + i * kWave + lane;
+    uint32_t x;
+    if constexpr (kRegs) x = u[i];
+    else x = j < n ? key_of(s[j], j) : 0u;
+    mg = __ballot(j < n && x > thresh);
+    me = __ballot(j < n && x == thresh);
+  };
+  constexpr int kSaved = kRegs ? kPerThread : 1;
+  uint64_t sg[kSaved], se[kSaved];
+  uint32_t gt_w = 0, eq_w = 0;
+#pragma unroll
+  for (int i = 0; i < iters; ++i) {
+    uint64_t mg, me;
+    masks(i, mg, me);
+    if constexpr (kRegs) {
+      sg[i] = mg;
+      se[i] = me;
+    }
+    gt_w += (uint32_t)__popcll(mg);
+    eq_w += (uint32_t)__popcll(me);
+  }
+  if (lane == 0) {
+    sh.cnt_gt[wave] = gt_w;
+    sh.cnt_eq[wave] = eq_w;
+  }
+  __syncthreads();
+  uint32_t gt_b = sum_of_earlier_waves(sh.cnt_gt, wave);
+  uint32_t eq_b = sum_of_earlier_waves(sh.cnt_eq, wave);
+#pragma unroll
+  for (int i = 0; i < iters; ++i) {
+    uint64_t mg, me;
+    if constexpr (kRegs) {
+      mg = sg[i];
+      me = se[i];
+    } else {
+      masks(i, mg, me);
+    }
+    // kept pages of this wave before this lane, plus those of earlier waves
+    const uint32_t gt_before =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, gt_b));
+    const uint32_t eq_before =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, eq_b));
+    const bool is_gt = (mg >> lane) & 1ull;
+    const bool is_eq = (me >> lane) & 1ull;
+    if (is_gt || (is_eq && eq_before < krem)) {
+      const uint32_t pos = gt_before + min(eq_before, krem);
+      if (pos < (uint32_t)k) emit((int)pos, w0 + i * kWave + lane);   // never past the row
+    }
+    gt_b += (uint32_t)__popcll(mg);
+    eq_b += (uint32_t)__popcll(me);
+  }
+}
+
+}  // namespace quest

@@ -25,7 +25,8 @@ QUEST_SELECT_PER_KV_HEAD, QUEST_SELECT_PER_Q_HEAD = 0, 1
 # exported symbols declared in include/quest.h
 EXPORTS = ("quest_abi_version", "quest_status_string", "quest_append_kv", "quest_page_scores",
            "quest_append_score", "quest_topk_pages", "quest_topk_pages_forced",
-           "quest_sparse_decode_workspace_bytes", "quest_sparse_decode", "quest_sparse_decode_plan")
+           "quest_sparse_decode_workspace_bytes", "quest_sparse_decode", "quest_sparse_decode_plan",
+           "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused")
 
 
 class QuestError(RuntimeError):
@@ -76,8 +77,12 @@ def load(path: str = LIB_PATH):
     L.quest_sparse_decode.argtypes = [lp, i32, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp,
                                       sz, vp]
     L.quest_sparse_decode_plan.argtypes = [lp, i32, i32, ip, ip]
+    L.quest_topk_sparse_decode.argtypes = [lp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                           f32, vp, vp, vp, vp, sz, vp]
+    L.quest_topk_sparse_decode_fused.argtypes = [lp, i32, i32]
     for name in ("quest_append_kv", "quest_page_scores", "quest_append_score", "quest_topk_pages",
-                 "quest_topk_pages_forced", "quest_sparse_decode", "quest_sparse_decode_plan"):
+                 "quest_topk_pages_forced", "quest_sparse_decode", "quest_sparse_decode_plan",
+                 "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused"):
         getattr(L, name).restype = ctypes.c_int
     if L.quest_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libquest ABI {L.quest_abi_version()} != binding ABI {ABI_VERSION}")
@@ -291,6 +296,44 @@ def quest_sparse_decode(L: QuestLayout, q, k_cache, v_cache, page_table, ctx_len
     _raise("quest_sparse_decode", st)
 
 
+def quest_topk_sparse_decode(L: QuestLayout, q, k_cache, v_cache, page_table, ctx_lens, scores,
+                             budget_tokens, max_k, sm_scale, sel_pages, num_sel, out, workspace,
+                             n_sink=0, n_recent=0):
+    """quest_topk_pages_forced then quest_sparse_decode on its selection, in
+    one kernel (plus the merge) where the shape allows."""
+    dt, dev = _layout_dtype(L), q.device
+    batch = ctx_lens.shape[0]
+    kshape, vshape, _ = _pool_shapes(L)
+    rows = selection_rows(L)
+    _check(q, "q", dt, (batch, L.num_q_heads, L.head_dim), dev)
+    _check(k_cache, "k_cache", dt, kshape, dev)
+    _check(v_cache, "v_cache", dt, vshape, dev)
+    _check(page_table, "page_table", torch.int32, (batch, L.max_pages_per_seq), dev)
+    _check(ctx_lens, "ctx_lens", torch.int32, (batch,), dev)
+    _check(scores, "scores", torch.float32, (batch, rows, L.max_pages_per_seq), dev)
+    _check(budget_tokens, "budget_tokens", torch.int32, (batch,), dev)
+    _check(sel_pages, "sel_pages", torch.int32, (batch, rows, max_k), dev)
+    _check(num_sel, "num_sel", torch.int32, (batch, rows), dev)
+    _check(out, "out", dt, (batch, L.num_q_heads, L.head_dim), dev)
+    _check(workspace, "workspace", None, None, dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load().quest_topk_sparse_decode(ctypes.byref(L), batch, _ptr(q), _ptr(k_cache),
+                                         _ptr(v_cache), _ptr(page_table), _ptr(ctx_lens),
+                                         _ptr(scores), _ptr(budget_tokens), int(max_k),
+                                         int(n_sink), int(n_recent), float(sm_scale),
+                                         _ptr(sel_pages), _ptr(num_sel), _ptr(out),
+                                         _ptr(workspace), nbytes, _stream(dev))
+    _raise("quest_topk_sparse_decode", st)
+
+
+def quest_topk_sparse_decode_fused(L: QuestLayout, batch: int, max_k: int) -> bool:
+    """Whether quest_topk_sparse_decode runs as one fused kernel here."""
+    st = load().quest_topk_sparse_decode_fused(ctypes.byref(L), int(batch), int(max_k))
+    if st < 0:
+        _raise("quest_topk_sparse_decode_fused", st)
+    return st == 1
+
+
 @dataclass
 class DecodeBuffers:
     """Caller-owned per-step buffers for one layer (scores, selection, output)."""
@@ -320,13 +363,12 @@ def decode_step(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, ctx_lens, b
                 page_table, k_cache, v_cache, kmeta, bufs: DecodeBuffers, sm_scale,
                 group_reduce="max", max_new_per_seq=1):
     """One Quest decode step of one layer: on_kv_stored fused with the page
-    scores, then the top-k (the rest of build_decode_view), then attention
-    over the view.  Three ABI calls, all asynchronous on the current stream;
+    scores, then the top-k (the rest of build_decode_view) and attention over
+    the view.  Two ABI calls, both asynchronous on the current stream;
     ctx_lens must equal ctx_before + the new tokens."""
     quest_append_score(L, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq, page_table,
                        k_cache, v_cache, kmeta, bufs.scores, group_reduce)
-    quest_topk_pages(L, bufs.scores, ctx_lens, budget_tokens, bufs.max_k, bufs.sel_pages,
-                     bufs.num_sel)
-    quest_sparse_decode(L, q, k_cache, v_cache, page_table, ctx_lens, bufs.sel_pages,
-                        bufs.num_sel, bufs.max_k, sm_scale, bufs.out, bufs.workspace)
+    quest_topk_sparse_decode(L, q, k_cache, v_cache, page_table, ctx_lens, bufs.scores,
+                             budget_tokens, bufs.max_k, sm_scale, bufs.sel_pages, bufs.num_sel,
+                             bufs.out, bufs.workspace)
     return bufs.out

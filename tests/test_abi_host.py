@@ -226,3 +226,50 @@ def test_product_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "quest_oracle" not in text and "libquest_oracle" not in text, f
+
+
+def topk_decode_call(lib, L, batch=1, max_k=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, scores=FAKE,
+               scale=0.1, n_sink=0, n_recent=0):
+    return lib.quest_topk_sparse_decode(ctypes.byref(L), batch, q, FAKE, FAKE, FAKE, FAKE,
+                                        scores, FAKE, max_k, n_sink, n_recent, scale, FAKE, FAKE,
+                                        FAKE, ws, ws_bytes, None)
+
+
+def test_topk_sparse_decode_rejections(lib):
+    """The combined call validates like quest_topk_pages_forced and
+    quest_sparse_decode together, before any launch."""
+    L = layout()
+    assert topk_decode_call(lib, L, scores=None) == ERR_NULL
+    assert topk_decode_call(lib, L, q=None) == ERR_NULL
+    assert topk_decode_call(lib, L, n_sink=-1) == ERR_SHAPE
+    assert topk_decode_call(lib, L, n_recent=-1) == ERR_SHAPE
+    assert topk_decode_call(lib, L, max_k=0) == ERR_SHAPE
+    assert topk_decode_call(lib, L, scale=float("nan")) == ERR_SHAPE
+    assert topk_decode_call(lib, L, q=ctypes.c_void_p(0x100002)) == ERR_SHAPE
+    need = lib.quest_sparse_decode_workspace_bytes(ctypes.byref(L), 1, 16)
+    assert topk_decode_call(lib, L, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert topk_decode_call(lib, L, ws=None) == ERR_WORKSPACE
+    assert topk_decode_call(lib, layout(head_dim=96)) == ERR_UNSUPPORTED
+    assert lib.quest_topk_sparse_decode(ctypes.byref(L), 0, None, None, None, None, None, None,
+                                        None, 4, 0, 0, 0.1, None, None, None, None, 0,
+                                        None) == OK
+
+
+def test_topk_sparse_decode_fused_rule(lib):
+    """One kernel for bf16 rows of at most 8192 pages, D 64 or (D 128, P 16),
+    at most 256 pages per split and 256 work-groups; two kernels otherwise."""
+    bench = layout(num_pool_pages=8 * 8009, max_pages_per_seq=8009)
+    assert quest.quest_topk_sparse_decode_fused(bench, 8, 256)          # 32 rows x 8 splits
+    assert not quest.quest_topk_sparse_decode_fused(bench, 9, 256)      # 288 work-groups
+    assert not quest.quest_topk_sparse_decode_fused(layout(selection=1), 8, 256)
+    assert not quest.quest_topk_sparse_decode_fused(layout(page_size=32), 1, 16)
+    assert not quest.quest_topk_sparse_decode_fused(layout(page_size=8), 1, 16)
+    assert quest.quest_topk_sparse_decode_fused(layout(head_dim=64, page_size=64), 1, 16)
+    assert not quest.quest_topk_sparse_decode_fused(layout(dtype=0, head_dim=64), 1, 16)
+    assert not quest.quest_topk_sparse_decode_fused(layout(max_pages_per_seq=8193), 1, 16)
+    assert quest.quest_topk_sparse_decode_fused(layout(max_pages_per_seq=8192), 1, 16)
+    assert not quest.quest_topk_sparse_decode_fused(layout(), 0, 16)
+    big = layout(num_kv_heads=1, num_q_heads=8, num_pool_pages=9000, max_pages_per_seq=8000)
+    assert quest.quest_topk_sparse_decode_fused(big, 1, 8000)           # 250 splits of 32
+    assert not quest.quest_topk_sparse_decode_fused(big, 1, 100000)     # 256 splits of 416
+    assert lib.quest_topk_sparse_decode_fused(ctypes.byref(layout()), 1, 0) == ERR_SHAPE
