@@ -149,3 +149,59 @@ def test_fused_bench_shape_equals_two_calls(gpu_lib):
     assert torch.equal(fb.sel_pages, bufs.sel_pages)
     one, two = to_f64(fb.out), to_f64(bufs.out)
     assert np.all(one_bf16_ulp(one, two)), float(np.abs(one - two).max())
+
+
+@pytest.mark.parametrize("n_max,P,D,max_k,forced", [
+    (300, 16, 128, 298, (0, 0)), (300, 16, 128, 298, (1, 2)), (2050, 32, 64, 400, (0, 0)),
+    (8008, 16, 128, 256, (0, 0)), (8008, 16, 128, 256, (4, 4)), (900, 8, 64, 300, (0, 0)),
+    (500, 64, 64, 200, (2, 1))])
+def test_fused_selection_on_constructed_rows(n_max, P, D, max_k, forced, gpu_lib):
+    """The fused kernel's selection on score rows built to reach every branch
+    of the row selection (distinct keys, heavy ties, all equal, signed zeros,
+    adjacent floats, more than 64 keys tied at the threshold, wide and narrow
+    ranges; k = 1, n - 1, n, truncation by max_k; forced pages) equals the
+    oracle's, and its outputs equal the two-call path's within one bf16 step."""
+    from test_gpu_parity import _topk_rows
+    gen = torch.Generator().manual_seed(7000 + n_max + P)
+    rows = _topk_rows(n_max, gen)
+    Hkv, G = 2, 8
+    B = (len(rows) + 1) // 2
+    while len(rows) < B * Hkv:
+        rows.append(torch.randn(n_max, generator=gen))
+    scores = torch.stack(rows).reshape(B, Hkv, n_max).contiguous().to(DEV)
+    ctx_choices = [n_max * P, n_max * P - P + 1, 1, P + 1, (n_max // 2) * P, n_max * P - 3]
+    bud_choices = [3 * P, (n_max - 1) * P, 5, 0, n_max * P * 2, P * (n_max // 3) + 7]
+    ctx = torch.tensor([ctx_choices[b % 6] for b in range(B)], dtype=torch.int32, device=DEV)
+    bud = torch.tensor([bud_choices[b % 6] for b in range(B)], dtype=torch.int32, device=DEV)
+    pool = B * n_max
+    L = quest.make_layout(G * Hkv, Hkv, D, P, torch.bfloat16, pool, n_max)
+    assert quest.quest_topk_sparse_decode_fused(L, B, max_k)
+    pt = torch.arange(pool, dtype=torch.int32, device=DEV).view(B, n_max)
+    g = torch.Generator(device=DEV).manual_seed(8000 + n_max)
+    k_cache = torch.randn((pool, Hkv, P, D), generator=g, device=DEV).to(torch.bfloat16)
+    v_cache = torch.randn((pool, Hkv, D, P), generator=g, device=DEV).to(torch.bfloat16)
+    q = torch.randn((B, G * Hkv, D), generator=g, device=DEV).to(torch.bfloat16)
+    sm = D ** -0.5
+    ns, nr = forced
+    two = quest.alloc_decode_buffers(L, B, max_k, DEV)
+    one = quest.alloc_decode_buffers(L, B, max_k, DEV)
+    one.sel_pages.fill_(12345)
+    quest.quest_topk_pages_forced(L, scores, ctx, bud, max_k, ns, nr, two.sel_pages, two.num_sel)
+    quest.quest_sparse_decode(L, q, k_cache, v_cache, pt, ctx, two.sel_pages, two.num_sel, max_k,
+                              sm, two.out, two.workspace)
+    quest.quest_topk_sparse_decode(L, q, k_cache, v_cache, pt, ctx, scores, bud, max_k, sm,
+                                   one.sel_pages, one.num_sel, one.out, one.workspace, ns, nr)
+    torch.cuda.synchronize()
+    sel, nsel = one.sel_pages.cpu().numpy(), one.num_sel.cpu().numpy()
+    s64 = scores.cpu().double().numpy()
+    for b in range(B):
+        n = min(-(-int(ctx[b]) // P), n_max)
+        k = min(oracle.pages_for_budget(int(bud[b]), int(ctx[b]), P), max_k)
+        for h in range(Hkv):
+            want = oracle.select(np.ascontiguousarray(s64[b, h, :n]), k, ns, nr)
+            assert nsel[b, h] == k, (b, h)
+            assert np.array_equal(sel[b, h, :k], want), (b, h, n, k)
+            assert np.all(sel[b, h, k:] == -1)
+    assert torch.equal(one.sel_pages, two.sel_pages)
+    a, c = to_f64(one.out), to_f64(two.out)
+    assert np.all(one_bf16_ulp(a, c)), float(np.abs(a - c).max())
