@@ -89,9 +89,9 @@ class Layer:
                                     self.pt_host[r], self.host[0], self.host[1])
         self.ctx = self.ctx + 1
 
-    def append_score_step(self, q, k_new, v_new, bufs, reduce="max"):
+    def append_score_step(self, q, k_new, v_new, bufs, reduce="max", topk=True):
         """One token per request through the fused quest_append_score (and the
-        same store on the host), then the top-k."""
+        same store on the host), then (topk) the top-k."""
         B = self.w.batch
         cu = torch.arange(B + 1, dtype=torch.int32, device=self.device)
         quest.quest_append_score(self.L, q, k_new, v_new, cu, self.ctx, 1, self.pt, self.k_cache,
@@ -104,8 +104,16 @@ class Layer:
                                     np.ascontiguousarray(vn[r:r + 1]), int(ctx[r]),
                                     self.pt_host[r], self.host[0], self.host[1])
         self.ctx = self.ctx + 1
-        quest.quest_topk_pages(self.L, bufs.scores, self.ctx, self.budgets(), bufs.max_k,
-                               bufs.sel_pages, bufs.num_sel)
+        if topk:
+            quest.quest_topk_pages(self.L, bufs.scores, self.ctx, self.budgets(), bufs.max_k,
+                                   bufs.sel_pages, bufs.num_sel)
+
+    def select_attend(self, q, bufs, sm_scale=None):
+        """The top-k and the attention through quest_topk_sparse_decode."""
+        sm = workloads.default_sm_scale(self.w) if sm_scale is None else sm_scale
+        quest.quest_topk_sparse_decode(self.L, q, self.k_cache, self.v_cache, self.pt, self.ctx,
+                                       bufs.scores, self.budgets(), bufs.max_k, sm,
+                                       bufs.sel_pages, bufs.num_sel, bufs.out, bufs.workspace)
 
     def budgets(self):
         return workloads.budget_tokens(self.w, self.ctx).to(self.device)
