@@ -516,14 +516,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
     if (tid == 0) num_sel[row] = k;
     for (int i = k + tid; i < max_k; i += kTopkThreads) out[i] = -1;
   }
+  // positions of the split at or past the row's count k are never emitted
+  // (and never live below): they hold 0; the emitted ones are disjoint
+  for (int i = tid; i < pps; i += kTopkThreads)
+    if (first + i >= k) split_pages[i] = 0;
   select_row<true>(sh, s, sv, n, k, n_sink, n_recent, [&](int pos, int j) {
     if (split == 0) out[pos] = j;
     const unsigned x = (unsigned)(pos - first);
     if (x < (unsigned)pps) split_pages[x] = j;
   });
   __syncthreads();
-  // positions of the split that hold no kept page are never live in the
-  // decode; any index is clamped into the list
+  // any index is clamped into the list
   decode_split<D, P, kPack, kFusedWaves>(
       row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
       v_cache, page_table, ctx_lens,

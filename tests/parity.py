@@ -22,6 +22,7 @@ import torch
 import oracle
 from helpers import elem_of, to_f64, to_oracle
 from kv_cache_decode_quest_amd import quest, workloads
+from kv_cache_decode_quest_amd.workloads import WORKLOADS, scaled
 
 U32 = 2.0 ** -24
 
@@ -226,3 +227,67 @@ def check_out(got, ref, dtype, what="output"):
     bad = err > tol
     assert not bad.any(), f"{what}: {bad.sum()} elements beyond the internal bar, max {err.max():.3g}"
     return float(err.max())
+
+
+# Reduced copies of the workloads (the oracle finishes them in seconds; they
+# still span several tiles and a ragged tail), and edge workloads.
+SMALL = {
+    "tiny": WORKLOADS["tiny"],
+    "layer32k_small": scaled(WORKLOADS["layer32k"], batch=3, ctx=4000, budget_tokens=512,
+                             steps=3),
+    "bench128k_small": scaled(WORKLOADS["bench128k"], batch=2, ctx=6000, budget_tokens=1024,
+                              steps=3),
+    "ragged_small": scaled(WORKLOADS["ragged"], batch=6, ctx_range=(40, 3000), steps=3),
+    "layers48_small": scaled(WORKLOADS["layers48"], batch=3, ctx=2048, budget_tokens=256,
+                             layers=2, steps=2),
+    "edges": workloads.Workload("edges", 7, 16, 2, 128, 16, "bf16",
+                                ctx_list=(0, 1, 15, 16, 17, 33, 700), budget_tokens=40,
+                                poison=float("nan"), steps=2, seed=77),
+    "edges_d64_p32": workloads.Workload("edges_d64_p32", 5, 12, 4, 64, 32, "bf16",
+                                        ctx_list=(1, 31, 32, 65, 1000), budget_tokens=100,
+                                        poison=float("nan"), steps=2, seed=78),
+    "f32_g1": workloads.Workload("f32_g1", 2, 2, 2, 128, 32, "f32", ctx=2100,
+                                 budget_tokens=300, steps=2, seed=79, permute_pages=True,
+                                 poison=1e4),
+    # groups wider than 8 q heads (every head column of the matrix-core tiles in use)
+    "g16_p32": workloads.Workload("g16_p32", 3, 32, 2, 128, 32, "bf16", ctx=3000,
+                                  budget_tokens=600, steps=2, seed=80, poison=float("nan")),
+    "g12_d64": workloads.Workload("g12_d64", 2, 24, 2, 64, 16, "bf16", ctx_list=(500, 2000),
+                                  budget_tokens=256, steps=2, seed=81, permute_pages=True),
+    # 64-token pages (one page per wave and round in the decode)
+    "p64_d128": workloads.Workload("p64_d128", 4, 32, 4, 128, 64, "bf16",
+                                   ctx_list=(1, 64, 1000, 6001), budget_tokens=640, steps=2,
+                                   seed=82, poison=float("nan"), permute_pages=True),
+    "p64_d64_f32": workloads.Workload("p64_d64_f32", 2, 8, 2, 64, 64, "f32", ctx=2100,
+                                      budget_tokens=500, steps=2, seed=83),
+    # 8-token pages (two to a 16-token matrix-core tile in the decode); odd
+    # page budgets leave the second half of a tile empty
+    "p8_d128": workloads.Workload("p8_d128", 4, 32, 4, 128, 8, "bf16",
+                                  ctx_list=(1, 9, 1001, 5003), budget_tokens=200, steps=2,
+                                  seed=84, poison=float("nan"), permute_pages=True),
+    "p8_d64": workloads.Workload("p8_d64", 3, 12, 4, 64, 8, "bf16", ctx_list=(7, 800, 3000),
+                                 budget_tokens=88, steps=2, seed=85),
+    "p8_f32": workloads.Workload("p8_f32", 2, 8, 2, 128, 8, "f32", ctx=700, budget_tokens=136,
+                                 steps=2, seed=86),
+}
+
+
+def topk_rows(n_max, gen):
+    """Score rows that reach every branch of the row selection."""
+    rows = []
+    rows.append(torch.randn(n_max, generator=gen))                           # distinct
+    rows.append(torch.randint(0, 5, (n_max,), generator=gen).float())        # heavy ties
+    rows.append(torch.full((n_max,), 3.25))                                  # all equal
+    z = torch.zeros(n_max)
+    z[::2] = -0.0
+    z[::7] = -1.0
+    rows.append(z)                                                           # signed zeros
+    base = torch.ones(n_max)
+    rows.append(torch.nextafter(base, base + 1) + (torch.arange(n_max) % 13) * 2 ** -23)
+    thr = torch.full((n_max,), 5.0)                                          # > 64 tied keys
+    thr[: n_max // 10] = 9.0 + torch.rand(n_max // 10, generator=gen)
+    thr[n_max // 2:] = -torch.rand(n_max - n_max // 2, generator=gen)
+    rows.append(thr[torch.randperm(n_max, generator=gen)])
+    rows.append(torch.randn(n_max, generator=gen) * 1e30)                    # wide range
+    rows.append(torch.randn(n_max, generator=gen) * 1e-3 + 100.0)            # narrow range
+    return rows

@@ -16,8 +16,7 @@ import oracle
 from helpers import to_f64, to_oracle
 from kv_cache_decode_quest_amd import quest, workloads
 from kv_cache_decode_quest_amd.workloads import WORKLOADS, scaled
-from parity import Layer, check_out, compare_selection, log
-from test_gpu_parity import SMALL
+from parity import SMALL, Layer, check_out, compare_selection, log, topk_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -161,9 +160,8 @@ def test_fused_selection_on_constructed_rows(n_max, P, D, max_k, forced, gpu_lib
     adjacent floats, more than 64 keys tied at the threshold, wide and narrow
     ranges; k = 1, n - 1, n, truncation by max_k; forced pages) equals the
     oracle's, and its outputs equal the two-call path's within one bf16 step."""
-    from test_gpu_parity import _topk_rows
     gen = torch.Generator().manual_seed(7000 + n_max + P)
-    rows = _topk_rows(n_max, gen)
+    rows = topk_rows(n_max, gen)
     Hkv, G = 2, 8
     B = (len(rows) + 1) // 2
     while len(rows) < B * Hkv:
