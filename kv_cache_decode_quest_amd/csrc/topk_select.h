@@ -18,14 +18,20 @@
 //  2. refinement: an (up to) 11-bit histogram of the keys matching the known
 //     prefix, on the next bits, gives the bucket holding the k-th largest key
 //     and the count kept above it; repeated until the bucket holds at most 64
-//     keys (usually twice) or the key is fully known;
-//  3. the bucket's keys are gathered into LDS and one wave ranks the
-//     (key, page) pairs in the 64-bit order, which fixes the threshold;
-//  4. each wave walks a contiguous range of pages with ballots: a count pass,
-//     one barrier to exchange the per-wave counts, then a write pass that puts
-//     every page above the threshold, and the lowest-index pages equal to it
-//     up to the count still needed, at its ascending position (lane prefixes
-//     of the ballot masks by v_mbcnt).
+//     keys (one pass on rows of a few thousand normal scores) or the key is
+//     fully known;
+//  3. the bucket's keys are gathered into LDS (register rows also count, per
+//     wave, the keys above the bucket) and one wave ranks the (key, page)
+//     pairs in the 64-bit order, which fixes the threshold pair;
+//  4. one ballot pass: a page is kept iff its pair is at or above the
+//     threshold pair; a wave's first position is the above-bucket keys of
+//     earlier waves plus the kept bucket keys at lower pages, and lane
+//     positions are prefixes of the ballot masks (v_mbcnt).  Rows over 8192
+//     pages, and thresholds resolved to a full key, take a two-pass form
+//     instead: a count pass, one barrier to exchange the per-wave counts,
+//     then a write pass that puts every page above the threshold key, and
+//     the lowest-index pages equal to it up to the count still needed, at
+//     its ascending position.
 #pragma once
 #include "quest_device.h"
 
