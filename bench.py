@@ -489,13 +489,18 @@ def main():
         rot_step(s)
     torch.cuda.synchronize()
     eager_sel, eager_nsel = sels.clone(), nsels.clone()
+    eager_out = [b.out.clone() for b in per_copy]        # each copy's last step
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for s in range(K):
             rot_step(s)
     graph.replay()
     torch.cuda.synchronize()
-    same = [torch.equal(sels, eager_sel) and torch.equal(nsels, eager_nsel)]
+    def same_as_eager():
+        return (torch.equal(sels, eager_sel) and torch.equal(nsels, eager_nsel) and
+                all(torch.equal(b.out, o) for b, o in zip(per_copy, eager_out)))
+
+    same = [same_as_eager()]
     log(f"timed: {K} steps replayed")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     evict()
@@ -507,7 +512,7 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_s = ev[0].elapsed_time(ev[1]) / 1e3
-    same.append(torch.equal(sels, eager_sel) and torch.equal(nsels, eager_nsel))
+    same.append(same_as_eager())
     value = w.batch * K / total_s
 
     meta_b, kv_b = 0, 0
@@ -650,7 +655,7 @@ def main():
                         "one_kernel": quest.quest_topk_sparse_decode_fused(layer.L, w.batch,
                                                                            max_k)},
         "launch": {"hip_graph": True, "resident_layer_copies": NL,
-                   "steps_per_replay": K, "selections_equal_eager": all(same)},
+                   "steps_per_replay": K, "selections_and_outputs_equal_eager": all(same)},
         "wall_s_timed_replay": t_wall,
         "eager_evicted": eager,
         "dense_reference": dense,
