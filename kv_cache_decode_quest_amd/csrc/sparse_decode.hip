@@ -284,14 +284,15 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
 // with half the pages per wave: the same pages per round).  ids(i) is the
 // row's i-th selected page (read for some i past the split or the count,
 // whose value is then ignored); count() the row's selected count, at most
-// max_k.  Writes the split's partial (acc, m, l) per head.
-template <int D, int P, bool kPack, int kWaves, typename Ids, typename Count>
+// max_k; ctx_of(r) request r's length.  Writes the split's partial (acc, m,
+// l) per head.
+template <int D, int P, bool kPack, int kWaves, typename Ids, typename Count, typename CtxOf>
 __device__ __forceinline__ void decode_split(
     int row, int split, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages,
     int max_k, int n_split, int pps, float scale2, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
-    const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens, Ids ids,
-    Count count, float *__restrict__ partial) {
+    const int32_t *__restrict__ page_table, CtxOf ctx_of, Ids ids, Count count,
+    float *__restrict__ partial) {
   static_assert(kWaves == kDecodeWaves || kWaves == 2 * kDecodeWaves, "wave count");
   // 8-token pages are attended two to a 16-token tile ("tile page")
   constexpr bool kHalf = P < 16;
@@ -328,7 +329,7 @@ __device__ __forceinline__ void decode_split(
   }
   const int jfirst = ids(first < max_k ? first : max_k - 1);
   const int nsel = count();
-  const int ctx = ctx_lens[r];
+  const int ctx = ctx_of(r);
   if (first >= nsel) {                             // no page in this split:
     float *mine = partial + ((int64_t)row * n_split + split) * G * (D + 2);
     for (int h = threadIdx.x; h < G; h += blockDim.x) {   // an empty partial
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
   const int32_t *sel = sel_pages + (int64_t)row * max_k;
   decode_split<D, P, kPack, kDecodeWaves>(
       row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
-      v_cache, page_table, ctx_lens, [&](int i) { return sel[i]; },
+      v_cache, page_table, [&](int r) { return ctx_lens[r]; }, [&](int i) { return sel[i]; },
       [&] { return min(num_sel[row], max_k); }, partial);
 }
 
@@ -508,8 +509,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
     const int j = wave * kRegSpan + i * kWave + lane;
     sv[i] = s[j < max_pages ? j : 0];
   }
+  const int ctx = ctx_lens[r];
   int n, k;
-  row_size(ctx_lens[r], budget_tokens[r], log2p, max_pages, max_k, n, k);
+  row_size(ctx, budget_tokens[r], log2p, max_pages, max_k, n, k);
   const int first = split * pps;
   int32_t *out = sel_pages + (int64_t)row * max_k;
   if (split == 0) {
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
   // any index is clamped into the list
   decode_split<D, P, kPack, kFusedWaves>(
       row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
-      v_cache, page_table, ctx_lens,
+      v_cache, page_table, [&](int) { return ctx; },
       [&](int i) {
         const int x = i - first;
         return split_pages[x < 0 ? 0 : (x < pps ? x : pps - 1)];
