@@ -196,6 +196,77 @@ def per_q_head_reference(layer, inputs, ctx_b, ctx_a, budgets, sm, evict, n_step
             "hbm_frac_peak": (meta_b + kv_b) / total_s / 1e9 / PEAK_HBM_GBPS}
 
 
+def timed_variant(layer, inputs, ctx_b, ctx_a, budgets, sm, evict, n_steps, dev, reduce="max",
+                  n_sink=0, n_recent=0):
+    """The step (quest_append_score + quest_topk_sparse_decode) of one
+    variant, timed like eager_evicted: one event pair per step, the cache
+    evicted before each.  Bytes = metadata + selected valid K/V."""
+    w, L = layer.w, layer.L
+    B, P = w.batch, w.page_size
+    max_k = max(1, max(int((b // P).max()) for b in budgets[:n_steps]))
+    bufs = quest.alloc_decode_buffers(L, B, max_k, dev)
+    sels = torch.empty((n_steps,) + tuple(bufs.sel_pages.shape), dtype=torch.int32, device=dev)
+    nsels = torch.empty((n_steps,) + tuple(bufs.num_sel.shape), dtype=torch.int32, device=dev)
+
+    def step(s):
+        q, k_new, v_new = inputs[s]
+        quest.quest_append_score(L, q, k_new, v_new, layer.cu1, ctx_b[s], 1, layer.pt,
+                                 layer.k_cache, layer.v_cache, layer.kmeta, bufs.scores, reduce)
+        quest.quest_topk_sparse_decode(L, q, layer.k_cache, layer.v_cache, layer.pt, ctx_a[s],
+                                       bufs.scores, budgets[s], max_k, sm, bufs.sel_pages,
+                                       bufs.num_sel, bufs.out, bufs.workspace, n_sink, n_recent)
+
+    step(0)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for s in range(n_steps):
+        evict()
+        ev[s][0].record()
+        step(s)
+        ev[s][1].record()
+        sels[s].copy_(bufs.sel_pages)
+        nsels[s].copy_(bufs.num_sel)
+    torch.cuda.synchronize()
+    total_s = sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3
+    meta_b = kv_b = 0
+    for s in range(n_steps):
+        m, kv = step_bytes(w, ctx_a[s], sels[s], nsels[s])
+        meta_b += m
+        kv_b += kv
+    return {"page_size": P, "group_reduce": reduce, "n_sink": n_sink, "n_recent": n_recent,
+            "tokens_per_s": B * n_steps / total_s, "ms_per_step": total_s / n_steps * 1e3,
+            "steps": n_steps, "metadata_bytes_per_step": meta_b / n_steps,
+            "selected_kv_bytes_per_step": kv_b / n_steps,
+            "hbm_gbps": (meta_b + kv_b) / total_s / 1e9,
+            "hbm_frac_peak": (meta_b + kv_b) / total_s / 1e9 / PEAK_HBM_GBPS,
+            "one_kernel_topk_decode": quest.quest_topk_sparse_decode_fused(L, B, max_k)}
+
+
+def variant_legs(layer, inputs, ctx_b, ctx_a, budgets, sm, evict, n_steps, dev, restore):
+    """The variants the method leaves open, on the benchmark's shape and token
+    budget: the SUM group reduction and forced sink / recent pages on the
+    same cache, and page sizes 8, 32 and 64 on caches of their own."""
+    out = {}
+    restore()
+    out["sum_reduce"] = timed_variant(layer, inputs, ctx_b, ctx_a, budgets, sm, evict, n_steps,
+                                      dev, reduce="sum")
+    restore()
+    out["forced_1_sink_2_recent"] = timed_variant(layer, inputs, ctx_b, ctx_a, budgets, sm,
+                                                  evict, n_steps, dev, n_sink=1, n_recent=2)
+    restore()
+    for P in (8, 32, 64):
+        wp = workloads.scaled(layer.w, page_size=P)
+        lp = BenchLayer(wp, n_steps, dev)
+        lp.prefill = None
+        cb = [(lp.ctx0 + s).to(torch.int32) for s in range(n_steps)]
+        ca = [(lp.ctx0 + s + 1).to(torch.int32) for s in range(n_steps)]
+        bp = [workloads.budget_tokens(wp, c).to(dev) for c in ca]
+        out[f"page_{P}"] = timed_variant(lp, inputs, cb, ca, bp, sm, evict, n_steps, dev)
+        del lp
+        torch.cuda.empty_cache()
+    return out
+
+
 def prefill_chunk_append(layer, chunk, n_calls, evict, dev):
     """Bulk on_kv_stored at prefill-chunk granularity: each call stores one
     `chunk`-token chunk of every request's prompt (positions c*chunk ..) with
@@ -403,6 +474,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=16)
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the per-q-head selection reference")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the SUM-reduction, forced-page and page-size variants")
     ap.add_argument("--prefill-chunk", type=int, default=4096,
                     help="chunk size of the prefill append leg (0 to skip)")
     ap.add_argument("--roofline-copies", type=int, default=8)
@@ -609,6 +682,16 @@ def main():
         per_head["shared_speedup"] = eager["tokens_per_s"] / per_head["tokens_per_s"]
         restore()
 
+    variants = None
+    if not args.no_variants:
+        log(f"variants: SUM reduction, forced pages, page sizes 8/32/64, "
+            f"{min(args.dense_steps, K)} steps each")
+        variants = variant_legs(layer, inputs, ctx_b, ctx_a, budgets, sm, evict,
+                                max(1, min(args.dense_steps, K)), dev, restore)
+        for v in variants.values():
+            v["vs_eager_evicted_page16"] = v["tokens_per_s"] / eager["tokens_per_s"]
+        restore()
+
     prefill = None
     if args.prefill_chunk > 0:
         log(f"prefill append: {args.prefill_chunk}-token chunks")
@@ -660,6 +743,7 @@ def main():
         "eager_evicted": eager,
         "dense_reference": dense,
         "per_q_head_reference": per_head,
+        "variants": variants,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
         "host": platform.node(),
