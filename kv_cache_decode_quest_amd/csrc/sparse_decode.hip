@@ -522,11 +522,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
   // (and never live below): they hold 0; the emitted ones are disjoint
   for (int i = tid; i < pps; i += kTopkThreads)
     if (first + i >= k) split_pages[i] = 0;
-  select_row<true>(sh, s, sv, n, k, n_sink, n_recent, [&](int pos, int j) {
+  auto emit = [&](int pos, int j) {
     if (split == 0) out[pos] = j;
     const unsigned x = (unsigned)(pos - first);
     if (x < (unsigned)pps) split_pages[x] = j;
-  });
+  };
+  if (n_sink > 0 || n_recent > 0) select_row<true, true>(sh, s, sv, n, k, n_sink, n_recent, emit);
+  else select_row<true, false>(sh, s, sv, n, k, 0, 0, emit);
   __syncthreads();
   // any index is clamped into the list
   decode_split<D, P, kPack, kFusedWaves>(

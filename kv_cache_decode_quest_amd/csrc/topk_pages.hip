@@ -35,7 +35,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
   int32_t *out = sel_pages + (int64_t)row * max_k;
   if (tid == 0) num_sel[row] = k;
   for (int i = k + tid; i < max_k; i += kTopkThreads) out[i] = -1;
-  select_row<kRegs>(sh, s, sv, n, k, n_sink, n_recent, [&](int pos, int j) { out[pos] = j; });
+  auto emit = [&](int pos, int j) { out[pos] = j; };
+  if (n_sink > 0 || n_recent > 0) select_row<kRegs, true>(sh, s, sv, n, k, n_sink, n_recent, emit);
+  else select_row<kRegs, false>(sh, s, sv, n, k, 0, 0, emit);
 }
 
 hipError_t launch_topk(const Dims &dm, int batch, const float *scores,

@@ -136,11 +136,6 @@ constexpr int kRegKeys = 8192;
 constexpr int kPerThread = kRegKeys / kTopkThreads;
 constexpr int kRegSpan = kPerThread * kWave;              // pages per wave
 
-// Forced pages (the first n_sink and the last n_recent of a request) take the
-// largest key, above the key of any score but a NaN, so they are kept before
-// every scored page, the lower page first among them.
-constexpr uint32_t kForcedKey = 0xffffffffu;
-
 // k = min(max_k, clamp(floor(budget / P), 1, n)) of the row's n pages (n =
 // 0 and k = 0 for a request with no token); P a power of two.
 __device__ __forceinline__ void row_size(int ctx, int budget, int log2p, int max_pages,
@@ -159,7 +154,10 @@ __device__ __forceinline__ void row_size(int ctx, int budget, int log2p, int max
 // register row (wave w, lane l, slot i holds page kRegSpan w + 64 i + l);
 // n pages, k of them kept (0 <= k <= n).  emit(pos, page) is called once for
 // each kept page with its position pos in [0, k) of the ascending page list.
-template <bool kRegs, typename Emit>
+// kForced: the first n_sink and the last n_recent pages rank above every
+// scored page, the lower page first among them (without, n_sink and
+// n_recent are ignored).
+template <bool kRegs, bool kForced, typename Emit>
 __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restrict__ s,
                                            const float (&sv)[kRegs ? kPerThread : 1], int n,
                                            int k, int n_sink, int n_recent, Emit emit) {
@@ -168,21 +166,37 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     for (int i = tid; i < n; i += kTopkThreads) emit(i, i);
     return;
   }
-  // The thread's keys: registers, or global memory for long rows.  Invalid
-  // slots (past the row) never count; their key is 0.
-  const int recent0 = n - n_recent;                   // first forced recent page
-  auto key_of = [&](float score, int j) -> uint32_t {
-    return (j < n_sink || j >= recent0) ? kForcedKey : order_key(score);
-  };
+  // Forced pages are emitted here; the radix select below runs over the
+  // scored pages [a, b) for the kk places they leave.
+  int a = 0, b = n, kk = k;
+  if constexpr (kForced) {
+    const int ns = min(n_sink, n), nr = min(n_recent, n - ns);
+    a = ns;
+    b = n - nr;
+    if (k <= ns + nr) {                               // only forced pages: the lowest k
+      for (int i = tid; i < k; i += kTopkThreads) emit(i, i < ns ? i : b + (i - ns));
+      return;
+    }
+    kk = k - ns - nr;
+    for (int i = tid; i < ns; i += kTopkThreads) emit(i, i);               // sink pages
+    for (int i = tid; i < nr; i += kTopkThreads) emit(ns + kk + i, b + i); // recent pages
+    if (kk == b - a) {                                // and every scored page
+      for (int i = tid; i < kk; i += kTopkThreads) emit(a + i, a + i);
+      return;
+    }
+  }
+  auto in_row = [&](int j) { return (!kForced || j >= a) && j < b; };
+  // The thread's keys: registers, or global memory for long rows.  Slots
+  // outside the scored range never count; their key is 0.
   uint32_t u[kRegs ? kPerThread : 1];
   if constexpr (kRegs) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int j = wave * kRegSpan + i * kWave + lane;
-      u[i] = j < n ? key_of(sv[i], j) : 0u;
+      u[i] = in_row(j) ? order_key(sv[i]) : 0u;
     }
   }
-  auto valid = [&](int i) { return wave * kRegSpan + i * kWave + lane < n; };
+  auto valid = [&](int i) { return in_row(wave * kRegSpan + i * kWave + lane); };
 
   // 1. min and max key
   uint32_t lo = 0xffffffffu, hi = 0u;
@@ -194,8 +208,8 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
         hi = max(hi, u[i]);
       }
   } else {
-    for (int j = tid; j < n; j += kTopkThreads) {
-      const uint32_t x = key_of(s[j], j);
+    for (int j = a + tid; j < b; j += kTopkThreads) {
+      const uint32_t x = order_key(s[j]);
       lo = min(lo, x);
       hi = max(hi, x);
     }
@@ -212,9 +226,9 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
   __syncthreads();
   minmax_over_waves(sh.wave_a, sh.wave_b, lo, hi);
 
-  uint32_t thresh, krem = (uint32_t)k;
-  if (lo == hi) {                                     // every key equal: the first k pages
-    for (int i = tid; i < k; i += kTopkThreads) emit(i, i);
+  uint32_t thresh, krem = (uint32_t)kk;
+  if (lo == hi) {                                     // every key equal: the lowest kk pages
+    for (int i = tid; i < kk; i += kTopkThreads) emit(a + i, a + i);
     return;
   }
   // 2. refine the threshold key, 11 bits at a time
@@ -238,8 +252,8 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
         if (valid(i) && ((u[i] ^ prefix) & himask) == 0u)
           atomicAdd(&sh.hist[(u[i] >> shift) & bmask], 1u);
     } else {
-      for (int j = tid; j < n; j += kTopkThreads) {
-        const uint32_t x = key_of(s[j], j);
+      for (int j = a + tid; j < b; j += kTopkThreads) {
+        const uint32_t x = order_key(s[j]);
         if (((x ^ prefix) & himask) == 0u) atomicAdd(&sh.hist[(x >> shift) & bmask], 1u);
       }
     }
@@ -278,7 +292,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
       }
       if (lane == 0) sh.cnt_gt[wave] = above;
     } else {
-      for (int j = tid; j < n; j += kTopkThreads) gather(key_of(s[j], j), j);
+      for (int j = a + tid; j < b; j += kTopkThreads) gather(order_key(s[j]), j);
     }
     __syncthreads();
     if (wave == 0) {
@@ -324,12 +338,12 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
       for (int i = 0; i < kPerThread; ++i) {
         const int j = w0 + i * kWave + lane;
         const uint32_t x = u[i];
-        const bool kept = j < n && (x > thresh || (x == thresh && j <= tidx));
+        const bool kept = in_row(j) && (x > thresh || (x == thresh && j <= tidx));
         const uint64_t m = __ballot(kept);
         if (kept) {
           const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos0));
-          if (pos < (uint32_t)k) emit((int)pos, j);   // never past the row
+          if (pos < (uint32_t)kk) emit(a + (int)pos, j);   // never past the row
         }
         pos0 += (uint32_t)__popcll(m);
       }
@@ -352,9 +366,9 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     const int j = w0 + i * kWave + lane;
     uint32_t x;
     if constexpr (kRegs) x = u[i];
-    else x = j < n ? key_of(s[j], j) : 0u;
-    mg = __ballot(j < n && x > thresh);
-    me = __ballot(j < n && x == thresh);
+    else x = in_row(j) ? order_key(s[j]) : 0u;
+    mg = __ballot(in_row(j) && x > thresh);
+    me = __ballot(in_row(j) && x == thresh);
   };
   constexpr int kSaved = kRegs ? kPerThread : 1;
   uint64_t sg[kSaved], se[kSaved];
@@ -395,7 +409,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     const bool is_eq = (me >> lane) & 1ull;
     if (is_gt || (is_eq && eq_before < krem)) {
       const uint32_t pos = gt_before + min(eq_before, krem);
-      if (pos < (uint32_t)k) emit((int)pos, w0 + i * kWave + lane);   // never past the row
+      if (pos < (uint32_t)kk) emit(a + (int)pos, w0 + i * kWave + lane);   // never past the row
     }
     gt_b += (uint32_t)__popcll(mg);
     eq_b += (uint32_t)__popcll(me);
