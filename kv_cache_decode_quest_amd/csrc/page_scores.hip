@@ -197,6 +197,8 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
   }
 }
 
+constexpr int kMaxGroup = 16;       // q heads per KV head the layout allows
+
 // fp32 path: one thread per page, the group's q in LDS.  Each term takes the
 // product on the side the sign of q selects; rounding is monotonic, so this
 // is the larger of the two rounded products.
@@ -221,16 +223,27 @@ __global__ __launch_bounds__(256) void page_scores_valu_kernel(
   if (phys < 0 || phys >= pool) return;
   const float *lo = kmeta + (phys * Hkv + g) * 2 * D;
   const float *hi = lo + D;
-  float v = reduce == 0 ? -__builtin_huge_valf() : 0.f;
-  for (int h = 0; h < G; ++h) {
-    float u = 0.f;
-    for (int d = 0; d < D; ++d) {
-      const float qd = q_lds[h * D + d];
-      u += qd >= 0.f ? qd * hi[d] : qd * lo[d];
+  // each metadata element is read once; every head sums over d in order
+  float u[kMaxGroup];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) u[h] = 0.f;
+  for (int d = 0; d < D; ++d) {
+    const float a = lo[d], b = hi[d];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < G) {
+        const float qd = q_lds[h * D + d];
+        u[h] += qd >= 0.f ? qd * b : qd * a;
+      }
     }
-    if (per_head)
-      scores[((int64_t)(r * Hkv + g) * G + h) * max_pages + j] = u;
-    v = reduce == 0 ? fmaxf(v, u) : v + u;
+  }
+  float v = reduce == 0 ? -__builtin_huge_valf() : 0.f;
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h < G) {
+      if (per_head) scores[((int64_t)(r * Hkv + g) * G + h) * max_pages + j] = u[h];
+      v = reduce == 0 ? fmaxf(v, u[h]) : v + u[h];
+    }
   }
   if (!per_head) scores[((int64_t)r * Hkv + g) * max_pages + j] = v;
 }

@@ -63,7 +63,10 @@ constexpr long kTargetWorkGroups = 1024;
 DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
   DecodePlan p{1, max_k > 0 ? max_k : 1};
   if (batch <= 0 || max_k <= 0) return p;
-  const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
+  // A round: the bf16 kernel's waves take pages_per_wave pages each at once;
+  // the fp32 kernel walks its pages one at a time (each a chain of loads and
+  // barriers), so its splits start at one page.
+  const long per_round = dm.dtype == 1 ? (long)kDecodeWaves * pages_per_wave(dm.P, dm.D) : 1;
   const long rows = (long)batch * dm.R;
   const long want_splits = std::max(1L, (kTargetWorkGroups + rows - 1) / rows);
   long rounds = 1;

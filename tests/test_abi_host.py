@@ -195,11 +195,13 @@ def test_workspace_contract(lib):
 
 def test_plan_covers_every_page():
     """Splits cover max_k pages with no empty split, and never exceed the 256
-    splits a plan may use."""
+    splits a plan may use (bf16 at every page size; fp32, whose splits start
+    at one page)."""
     for batch, hkv, max_k in [(1, 1, 1), (1, 1, 16), (8, 4, 256), (8, 4, 128), (32, 4, 409),
                               (64, 4, 128), (3, 2, 1000), (1, 1, 60000), (2, 4, 4097)]:
-        for page_size in (8, 16, 32, 64):
-            L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8, page_size=page_size)
+        for page_size, dtype in ((8, 1), (16, 1), (32, 1), (64, 1), (16, 0), (32, 0)):
+            L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8, page_size=page_size,
+                       dtype=dtype)
             p = quest.quest_sparse_decode_plan(L, batch, max_k)
             assert p["pages_per_split"] >= 1
             assert 1 <= p["num_splits"] <= 256
