@@ -6,8 +6,8 @@ paged cache (page 16), token budget 4096 (256 pages per KV head).  A step is
 the whole hot path for one new token per request: quest_append_score (KV store
 and min/max refresh fused with the page scores) and quest_topk_sparse_decode
 (the top-k selection and the split-K attention in one kernel at this shape,
-then the merge).  Inputs are seeded synthetic
-tensors already resident in HBM.
+then the merge).  Inputs are seeded synthetic tensors already resident in
+HBM.
 
 Timing: the layer's cache is resident in several copies (own K/V pools and
 metadata per copy, one shared page table, as a model's layers share one block
@@ -19,7 +19,12 @@ W eager warm-up steps, one eager pass over the sequence and one untimed
 replay; a HIP event pair brackets the timed replay.  value = batch * K /
 replay time.  Also reported: the same steps launched eagerly one at a time,
 the cache evicted before each by an untimed 2 GiB read sweep (each step then
-pays its own dispatch latency).
+pays its own dispatch latency); a per-kernel breakdown; the dominant kernel's
+roofline (its launch time over 8 copies of the metadata, and the committed
+counter record of its HBM traffic); the dense decode over every page, the
+per-q-head selection, the SUM / forced-page / page-size variants and the
+prefill-chunk append, each timed like the eager steps; and the CPU oracle on
+a bounded sample of the same workload.
 
 Prints one JSON line.
 """
