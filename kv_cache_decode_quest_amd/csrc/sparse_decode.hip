@@ -177,7 +177,7 @@ __device__ __forceinline__ void load_v_half(PageRegs<D, 16> &pr, const uint16_t 
 template <int D, int P, int NPG, bool kPack>
 __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
                                              const bool *full, int tok0, const bf16x8 *qop,
-                                             float scale2, int col, int grp, float &m, float &l,
+                                             float scale2, int col, float &m, float &l,
                                              f32x4 *acc) {
   using PR = PageRegs<D, P>;
   constexpr float kNegInf = -__builtin_huge_valf();
@@ -420,8 +420,8 @@ __device__ __forceinline__ void decode_split(
     const int tok0 = kHalf ? 4 * (grp & 1) : 4 * grp;
 #pragma unroll
     for (int g0 = 0; g0 < NV; g0 += UPG)
-      attend_round<D, TP, UPG, kPack>(pg + g0, lim + g0, full + g0, tok0, qop, scale2, col, grp,
-                                      m, l, acc);
+      attend_round<D, TP, UPG, kPack>(pg + g0, lim + g0, full + g0, tok0, qop, scale2, col, m,
+                                      l, acc);
   }
 
   // merge the waves of this work-group

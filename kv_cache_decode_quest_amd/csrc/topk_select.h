@@ -373,8 +373,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
   constexpr int kSaved = kRegs ? kPerThread : 1;
   uint64_t sg[kSaved], se[kSaved];
   uint32_t gt_w = 0, eq_w = 0;
-#pragma unroll
-  for (int i = 0; i < iters; ++i) {
+  auto count_pass = [&](int i) {
     uint64_t mg, me;
     masks(i, mg, me);
     if constexpr (kRegs) {
@@ -383,6 +382,13 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     }
     gt_w += (uint32_t)__popcll(mg);
     eq_w += (uint32_t)__popcll(me);
+  };
+  // (loops holding ballots unroll only at a trip count known when compiled)
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) count_pass(i);
+  } else {
+    for (int i = 0; i < iters; ++i) count_pass(i);
   }
   if (lane == 0) {
     sh.cnt_gt[wave] = gt_w;
@@ -391,8 +397,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
   __syncthreads();
   uint32_t gt_b = sum_of_earlier_waves(sh.cnt_gt, wave);
   uint32_t eq_b = sum_of_earlier_waves(sh.cnt_eq, wave);
-#pragma unroll
-  for (int i = 0; i < iters; ++i) {
+  auto write_pass = [&](int i) {
     uint64_t mg, me;
     if constexpr (kRegs) {
       mg = sg[i];
@@ -413,6 +418,12 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     }
     gt_b += (uint32_t)__popcll(mg);
     eq_b += (uint32_t)__popcll(me);
+  };
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) write_pass(i);
+  } else {
+    for (int i = 0; i < iters; ++i) write_pass(i);
   }
 }
 
