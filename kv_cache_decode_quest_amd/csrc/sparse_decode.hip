@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int j = wave * kRegSpan + i * kWave + lane;
-    sv[i] = s[j < max_pages ? j : 0];
+    sv[i] = s[min(j, max_pages - 1)];
   }
   const int ctx = ctx_lens[r];
   int n, k;

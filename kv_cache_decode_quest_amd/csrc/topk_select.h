@@ -48,8 +48,8 @@ static_assert(kBinsPerLane * kTopkThreads == kBins && kTopkWaves <= 16, "bucket 
 // Larger score <-> larger key; -0.0 and +0.0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);
-  if ((u & 0x7fffffffu) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = u == 0x80000000u ? 0u : u;                     // -0.0 -> +0.0
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 struct TopkShared {
@@ -201,12 +201,12 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
   // 1. min and max key
   uint32_t lo = 0xffffffffu, hi = 0u;
   if constexpr (kRegs) {
+    // slots outside the range hold key 0, which never raises hi
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i)
-      if (valid(i)) {
-        lo = min(lo, u[i]);
-        hi = max(hi, u[i]);
-      }
+    for (int i = 0; i < kPerThread; ++i) {
+      lo = min(lo, valid(i) ? u[i] : 0xffffffffu);
+      hi = max(hi, u[i]);
+    }
   } else {
     for (int j = a + tid; j < b; j += kTopkThreads) {
       const uint32_t x = order_key(s[j]);
