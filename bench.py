@@ -272,6 +272,73 @@ def variant_legs(layer, inputs, ctx_b, ctx_a, budgets, sm, evict, n_steps, dev, 
     return out
 
 
+def layers48_step(n_steps, n_copies, evict, dev):
+    """The 48-layer decode step (batch 64 x 32768 tokens, page 16, budget 2048):
+    48 layer-steps per model step, layer l on resident copy l mod n_copies
+    (every layer has the same shape and cost; n_copies x 537 MB of metadata
+    and selected K/V keeps each layer's bytes out of the Infinity Cache),
+    n_steps model steps captured in one HIP graph and replayed back to back.
+    Bytes = metadata + selected valid K/V of every layer-step."""
+    w = workloads.scaled(workloads.WORKLOADS["layers48"], layers=1)
+    n_layers = workloads.WORKLOADS["layers48"].layers
+    base = BenchLayer(w, n_steps, dev)
+    base.prefill = None
+    copies = [base] + [base.resident_copy() for _ in range(n_copies - 1)]
+    sm = workloads.default_sm_scale(w)
+    B, P = w.batch, w.page_size
+    inputs = make_steps(w, n_copies, dev)
+    ctx_b = [(base.ctx0 + s).to(torch.int32) for s in range(n_steps)]
+    ctx_a = [(base.ctx0 + s + 1).to(torch.int32) for s in range(n_steps)]
+    budgets = [workloads.budget_tokens(w, c).to(dev) for c in ctx_a]
+    max_k = max(1, max(int((b // P).max()) for b in budgets))
+    total = n_steps * n_layers
+    per_copy = [quest.alloc_decode_buffers(base.L, B, max_k, dev) for _ in range(n_copies)]
+    sels = torch.empty((total,) + tuple(per_copy[0].sel_pages.shape), dtype=torch.int32,
+                       device=dev)
+    nsels = torch.empty((total,) + tuple(per_copy[0].num_sel.shape), dtype=torch.int32,
+                        device=dev)
+    step_bufs = [dataclasses.replace(per_copy[i % n_copies], sel_pages=sels[i],
+                                     num_sel=nsels[i]) for i in range(total)]
+
+    def layer_step(i):
+        m, c = i // n_layers, (i % n_layers) % n_copies
+        run_step(copies[c], step_bufs[i], i, inputs[c], ctx_b[m], ctx_a[m], budgets[m], sm)
+
+    for i in range(total):
+        layer_step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(total):
+            layer_step(i)
+    graph.replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    evict()
+    torch.cuda.synchronize()
+    ev[0].record()
+    graph.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    total_s = ev[0].elapsed_time(ev[1]) / 1e3
+    meta_b = kv_b = 0
+    for i in range(total):
+        m_, kv = step_bytes(w, ctx_a[i // n_layers], sels[i], nsels[i])
+        meta_b += m_
+        kv_b += kv
+    res = {"what": "48 layer-steps per model step (batch 64 x 32768, page 16, budget 2048), "
+                   f"layer l on resident copy l mod {n_copies}, {n_steps} model steps replayed "
+                   "from one HIP graph",
+           "ms_per_step": total_s / n_steps * 1e3, "tokens_per_s": B * n_steps / total_s,
+           "layers": n_layers, "steps": n_steps, "resident_layer_copies": n_copies,
+           "bytes_per_step": (meta_b + kv_b) / n_steps,
+           "hbm_gbps": (meta_b + kv_b) / total_s / 1e9,
+           "hbm_frac_peak": (meta_b + kv_b) / total_s / 1e9 / PEAK_HBM_GBPS,
+           "one_kernel_topk_decode": quest.quest_topk_sparse_decode_fused(base.L, B, max_k)}
+    del graph, step_bufs, per_copy, copies, base
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_chunk_append(layer, chunk, n_calls, evict, dev):
     """Bulk on_kv_stored at prefill-chunk granularity: each call stores one
     `chunk`-token chunk of every request's prompt (positions c*chunk ..) with
@@ -479,6 +546,9 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=16)
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the per-q-head selection reference")
+    ap.add_argument("--no-layers48", action="store_true",
+                    help="skip the 48-layer batch-64 step")
+    ap.add_argument("--layers48-steps", type=int, default=4)
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the SUM-reduction, forced-page and page-size variants")
     ap.add_argument("--prefill-chunk", type=int, default=4096,
@@ -703,6 +773,11 @@ def main():
         prefill = prefill_chunk_append(layer, args.prefill_chunk, 16, evict, dev)
         restore()
 
+    layers48 = None
+    if not args.no_layers48 and w.name == "bench128k":
+        log("48-layer step: batch 64 x 32768 over 8 resident layers")
+        layers48 = layers48_step(args.layers48_steps, 8, evict, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, (layer.lay,) + layer.prefill, inputs,
@@ -749,6 +824,7 @@ def main():
         "dense_reference": dense,
         "per_q_head_reference": per_head,
         "variants": variants,
+        "layers48_step": layers48,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
         "host": platform.node(),

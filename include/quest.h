@@ -239,16 +239,19 @@ int quest_sparse_decode(const quest_layout *layout, int32_t batch,
 
 /* quest_topk_pages_forced followed by quest_sparse_decode on its selection,
  * in fewer launches where the shape allows (one kernel for the selection and
- * the attention, then the merge).  Arguments as in those two calls; the
- * selection and counts written are exactly those of quest_topk_pages_forced.
- * The outputs equal the two calls' up to the order of the fp32 sums inside a
- * work-group (the fused kernel merges 16 waves of half the pages each): the
- * same tolerance against exact attention holds.  In the fused kernel every
- * split of a row repeats the row's selection, which pays while the grid fits
- * one resident work-group per CU (bf16, rows of at most 8192 pages, D = 64,
- * or D = 128 with 16-token pages, at most 256 work-groups and 256 pages per
- * split); other shapes take the two kernels in sequence.  Errors: those of
- * both calls. */
+ * the attention, then the merge, or no merge when each selection row is
+ * attended by one work-group).  Arguments as in those two calls; the
+ * workspace of quest_sparse_decode_workspace_bytes suffices.  The selection
+ * and counts written are exactly those of quest_topk_pages_forced.  The
+ * outputs equal the two calls' up to the order of the fp32 sums inside a
+ * work-group (the fused kernel merges 16 waves of half the pages each, and
+ * may split a row differently): the same tolerance against exact attention
+ * holds.  In the fused kernel every split of a row repeats the row's
+ * selection, which pays while the grid fits one resident work-group per CU:
+ * bf16, rows of at most 8192 pages, D = 64 or D = 128 with 16-token pages,
+ * and a split of each row into at most 256 / (batch x rows) parts of at most
+ * 256 pages; other shapes take the two kernels in sequence.  Errors: those
+ * of both calls. */
 int quest_topk_sparse_decode(const quest_layout *layout, int32_t batch,
                              const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *page_table, const int32_t *ctx_lens,

@@ -288,14 +288,16 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
 // row's i-th selected page (read for some i past the split or the count,
 // whose value is then ignored); count() the row's selected count, at most
 // max_k; ctx_of(r) request r's length.  Writes the split's partial (acc, m,
-// l) per head.
+// l) per head, or, with final_out (a row of one split), the row's output
+// acc / l in bf16 directly — what the merge would compute from that single
+// partial, bit for bit.
 template <int D, int P, bool kPack, int kWaves, typename Ids, typename Count, typename CtxOf>
 __device__ __forceinline__ void decode_split(
     int row, int split, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages,
     int max_k, int n_split, int pps, float scale2, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
     const int32_t *__restrict__ page_table, CtxOf ctx_of, Ids ids, Count count,
-    float *__restrict__ partial) {
+    float *__restrict__ partial, uint16_t *__restrict__ final_out = nullptr) {
   static_assert(kWaves == kDecodeWaves || kWaves == 2 * kDecodeWaves, "wave count");
   // 8-token pages are attended two to a 16-token tile ("tile page")
   constexpr bool kHalf = P < 16;
@@ -334,6 +336,11 @@ __device__ __forceinline__ void decode_split(
   const int nsel = count();
   const int ctx = ctx_of(r);
   if (first >= nsel) {                             // no page in this split:
+    if (final_out) {                                // a row with no page outputs zeros
+      for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x)
+        Elem<uint16_t>::store(final_out, (int64_t)row * G * D + idx, 0.f);
+      return;
+    }
     float *mine = partial + ((int64_t)row * n_split + split) * G * (D + 2);
     for (int h = threadIdx.x; h < G; h += blockDim.x) {   // an empty partial
       mine[h * (D + 2) + D] = -__builtin_huge_valf();
@@ -448,6 +455,10 @@ __device__ __forceinline__ void decode_split(
       a += f * aw;
       L += f * lds_l[w][h];
     }
+    if (final_out) {
+      Elem<uint16_t>::store(final_out, ((int64_t)row * G + h) * D + d, L > 0.f ? a / L : 0.f);
+      continue;
+    }
     float *ph = out + h * (D + 2);
     ph[d] = a;
     if (d == 0) {
@@ -478,11 +489,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
 // selection itself (1024 threads, the row's scores read from global memory),
 // keeps the page ids of its own split in LDS, then attends them with 16
 // waves of half the pages each (the same pages per round as the 8-wave
-// kernel, so the plan and the partials are the same).  Split 0 also writes
-// the row's selection and count.  The selection is repeated by every split
-// of a row: it pays where the grid fits in one wave of resident work-groups
-// (one per CU at this kernel's LDS size), so the repeats run side by side
-// instead of one launch before the decode.
+// kernel, so the partials have the same form).  Split 0 also writes the
+// row's selection and count.  The selection is repeated by every split of a
+// row: it pays where the grid fits in one wave of resident work-groups (one
+// per CU at this kernel's LDS size), so the repeats run side by side instead
+// of one launch before the decode.  The plan (fused_plan) splits a row only
+// as far as that allows; a row of one split (many rows) writes its output
+// directly, and then no merge runs at all.
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 2 * kDecodeWaves;
 static_assert(kFusedWaves * kWave == kTopkThreads, "the fused kernel runs the 1024-thread selection");
@@ -497,7 +510,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
     const float *__restrict__ scores, const int32_t *__restrict__ budget_tokens,
     int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel,
-    float *__restrict__ partial) {
+    float *__restrict__ partial, uint16_t *__restrict__ out_final) {
   __shared__ TopkShared sh;
   __shared__ int32_t split_pages[kMaxFusedPages];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -541,7 +554,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
         const int x = i - first;
         return split_pages[x < 0 ? 0 : (x < pps ? x : pps - 1)];
       },
-      [&] { return k; }, partial);
+      [&] { return k; }, partial, n_split == 1 ? out_final : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -778,9 +791,26 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
 // work-group leaves each lane (the others spill, and stay two launches).
 static bool fused_shape(int P, int D) { return D == 64 || (D == 128 && P == 16); }
 
+// The fused kernel's plan: as many splits per row as keep the grid within
+// one resident work-group per CU, each a whole number of the decode's rounds.
+// It never has more splits than decode_plan, so the same workspace fits; a
+// row of one split writes its output directly (no merge launch).
+static DecodePlan fused_plan(const Dims &dm, int batch, int max_k) {
+  const long rows = (long)batch * dm.R;
+  const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
+  const long cap = std::max(1L, kFusedMaxWorkGroups / std::max(1L, rows));
+  long pps = (max_k + cap - 1) / cap;
+  pps = (pps + per_round - 1) / per_round * per_round;
+  DecodePlan p;
+  p.pages_per_split = (int)pps;
+  p.n_split = (int)((max_k + pps - 1) / pps);
+  return p;
+}
+
 bool topk_decode_fused(const Dims &dm, int batch, int max_k) {
-  if (dm.dtype != 1 || dm.max_pages > kRegKeys || !fused_shape(dm.P, dm.D)) return false;
-  const DecodePlan p = decode_plan(dm, batch, max_k);
+  if (dm.dtype != 1 || dm.max_pages > kRegKeys || !fused_shape(dm.P, dm.D) || max_k <= 0)
+    return false;
+  const DecodePlan p = fused_plan(dm, batch, max_k);
   return p.pages_per_split <= kMaxFusedPages &&
          (long)batch * dm.R * p.n_split <= kFusedMaxWorkGroups;
 }
@@ -799,7 +829,7 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
     return launch_decode(dm, batch, q, k_cache, v_cache, page_table, ctx_lens, sel_pages,
                          num_sel, max_k, sm_scale, out, workspace, stream);
   }
-  const DecodePlan plan = decode_plan(dm, batch, max_k);
+  const DecodePlan plan = fused_plan(dm, batch, max_k);
   const float scale2 = sm_scale * kLog2e;
   const unsigned blocks = (unsigned)((long)batch * dm.R * plan.n_split);
 #define QUEST_FUSED(DD, PP)                                                               \
@@ -813,7 +843,7 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
                      max_k, plan.n_split, plan.pages_per_split, n_sink, n_recent, scale2,  \
                      (const uint16_t *)q, (const uint16_t *)k_cache,                      \
                      (const uint16_t *)v_cache, page_table, ctx_lens, scores,             \
-                     budget_tokens, sel_pages, num_sel, workspace)
+                     budget_tokens, sel_pages, num_sel, workspace, (uint16_t *)out)
   if (dm.D == 128 && dm.P == 16) QUEST_FUSED(128, 16);
   else if (dm.D == 64 && dm.P == 8) QUEST_FUSED(64, 8);
   else if (dm.D == 64 && dm.P == 16) QUEST_FUSED(64, 16);
@@ -823,7 +853,7 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
 #undef QUEST_FUSED
 #undef QUEST_FUSED_G
   const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || plan.n_split == 1) return err;
   return launch_merge(dm, batch, plan, workspace, out, stream);
 }
 

@@ -259,11 +259,15 @@ def test_topk_sparse_decode_rejections(lib):
 
 def test_topk_sparse_decode_fused_rule(lib):
     """One kernel for bf16 rows of at most 8192 pages, D 64 or (D 128, P 16),
-    at most 256 pages per split and 256 work-groups; two kernels otherwise."""
+    each row split into at most 256 / rows parts (whole rounds of 32 pages at
+    P 16, D 128) of at most 256 pages; two kernels otherwise."""
     bench = layout(num_pool_pages=8 * 8009, max_pages_per_seq=8009)
     assert quest.quest_topk_sparse_decode_fused(bench, 8, 256)          # 32 rows x 8 splits
-    assert not quest.quest_topk_sparse_decode_fused(bench, 9, 256)      # 288 work-groups
-    assert not quest.quest_topk_sparse_decode_fused(layout(selection=1), 8, 256)
+    assert quest.quest_topk_sparse_decode_fused(bench, 9, 256)          # 36 rows x 4 splits of 64
+    assert quest.quest_topk_sparse_decode_fused(bench, 64, 128)         # 256 rows, whole rows
+    assert not quest.quest_topk_sparse_decode_fused(bench, 65, 128)     # 260 rows
+    assert quest.quest_topk_sparse_decode_fused(layout(selection=1), 8, 256)   # 256 q-head rows
+    assert not quest.quest_topk_sparse_decode_fused(layout(selection=1), 8, 257)  # 288 pages
     assert not quest.quest_topk_sparse_decode_fused(layout(page_size=32), 1, 16)
     assert not quest.quest_topk_sparse_decode_fused(layout(page_size=8), 1, 16)
     assert quest.quest_topk_sparse_decode_fused(layout(head_dim=64, page_size=64), 1, 16)

@@ -24,16 +24,36 @@ DEV = torch.device("cuda:0")
 CASES = {name: w for name, w in SMALL.items() if w.dtype == "bf16"}
 CASES["bench128k_b4"] = scaled(WORKLOADS["bench128k"], batch=4, ctx=20000,
                                budget_tokens=2048, steps=1)
+# 64 requests x 4 KV heads = 256 rows: one work-group per row, no merge
+CASES["rows256"] = workloads.Workload("rows256", 64, 32, 4, 128, 16, "bf16",
+                                      ctx_range=(1, 1500), budget_tokens=320, steps=1,
+                                      seed=91, poison=float("nan"))
+# 40 requests: 160 rows, one split each
+CASES["rows160_d64"] = workloads.Workload("rows160_d64", 40, 16, 4, 64, 32, "bf16",
+                                          ctx_range=(0, 3000), budget_tokens=640, steps=1,
+                                          seed=92, permute_pages=True)
+
+
+def pages_per_round(P, D):
+    """Pages an 8-wave decode round takes (the fused kernel's 16 waves take
+    the same): 32 KB of K/V per wave at D 128."""
+    if P < 16:
+        return 2 * pages_per_round(16, D)
+    return 8 * (4 if P * D <= 2048 else (2 if P * D <= 4096 else 1))
 
 
 def expect_fused(w, L, max_k):
     """The documented rule: bf16, rows of at most 8192 pages, D 64 or (D 128,
-    P 16), at most 256 pages per split and 256 work-groups."""
-    plan = quest.quest_sparse_decode_plan(L, w.batch, max_k)
+    P 16), each row split into at most 256 / rows parts of whole rounds, of at
+    most 256 pages."""
     rows = w.batch * quest.selection_rows(L)
+    cap = max(1, 256 // rows)
+    per_round = pages_per_round(w.page_size, w.head_dim)
+    pps = -(-(-(-max_k // cap)) // per_round) * per_round
+    n_split = -(-max_k // pps)
     return (w.dtype == "bf16" and L.max_pages_per_seq <= 8192
             and (w.head_dim == 64 or (w.head_dim == 128 and w.page_size == 16))
-            and plan["pages_per_split"] <= 256 and rows * plan["num_splits"] <= 256)
+            and pps <= 256 and rows * n_split <= 256)
 
 
 def one_bf16_ulp(a, b):
