@@ -519,10 +519,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
   const int r = row / R;
   const int log2p = __builtin_ctz(P);                 // the page size is a power of two
   const float *s = scores + (int64_t)row * max_pages;
+  const int span = reg_span(max_pages);               // pages per wave of a register row
   float sv[kPerThread];                               // the row fits in registers
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int j = wave * kRegSpan + i * kWave + lane;
+    const int j = wave * span + i * kWave + lane;
     sv[i] = s[min(j, max_pages - 1)];
   }
   const int ctx = ctx_lens[r];
@@ -543,8 +544,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
     const unsigned x = (unsigned)(pos - first);
     if (x < (unsigned)pps) split_pages[x] = j;
   };
-  if (n_sink > 0 || n_recent > 0) select_row<true, true>(sh, s, sv, n, k, n_sink, n_recent, emit);
-  else select_row<true, false>(sh, s, sv, n, k, 0, 0, emit);
+  if (n_sink > 0 || n_recent > 0) select_row<true, true>(sh, s, sv, span, n, k, n_sink, n_recent, emit);
+  else select_row<true, false>(sh, s, sv, span, n, k, 0, 0, emit);
   __syncthreads();
   // any index is clamped into the list
   decode_split<D, P, kPack, kFusedWaves>(

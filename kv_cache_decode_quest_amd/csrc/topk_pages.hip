@@ -19,13 +19,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
   const int row = r * R + (int)blockIdx.x;
   const int log2p = __builtin_ctz(P);                 // the page size is a power of two
   const float *s = scores + (int64_t)row * max_pages;
+  const int span = reg_span(max_pages);               // pages per wave of a register row
   // Register rows: the whole score row is loaded in the same round trip as
   // the request's length and budget (entries past the length are ignored).
   float sv[kRegs ? kPerThread : 1];
   if constexpr (kRegs) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int j = wave * kRegSpan + i * kWave + lane;
+      const int j = wave * span + i * kWave + lane;
       sv[i] = s[min(j, max_pages - 1)];
     }
   }
@@ -36,8 +37,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(
   if (tid == 0) num_sel[row] = k;
   for (int i = k + tid; i < max_k; i += kTopkThreads) out[i] = -1;
   auto emit = [&](int pos, int j) { out[pos] = j; };
-  if (n_sink > 0 || n_recent > 0) select_row<kRegs, true>(sh, s, sv, n, k, n_sink, n_recent, emit);
-  else select_row<kRegs, false>(sh, s, sv, n, k, 0, 0, emit);
+  if (n_sink > 0 || n_recent > 0) select_row<kRegs, true>(sh, s, sv, span, n, k, n_sink, n_recent, emit);
+  else select_row<kRegs, false>(sh, s, sv, span, n, k, 0, 0, emit);
 }
 
 hipError_t launch_topk(const Dims &dm, int batch, const float *scores,

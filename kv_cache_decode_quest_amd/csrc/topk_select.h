@@ -129,12 +129,18 @@ __device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t k
 }
 
 // Rows of up to kRegKeys pages are read from HBM once, into registers: wave w
-// holds pages [S w, S w + S) with S = kRegSpan, lane l pages S w + 64 i + l
-// (i < kPerThread), the same wave-contiguous order the output pass needs, so
-// no pass re-reads memory.  Longer rows read their scores from global memory in every pass.
+// holds pages [S w, S w + S) with S = reg_span(max_pages), lane l pages
+// S w + 64 i + l (i < S / 64), the same wave-contiguous order the output pass
+// needs, so no pass re-reads memory.  S spreads the row's stride over all
+// waves in whole 64-page slots, so short rows keep every wave busy.  Longer
+// rows read their scores from global memory in every pass.
 constexpr int kRegKeys = 8192;
 constexpr int kPerThread = kRegKeys / kTopkThreads;
-constexpr int kRegSpan = kPerThread * kWave;              // pages per wave
+
+__host__ __device__ constexpr int reg_span(int max_pages) {
+  const int slots = ((max_pages + kTopkWaves - 1) / kTopkWaves + kWave - 1) / kWave;
+  return (slots < kPerThread ? (slots > 0 ? slots : 1) : kPerThread) * kWave;
+}
 
 // k = min(max_k, clamp(floor(budget / P), 1, n)) of the row's n pages (n =
 // 0 and k = 0 for a request with no token); P a power of two.
@@ -151,7 +157,8 @@ __device__ __forceinline__ void row_size(int ctx, int budget, int log2p, int max
 
 // The selection of one row by a kTopkThreads work-group; every thread calls
 // it.  s: the row's scores in global memory; sv: this thread's scores of a
-// register row (wave w, lane l, slot i holds page kRegSpan w + 64 i + l);
+// register row (wave w, lane l, slot i holds page span w + 64 i + l for
+// i < span / 64; span = reg_span(row stride));
 // n pages, k of them kept (0 <= k <= n).  emit(pos, page) is called once for
 // each kept page with its position pos in [0, k) of the ascending page list.
 // kForced: the first n_sink and the last n_recent pages rank above every
@@ -159,8 +166,8 @@ __device__ __forceinline__ void row_size(int ctx, int budget, int log2p, int max
 // n_recent are ignored).
 template <bool kRegs, bool kForced, typename Emit>
 __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restrict__ s,
-                                           const float (&sv)[kRegs ? kPerThread : 1], int n,
-                                           int k, int n_sink, int n_recent, Emit emit) {
+                                           const float (&sv)[kRegs ? kPerThread : 1], int span,
+                                           int n, int k, int n_sink, int n_recent, Emit emit) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   if (k == n) {                                       // the whole row (or nothing)
     for (int i = tid; i < n; i += kTopkThreads) emit(i, i);
@@ -186,17 +193,20 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     }
   }
   auto in_row = [&](int j) { return (!kForced || j >= a) && j < b; };
+  // The page of register slot i (slots past the span hold none: -1).
+  const int nslots = span / kWave;
+  auto slot_page = [&](int i) { return i < nslots ? wave * span + i * kWave + lane : -1; };
   // The thread's keys: registers, or global memory for long rows.  Slots
   // outside the scored range never count; their key is 0.
   uint32_t u[kRegs ? kPerThread : 1];
   if constexpr (kRegs) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int j = wave * kRegSpan + i * kWave + lane;
-      u[i] = in_row(j) ? order_key(sv[i]) : 0u;
+      const int j = slot_page(i);
+      u[i] = j >= 0 && in_row(j) ? order_key(sv[i]) : 0u;
     }
   }
-  auto valid = [&](int i) { return in_row(wave * kRegSpan + i * kWave + lane); };
+  auto valid = [&](int i) { const int j = slot_page(i); return j >= 0 && in_row(j); };
 
   // 1. min and max key
   uint32_t lo = 0xffffffffu, hi = 0u;
@@ -287,7 +297,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
       uint32_t above = 0;
 #pragma unroll
       for (int i = 0; i < kPerThread; ++i) {
-        if (valid(i)) gather(u[i], wave * kRegSpan + i * kWave + lane);
+        if (valid(i)) gather(u[i], slot_page(i));
         above += (uint32_t)__popcll(__ballot(valid(i) && u[i] > bucket_top));
       }
       if (lane == 0) sh.cnt_gt[wave] = above;
@@ -327,7 +337,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
       // the kept pages of earlier waves = their keys above the bucket plus
       // the kept candidates at a lower page than this wave's range.
       const int32_t tidx = (int32_t)sh.tidx;
-      const int w0 = wave * kRegSpan;
+      const int w0 = wave * span;
       const bool cmine = (uint32_t)lane < count;
       const uint32_t ck = cmine ? sh.cand_key[lane] : 0u;
       const int32_t ci = cmine ? sh.cand_idx[lane] : 0;
@@ -336,9 +346,9 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
                       (uint32_t)__popcll(__ballot(ckept && ci < w0));
 #pragma unroll
       for (int i = 0; i < kPerThread; ++i) {
-        const int j = w0 + i * kWave + lane;
+        const int j = slot_page(i);
         const uint32_t x = u[i];
-        const bool kept = in_row(j) && (x > thresh || (x == thresh && j <= tidx));
+        const bool kept = valid(i) && (x > thresh || (x == thresh && j <= tidx));
         const uint64_t m = __ballot(kept);
         if (kept) {
           const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -359,16 +369,18 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
   // page at its position, with lane prefixes of the ballot masks from
   // v_mbcnt.  Register rows keep the masks from the first pass; long rows
   // recompute them.
-  const int span = kRegs ? kRegSpan : ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
-  const int w0 = wave * span;
-  const int iters = kRegs ? kPerThread : span / kWave;
+  const int wspan = kRegs ? span : ((n + kTopkThreads - 1) / kTopkThreads) * kWave;
+  const int w0 = wave * wspan;
+  const int iters = kRegs ? kPerThread : wspan / kWave;
+  auto page_of = [&](int i) { return kRegs ? slot_page(i) : w0 + i * kWave + lane; };
   auto masks = [&](int i, uint64_t &mg, uint64_t &me) {
-    const int j = w0 + i * kWave + lane;
+    const int j = page_of(i);
+    const bool live = j >= 0 && in_row(j);
     uint32_t x;
     if constexpr (kRegs) x = u[i];
-    else x = in_row(j) ? order_key(s[j]) : 0u;
-    mg = __ballot(in_row(j) && x > thresh);
-    me = __ballot(in_row(j) && x == thresh);
+    else x = live ? order_key(s[j]) : 0u;
+    mg = __ballot(live && x > thresh);
+    me = __ballot(live && x == thresh);
   };
   constexpr int kSaved = kRegs ? kPerThread : 1;
   uint64_t sg[kSaved], se[kSaved];
@@ -414,7 +426,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     const bool is_eq = (me >> lane) & 1ull;
     if (is_gt || (is_eq && eq_before < krem)) {
       const uint32_t pos = gt_before + min(eq_before, krem);
-      if (pos < (uint32_t)kk) emit(a + (int)pos, w0 + i * kWave + lane);   // never past the row
+      if (pos < (uint32_t)kk) emit(a + (int)pos, page_of(i));   // never past the row
     }
     gt_b += (uint32_t)__popcll(mg);
     eq_b += (uint32_t)__popcll(me);
