@@ -42,6 +42,24 @@ constexpr int kDecodeWaves = 8;
 constexpr int kMaxSplits = 256;        // per (request, KV head); bounds the partials
 constexpr float kLog2e = 1.4426950408889634f;
 
+// XCDs of an MI355X.  With a grid of a multiple of kXcds work-groups,
+// work-group b runs on XCD b mod kXcds; xcd_major numbers the work items so
+// that consecutive items share an XCD (item = XCD x grid/kXcds + b/kXcds).
+constexpr unsigned kXcds = 8;
+__device__ __forceinline__ int xcd_major(unsigned b, unsigned grid) {
+  return (int)((b % kXcds) * (grid / kXcds) + b / kXcds);
+}
+// Whether a decode grid of `blocks` work-groups (n_split per row) and its
+// merge grid of `mblocks` can be numbered XCD-major with every row's splits
+// and merge on one XCD.  Used by the fused kernel only, whose grid is one
+// wave of work-groups (0.3 us per step at batch 8 x 128000); the standalone
+// decode's multi-wave grids ran slower numbered this way (the dense
+// reference 509 against 389 us), so they keep the plain order.
+static bool xcd_placement(unsigned blocks, int n_split, unsigned mblocks) {
+  return n_split > 1 && blocks % kXcds == 0 && (blocks / kXcds) % (unsigned)n_split == 0 &&
+         mblocks % kXcds == 0;
+}
+
 // Pages one wave loads at once (one round): 32 KB of K and V per wave in
 // flight at D = 128 (4 pages of 16 tokens, 2 of 32, 1 of 64), so the page
 // registers stay within budget.
@@ -510,12 +528,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
     const float *__restrict__ scores, const int32_t *__restrict__ budget_tokens,
     int32_t *__restrict__ sel_pages, int32_t *__restrict__ num_sel,
-    float *__restrict__ partial, uint16_t *__restrict__ out_final) {
+    float *__restrict__ partial, uint16_t *__restrict__ out_final, int xcd_rows) {
   __shared__ TopkShared sh;
   __shared__ int32_t split_pages[kMaxFusedPages];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int split = blockIdx.x % n_split;
-  const int row = blockIdx.x / n_split;
+  const int lin = xcd_rows ? xcd_major(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int split = lin % n_split;
+  const int row = lin / n_split;
   const int r = row / R;
   const int log2p = __builtin_ctz(P);                 // the page size is a power of two
   const float *s = scores + (int64_t)row * max_pages;
@@ -685,8 +704,9 @@ constexpr int kMergeChunk = 16;
 template <typename T>
 __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_split,
                                                     const float *__restrict__ partial,
-                                                    T *__restrict__ out) {
-  const int hq = blockIdx.x;                 // r * Hq + h
+                                                    T *__restrict__ out, int xcd_rows) {
+  // r * Hq + h
+  const int hq = xcd_rows ? xcd_major(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int Hq = R * G;
   const int r = hq / Hq, h = hq - r * Hq;
   const int g = h / G, hl = h - g * G;
@@ -730,14 +750,15 @@ __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_s
 }
 
 static hipError_t launch_merge(const Dims &dm, int batch, const DecodePlan &plan,
-                               const float *workspace, void *out, hipStream_t stream) {
+                               const float *workspace, void *out, hipStream_t stream,
+                               int xcd_rows = 0) {
   const unsigned mblocks = (unsigned)((long)batch * dm.Hq);
   if (dm.dtype == 1)
     hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, workspace, (uint16_t *)out);
+                       dm.Gcols, dm.D, plan.n_split, workspace, (uint16_t *)out, xcd_rows);
   else
     hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, workspace, (float *)out);
+                       dm.Gcols, dm.D, plan.n_split, workspace, (float *)out, xcd_rows);
   return hipGetLastError();
 }
 
@@ -833,6 +854,13 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
   const DecodePlan plan = fused_plan(dm, batch, max_k);
   const float scale2 = sm_scale * kLog2e;
   const unsigned blocks = (unsigned)((long)batch * dm.R * plan.n_split);
+  const unsigned mblocks = (unsigned)((long)batch * dm.Hq);
+  // XCD placement (a performance choice only; results do not depend on where
+  // a work-group runs): the dispatcher deals work-groups to the 8 XCDs in
+  // turn, so work-group b runs on XCD b mod 8.  Numbering the work items
+  // XCD-major keeps the splits of a row, and the merge of its heads, on one
+  // XCD, where the score row and the partials stay in that XCD's L2.
+  const int xcd_rows = xcd_placement(blocks, plan.n_split, mblocks);
 #define QUEST_FUSED(DD, PP)                                                               \
   do {                                                                                    \
     if (dm.Gcols <= 8) QUEST_FUSED_G(DD, PP, true);                                       \
@@ -844,7 +872,7 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
                      max_k, plan.n_split, plan.pages_per_split, n_sink, n_recent, scale2,  \
                      (const uint16_t *)q, (const uint16_t *)k_cache,                      \
                      (const uint16_t *)v_cache, page_table, ctx_lens, scores,             \
-                     budget_tokens, sel_pages, num_sel, workspace, (uint16_t *)out)
+                     budget_tokens, sel_pages, num_sel, workspace, (uint16_t *)out, xcd_rows)
   if (dm.D == 128 && dm.P == 16) QUEST_FUSED(128, 16);
   else if (dm.D == 64 && dm.P == 8) QUEST_FUSED(64, 8);
   else if (dm.D == 64 && dm.P == 16) QUEST_FUSED(64, 16);
@@ -855,7 +883,7 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
 #undef QUEST_FUSED_G
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.n_split == 1) return err;
-  return launch_merge(dm, batch, plan, workspace, out, stream);
+  return launch_merge(dm, batch, plan, workspace, out, stream, xcd_rows);
 }
 
 }  // namespace quest
