@@ -267,6 +267,24 @@ int quest_topk_sparse_decode(const quest_layout *layout, int32_t batch,
 int quest_topk_sparse_decode_fused(const quest_layout *layout, int32_t batch,
                                    int32_t max_k);
 
+/* The whole decode step of one layer in one call: quest_append_score (the
+ * new tokens' store and page bounds, then the page scores; "add-sparse-method",
+ * Placement Rules 2-4: on_kv_stored, then build_decode_view from the current
+ * q) followed by quest_topk_sparse_decode on those scores (the selection
+ * within the budget and attention over the explicit-KV view, SparseEngine
+ * digest, Method key points).  Arguments as in those two calls; ctx_lens must
+ * equal ctx_before plus each request's new tokens.  Results equal the two
+ * calls' bit for bit.  Errors: those of both calls. */
+int quest_decode_step(const quest_layout *layout, int32_t batch, const void *q,
+                      const void *k_new, const void *v_new, const int32_t *cu_new,
+                      const int32_t *ctx_before, int32_t max_new_per_seq,
+                      const int32_t *page_table, void *k_cache, void *v_cache, void *kmeta,
+                      int32_t group_reduce, const int32_t *ctx_lens,
+                      const int32_t *budget_tokens, int32_t max_k, int32_t n_sink,
+                      int32_t n_recent, float sm_scale, float *scores, int32_t *sel_pages,
+                      int32_t *num_sel, void *out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 /* Launch plan quest_sparse_decode uses (for reports): number of KV splits per
  * (request, selection row) and pages per split.  Never calls HIP. */
 int quest_sparse_decode_plan(const quest_layout *layout, int32_t batch,

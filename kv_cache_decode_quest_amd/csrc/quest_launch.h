@@ -74,4 +74,16 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
                               int32_t *num_sel, void *out, float *workspace,
                               hipStream_t stream);
 
+// The whole decode step: launch_append_scores, then launch_topk_decode on
+// its scores.
+hipError_t launch_decode_step(const Dims &dm, int batch, const void *q, const void *k_new,
+                              const void *v_new, const int32_t *cu_new,
+                              const int32_t *ctx_before, int max_new,
+                              const int32_t *page_table, void *k_cache, void *v_cache,
+                              void *kmeta, int reduce, const int32_t *ctx_lens,
+                              const int32_t *budget_tokens, int max_k, int n_sink,
+                              int n_recent, float sm_scale, float *scores,
+                              int32_t *sel_pages, int32_t *num_sel, void *out,
+                              float *workspace, hipStream_t stream);
+
 }  // namespace quest

@@ -886,4 +886,22 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
   return launch_merge(dm, batch, plan, workspace, out, stream, xcd_rows);
 }
 
+hipError_t launch_decode_step(const Dims &dm, int batch, const void *q, const void *k_new,
+                              const void *v_new, const int32_t *cu_new,
+                              const int32_t *ctx_before, int max_new,
+                              const int32_t *page_table, void *k_cache, void *v_cache,
+                              void *kmeta, int reduce, const int32_t *ctx_lens,
+                              const int32_t *budget_tokens, int max_k, int n_sink,
+                              int n_recent, float sm_scale, float *scores,
+                              int32_t *sel_pages, int32_t *num_sel, void *out,
+                              float *workspace, hipStream_t stream) {
+  const hipError_t err = launch_append_scores(dm, batch, q, k_new, v_new, cu_new, ctx_before,
+                                              max_new, page_table, k_cache, v_cache, kmeta,
+                                              reduce, scores, stream);
+  if (err != hipSuccess) return err;
+  return launch_topk_decode(dm, batch, q, k_cache, v_cache, page_table, ctx_lens, scores,
+                            budget_tokens, max_k, n_sink, n_recent, sm_scale, sel_pages,
+                            num_sel, out, workspace, stream);
+}
+
 }  // namespace quest

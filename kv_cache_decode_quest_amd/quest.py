@@ -26,7 +26,7 @@ QUEST_SELECT_PER_KV_HEAD, QUEST_SELECT_PER_Q_HEAD = 0, 1
 EXPORTS = ("quest_abi_version", "quest_status_string", "quest_append_kv", "quest_page_scores",
            "quest_append_score", "quest_topk_pages", "quest_topk_pages_forced",
            "quest_sparse_decode_workspace_bytes", "quest_sparse_decode", "quest_sparse_decode_plan",
-           "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused")
+           "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused", "quest_decode_step")
 
 
 class QuestError(RuntimeError):
@@ -80,9 +80,12 @@ def load(path: str = LIB_PATH):
     L.quest_topk_sparse_decode.argtypes = [lp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                            f32, vp, vp, vp, vp, sz, vp]
     L.quest_topk_sparse_decode_fused.argtypes = [lp, i32, i32]
+    L.quest_decode_step.argtypes = [lp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp,
+                                    i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     for name in ("quest_append_kv", "quest_page_scores", "quest_append_score", "quest_topk_pages",
                  "quest_topk_pages_forced", "quest_sparse_decode", "quest_sparse_decode_plan",
-                 "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused"):
+                 "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused",
+                 "quest_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     if L.quest_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libquest ABI {L.quest_abi_version()} != binding ABI {ABI_VERSION}")
@@ -334,6 +337,46 @@ def quest_topk_sparse_decode_fused(L: QuestLayout, batch: int, max_k: int) -> bo
     return st == 1
 
 
+def quest_decode_step(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq,
+                      page_table, k_cache, v_cache, kmeta, ctx_lens, budget_tokens, max_k,
+                      sm_scale, scores, sel_pages, num_sel, out, workspace, group_reduce="max",
+                      n_sink=0, n_recent=0):
+    """The whole decode step of one layer in one call: quest_append_score,
+    then quest_topk_sparse_decode on its scores."""
+    dt, dev = _layout_dtype(L), q.device
+    batch = ctx_before.shape[0]
+    kshape, vshape, mshape = _pool_shapes(L)
+    rows = selection_rows(L)
+    _check(q, "q", dt, (batch, L.num_q_heads, L.head_dim), dev)
+    _check(k_cache, "k_cache", dt, kshape, dev)
+    _check(v_cache, "v_cache", dt, vshape, dev)
+    _check(kmeta, "kmeta", dt, mshape, dev)
+    T = k_new.shape[0]
+    _check(k_new, "k_new", dt, (T, L.num_kv_heads, L.head_dim), dev)
+    _check(v_new, "v_new", dt, (T, L.num_kv_heads, L.head_dim), dev)
+    _check(cu_new, "cu_new", torch.int32, (batch + 1,), dev)
+    _check(ctx_before, "ctx_before", torch.int32, (batch,), dev)
+    _check(ctx_lens, "ctx_lens", torch.int32, (batch,), dev)
+    _check(page_table, "page_table", torch.int32, (batch, L.max_pages_per_seq), dev)
+    _check(budget_tokens, "budget_tokens", torch.int32, (batch,), dev)
+    _check(scores, "scores", torch.float32, (batch, rows, L.max_pages_per_seq), dev)
+    _check(sel_pages, "sel_pages", torch.int32, (batch, rows, max_k), dev)
+    _check(num_sel, "num_sel", torch.int32, (batch, rows), dev)
+    _check(out, "out", dt, (batch, L.num_q_heads, L.head_dim), dev)
+    _check(workspace, "workspace", None, None, dev)
+    if T == 0:                       # nothing to store
+        k_new = v_new = torch.empty((1, L.num_kv_heads, L.head_dim), dtype=dt, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load().quest_decode_step(ctypes.byref(L), batch, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                  _ptr(cu_new), _ptr(ctx_before), int(max_new_per_seq),
+                                  _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _ptr(kmeta),
+                                  REDUCE[group_reduce], _ptr(ctx_lens), _ptr(budget_tokens),
+                                  int(max_k), int(n_sink), int(n_recent), float(sm_scale),
+                                  _ptr(scores), _ptr(sel_pages), _ptr(num_sel), _ptr(out),
+                                  _ptr(workspace), nbytes, _stream(dev))
+    _raise("quest_decode_step", st)
+
+
 @dataclass
 class DecodeBuffers:
     """Caller-owned per-step buffers for one layer (scores, selection, output)."""
@@ -364,11 +407,10 @@ def decode_step(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, ctx_lens, b
                 group_reduce="max", max_new_per_seq=1):
     """One Quest decode step of one layer: on_kv_stored fused with the page
     scores, then the top-k (the rest of build_decode_view) and attention over
-    the view.  Two ABI calls, both asynchronous on the current stream;
+    the view, through quest_decode_step (asynchronous on the current stream);
     ctx_lens must equal ctx_before + the new tokens."""
-    quest_append_score(L, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq, page_table,
-                       k_cache, v_cache, kmeta, bufs.scores, group_reduce)
-    quest_topk_sparse_decode(L, q, k_cache, v_cache, page_table, ctx_lens, bufs.scores,
-                             budget_tokens, bufs.max_k, sm_scale, bufs.sel_pages, bufs.num_sel,
-                             bufs.out, bufs.workspace)
+    quest_decode_step(L, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq, page_table,
+                      k_cache, v_cache, kmeta, ctx_lens, budget_tokens, bufs.max_k, sm_scale,
+                      bufs.scores, bufs.sel_pages, bufs.num_sel, bufs.out, bufs.workspace,
+                      group_reduce)
     return bufs.out

@@ -279,3 +279,31 @@ def test_topk_sparse_decode_fused_rule(lib):
     assert quest.quest_topk_sparse_decode_fused(big, 1, 8000)           # 250 splits of 32
     assert not quest.quest_topk_sparse_decode_fused(big, 1, 100000)     # 256 splits of 416
     assert lib.quest_topk_sparse_decode_fused(ctypes.byref(layout()), 1, 0) == ERR_SHAPE
+
+
+def step_call(lib, L, batch=1, max_k=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, k_new=FAKE,
+              ctx_lens=FAKE, reduce=0, max_new=1, scale=0.1, n_sink=0):
+    return lib.quest_decode_step(ctypes.byref(L), batch, q, k_new, FAKE, FAKE, FAKE, max_new,
+                                 FAKE, FAKE, FAKE, FAKE, reduce, ctx_lens, FAKE, max_k, n_sink,
+                                 0, scale, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_decode_step_rejections(lib):
+    """The one-call step validates like quest_append_score and
+    quest_topk_sparse_decode together, before any launch."""
+    L = layout()
+    assert step_call(lib, L, q=None) == ERR_NULL
+    assert step_call(lib, L, k_new=None) == ERR_NULL
+    assert step_call(lib, L, ctx_lens=None) == ERR_NULL
+    assert step_call(lib, L, reduce=2) == ERR_UNSUPPORTED
+    assert step_call(lib, L, max_new=-1) == ERR_SHAPE
+    assert step_call(lib, L, max_k=0) == ERR_SHAPE
+    assert step_call(lib, L, n_sink=-1) == ERR_SHAPE
+    assert step_call(lib, L, scale=float("inf")) == ERR_SHAPE
+    assert step_call(lib, L, q=ctypes.c_void_p(0x100002)) == ERR_SHAPE
+    need = lib.quest_sparse_decode_workspace_bytes(ctypes.byref(L), 1, 16)
+    assert step_call(lib, L, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert step_call(lib, L, ws=None) == ERR_WORKSPACE
+    assert step_call(lib, layout(page_size=48)) == ERR_UNSUPPORTED
+    assert step_call(lib, layout(abi_version=2)) == ERR_ABI
+    assert step_call(lib, L, batch=0, q=None, k_new=None, ctx_lens=None, ws=None) == OK
