@@ -23,8 +23,11 @@ pays its own dispatch latency); a per-kernel breakdown; the dominant kernel's
 roofline (its launch time over 8 copies of the metadata, and the committed
 counter record of its HBM traffic); the dense decode over every page, the
 per-q-head selection, the SUM / forced-page / page-size variants and the
-prefill-chunk append, each timed like the eager steps; and the CPU oracle on
-a bounded sample of the same workload.
+prefill-chunk append, each timed like the eager steps; the 48-layer batch-64
+step; one step each of the other single-layer workloads (the tiny fp32
+request, the 32k-context layer, the ragged batch), each on a cache of its
+own and timed like the eager steps; and the CPU oracle on a bounded sample
+of the same workload.
 
 Prints one JSON line.
 """
@@ -388,6 +391,52 @@ def prefill_chunk_append(layer, chunk, n_calls, evict, dev):
             "hbm_gbps": nbytes / total_s / 1e9, "hbm_frac_peak": nbytes / total_s / 1e9 / PEAK_HBM_GBPS}
 
 
+def config_legs(names, n_steps, evict, dev, warm=2):
+    """One decode step (append + scores, then the combined top-k + decode
+    call) of each named workload on a cache of its own, after `warm`
+    untimed steps: the Infinity Cache evicted before each timed step, one
+    event pair per step; tokens/s, and HBM rate over metadata + selected
+    valid K/V."""
+    out = {}
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        layer = BenchLayer(w, warm + n_steps, dev)
+        inputs = make_steps(w, warm + n_steps, dev)
+        ctx_b = [(layer.ctx0 + s).to(torch.int32) for s in range(warm + n_steps)]
+        ctx_a = [(layer.ctx0 + s + 1).to(torch.int32) for s in range(warm + n_steps)]
+        budgets = [workloads.budget_tokens(w, c).to(dev) for c in ctx_a]
+        max_k = max(1, max(int((b // w.page_size).max()) for b in budgets))
+        bufs = quest.alloc_decode_buffers(layer.L, w.batch, max_k, dev)
+        sm = workloads.default_sm_scale(w)
+        for s in range(warm):
+            run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+        total_s, meta_b, kv_b = 0.0, 0, 0
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for s in range(warm, warm + n_steps):
+            evict()
+            ev[0].record()
+            run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
+            ev[1].record()
+            torch.cuda.synchronize()
+            total_s += ev[0].elapsed_time(ev[1]) / 1e3
+            m, kv = step_bytes(w, ctx_a[s], bufs.sel_pages, bufs.num_sel)
+            meta_b += m
+            kv_b += kv
+        gbps = (meta_b + kv_b) / total_s / 1e9
+        ctx = workloads.context_lengths(w)
+        out[name] = {"batch": w.batch, "ctx": [int(ctx.min()), int(ctx.max())],
+                     "page_size": w.page_size, "dtype": w.dtype, "max_k": max_k,
+                     "steps": n_steps, "us_per_step": total_s / n_steps * 1e6,
+                     "tokens_per_s": w.batch * n_steps / total_s,
+                     "bytes_per_step": (meta_b + kv_b) / n_steps,
+                     "hbm_gbps": gbps, "hbm_frac_peak": gbps / PEAK_HBM_GBPS,
+                     "one_kernel_topk_decode": quest.quest_topk_sparse_decode_fused(
+                         layer.L, w.batch, max_k)}
+        del layer, bufs, inputs
+        torch.cuda.empty_cache()
+    return out
+
+
 def step_bytes(w, ctx_after, sel, nsel):
     """Algorithmic HBM bytes of one step: every live page's metadata row plus
     the valid tokens of every selected page (K and V)."""
@@ -537,6 +586,9 @@ def main():
     ap.add_argument("--workload", default="bench128k", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--flush-mib", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip one timed step of each other single-layer workload")
+    ap.add_argument("--config-steps", type=int, default=4)
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=24)
     ap.add_argument("--resident-layers", type=int, default=8,
@@ -778,6 +830,12 @@ def main():
         log("48-layer step: batch 64 x 32768 over 8 resident layers")
         layers48 = layers48_step(args.layers48_steps, 8, evict, dev)
 
+    configs = None
+    if not args.no_configs and w.name == "bench128k":
+        names = ["tiny", "layer32k", "ragged"]
+        log(f"other workloads: {', '.join(names)}, {args.config_steps} timed steps each")
+        configs = config_legs(names, args.config_steps, evict, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, (layer.lay,) + layer.prefill, inputs,
@@ -825,6 +883,7 @@ def main():
         "per_q_head_reference": per_head,
         "variants": variants,
         "layers48_step": layers48,
+        "other_workloads": configs,
         "prefill_append": prefill,
         "cpu_baseline": cpu,
         "host": platform.node(),
