@@ -267,6 +267,16 @@ int quest_topk_sparse_decode(const quest_layout *layout, int32_t batch,
 int quest_topk_sparse_decode_fused(const quest_layout *layout, int32_t batch,
                                    int32_t max_k);
 
+/* The launch plan quest_topk_sparse_decode uses (for reports and tests):
+ * *fused = 1 for the fused kernel (then *num_splits and *pages_per_split are
+ * its plan), 0 for the two kernels (then they are quest_sparse_decode_plan's).
+ * The fused plan never has more splits than quest_sparse_decode_plan's, so
+ * the workspace of quest_sparse_decode_workspace_bytes always suffices.
+ * Never calls HIP; QUEST_ERR_NULL for a NULL output pointer. */
+int quest_topk_sparse_decode_plan(const quest_layout *layout, int32_t batch,
+                                  int32_t max_k, int32_t *fused, int32_t *num_splits,
+                                  int32_t *pages_per_split);
+
 /* The whole decode step of one layer in one call: quest_append_score (the
  * new tokens' store and page bounds, then the page scores; "add-sparse-method",
  * Placement Rules 2-4: on_kv_stored, then build_decode_view from the current

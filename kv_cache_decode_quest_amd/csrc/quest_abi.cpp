@@ -297,4 +297,22 @@ int quest_topk_sparse_decode_fused(const quest_layout *layout, int32_t batch, in
   return batch > 0 && quest::topk_decode_fused(dm, batch, max_k) ? 1 : 0;
 }
 
+int quest_topk_sparse_decode_plan(const quest_layout *layout, int32_t batch, int32_t max_k,
+                                  int32_t *fused, int32_t *num_splits,
+                                  int32_t *pages_per_split) {
+  Dims dm;
+  int st = check_layout(layout, dm);
+  if (st != QUEST_OK) return st;
+  if ((st = check_batch(batch, dm)) != QUEST_OK) return st;
+  if (max_k <= 0) return QUEST_ERR_SHAPE;
+  if (!fused || !num_splits || !pages_per_split) return QUEST_ERR_NULL;
+  const bool one = batch > 0 && quest::topk_decode_fused(dm, batch, max_k);
+  const quest::DecodePlan p =
+      one ? quest::fused_plan(dm, batch, max_k) : quest::decode_plan(dm, batch, max_k);
+  *fused = one ? 1 : 0;
+  *num_splits = p.n_split;
+  *pages_per_split = p.pages_per_split;
+  return QUEST_OK;
+}
+
 }  // extern "C"

@@ -6,20 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
-namespace quest {
+#include "quest_plan.h"
 
-struct Dims {
-  int Hq, Hkv, G, D, P;
-  int dtype;          // 0 fp32, 1 bf16
-  int64_t pool;       // physical pages
-  int max_pages;      // page-table row stride
-  // Selection rows: a request has R rows of scores / selections, row x holds
-  // q heads x*Gcols .. x*Gcols+Gcols-1 and reads KV head x / gdiv.  Shared
-  // per KV head: R = Hkv, Gcols = G, gdiv = 1; per q head: R = Hq, Gcols = 1,
-  // gdiv = G.
-  int R, Gcols, gdiv;
-  bool per_head() const { return R != Hkv || Gcols != G; }
-};
+namespace quest {
 
 hipError_t launch_append(const Dims &dm, int batch, const void *k_new,
                          const void *v_new, const int32_t *cu_new,
@@ -46,15 +35,6 @@ hipError_t launch_topk(const Dims &dm, int batch, const float *scores,
                        int max_k, int n_sink, int n_recent, int32_t *sel_pages,
                        int32_t *num_sel, hipStream_t stream);
 
-struct DecodePlan {
-  int n_split;          // splits per (request, KV head)
-  int pages_per_split;  // selected pages one work-group attends
-};
-
-// Pure host arithmetic; no HIP call.
-DecodePlan decode_plan(const Dims &dm, int batch, int max_k);
-size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k);
-
 hipError_t launch_decode(const Dims &dm, int batch, const void *q,
                          const void *k_cache, const void *v_cache,
                          const int32_t *page_table, const int32_t *ctx_lens,
@@ -64,8 +44,7 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
 
 // Top-k (forced pages as in launch_topk) then the decode of the selection;
 // one kernel where topk_decode_fused() says so, else launch_topk +
-// launch_decode.  Pure host test, no HIP call.
-bool topk_decode_fused(const Dims &dm, int batch, int max_k);
+// launch_decode.
 hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const void *k_cache,
                               const void *v_cache, const int32_t *page_table,
                               const int32_t *ctx_lens, const float *scores,

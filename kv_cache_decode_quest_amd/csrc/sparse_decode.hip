@@ -38,8 +38,6 @@
 
 namespace quest {
 
-constexpr int kDecodeWaves = 8;
-constexpr int kMaxSplits = 256;        // per (request, KV head); bounds the partials
 constexpr float kLog2e = 1.4426950408889634f;
 
 // XCDs of an MI355X.  With a grid of a multiple of kXcds work-groups,
@@ -60,54 +58,10 @@ static bool xcd_placement(unsigned blocks, int n_split, unsigned mblocks) {
          mblocks % kXcds == 0;
 }
 
-// Pages one wave loads at once (one round): 32 KB of K and V per wave in
-// flight at D = 128 (4 pages of 16 tokens, 2 of 32, 1 of 64), so the page
-// registers stay within budget.
-// 8-token pages go two to a 16-token tile (twice the pages of 16-token ones).
-__host__ __device__ constexpr int pages_per_wave(int P, int D) {
-  return P < 16 ? 2 * pages_per_wave(16, D) : ((P * D <= 2048) ? 4 : (P * D <= 4096 ? 2 : 1));
-}
 // Pages folded into the running softmax per update.  The loads of a round
 // are issued group by group (K then V of each group), so a group's update
 // can start while later groups are still in flight.
 constexpr int kPagesPerUpdate = 2;
-
-// Work-groups the plan aims for: four per resident slot (two work-groups per
-// CU at the decode's LDS size), so rows of very different selection sizes
-// (a ragged batch: every row's grid is sized by the largest) still spread
-// over the CUs; and at most kPlanSplits splits per bf16 row, so long rows
-// take several rounds per split instead of multiplying the partials the
-// merge reads (a dense 8008-page row: 32 splits of 8 rounds).  Measured on
-// the ragged batch (32 requests, page 32, 10% budgets): 134 us per step
-// against 162 us at 1024 work-groups; the dense reference unchanged.
-constexpr long kTargetWorkGroups = 2048;
-constexpr long kPlanSplits = 32;
-
-DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
-  DecodePlan p{1, max_k > 0 ? max_k : 1};
-  if (batch <= 0 || max_k <= 0) return p;
-  // A round: the bf16 kernel's waves take pages_per_wave pages each at once;
-  // the fp32 kernel walks its pages one at a time (each a chain of loads and
-  // barriers), so its splits start at one page.
-  const long per_round = dm.dtype == 1 ? (long)kDecodeWaves * pages_per_wave(dm.P, dm.D) : 1;
-  const long rows = (long)batch * dm.R;
-  long want_splits = std::max(1L, (kTargetWorkGroups + rows - 1) / rows);
-  if (dm.dtype == 1) want_splits = std::min(want_splits, kPlanSplits);
-  long rounds = 1;
-  while ((max_k + per_round * rounds - 1) / (per_round * rounds) >
-         std::min((long)kMaxSplits, want_splits) && per_round * rounds < max_k)
-    ++rounds;
-  const long pps = per_round * rounds;
-  p.pages_per_split = (int)pps;
-  p.n_split = (int)((max_k + pps - 1) / pps);
-  return p;
-}
-
-size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k) {
-  if (batch <= 0) return 0;
-  const DecodePlan p = decode_plan(dm, batch, max_k);
-  return (size_t)batch * dm.R * p.n_split * dm.Gcols * (dm.D + 2) * sizeof(float);
-}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -523,9 +477,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 2 * kDecodeWaves;
 static_assert(kFusedWaves * kWave == kTopkThreads, "the fused kernel runs the 1024-thread selection");
-constexpr int kMaxFusedPages = 256;          // pages per split the LDS list holds
-constexpr long kFusedMaxWorkGroups = 256;    // the CU count of an MI355X
-
 template <int D, int P, bool kPack>
 __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
     int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k, int n_split,
@@ -813,34 +764,6 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_merge(dm, batch, plan, workspace, out, stream);
-}
-
-// Shapes whose 16-wave decode fits the 128 registers a 1024-thread
-// work-group leaves each lane (the others spill, and stay two launches).
-static bool fused_shape(int P, int D) { return D == 64 || (D == 128 && P == 16); }
-
-// The fused kernel's plan: as many splits per row as keep the grid within
-// one resident work-group per CU, each a whole number of the decode's rounds.
-// It never has more splits than decode_plan, so the same workspace fits; a
-// row of one split writes its output directly (no merge launch).
-static DecodePlan fused_plan(const Dims &dm, int batch, int max_k) {
-  const long rows = (long)batch * dm.R;
-  const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
-  const long cap = std::max(1L, kFusedMaxWorkGroups / std::max(1L, rows));
-  long pps = (max_k + cap - 1) / cap;
-  pps = (pps + per_round - 1) / per_round * per_round;
-  DecodePlan p;
-  p.pages_per_split = (int)pps;
-  p.n_split = (int)((max_k + pps - 1) / pps);
-  return p;
-}
-
-bool topk_decode_fused(const Dims &dm, int batch, int max_k) {
-  if (dm.dtype != 1 || dm.max_pages > kRegKeys || !fused_shape(dm.P, dm.D) || max_k <= 0)
-    return false;
-  const DecodePlan p = fused_plan(dm, batch, max_k);
-  return p.pages_per_split <= kMaxFusedPages &&
-         (long)batch * dm.R * p.n_split <= kFusedMaxWorkGroups;
 }
 
 hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const void *k_cache,

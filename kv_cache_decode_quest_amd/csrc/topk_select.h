@@ -34,6 +34,7 @@
 //     its ascending position.
 #pragma once
 #include "quest_device.h"
+#include "quest_plan.h"
 
 namespace quest {
 
@@ -134,7 +135,6 @@ __device__ __forceinline__ void pick_bucket(TopkShared &sh, int bins, uint32_t k
 // needs, so no pass re-reads memory.  S spreads the row's stride over all
 // waves in whole 64-page slots, so short rows keep every wave busy.  Longer
 // rows read their scores from global memory in every pass.
-constexpr int kRegKeys = 8192;
 constexpr int kPerThread = kRegKeys / kTopkThreads;
 
 __host__ __device__ constexpr int reg_span(int max_pages) {

@@ -26,7 +26,8 @@ QUEST_SELECT_PER_KV_HEAD, QUEST_SELECT_PER_Q_HEAD = 0, 1
 EXPORTS = ("quest_abi_version", "quest_status_string", "quest_append_kv", "quest_page_scores",
            "quest_append_score", "quest_topk_pages", "quest_topk_pages_forced",
            "quest_sparse_decode_workspace_bytes", "quest_sparse_decode", "quest_sparse_decode_plan",
-           "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused", "quest_decode_step")
+           "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused",
+           "quest_topk_sparse_decode_plan", "quest_decode_step")
 
 
 class QuestError(RuntimeError):
@@ -80,12 +81,13 @@ def load(path: str = LIB_PATH):
     L.quest_topk_sparse_decode.argtypes = [lp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                            f32, vp, vp, vp, vp, sz, vp]
     L.quest_topk_sparse_decode_fused.argtypes = [lp, i32, i32]
+    L.quest_topk_sparse_decode_plan.argtypes = [lp, i32, i32, ip, ip, ip]
     L.quest_decode_step.argtypes = [lp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp,
                                     i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     for name in ("quest_append_kv", "quest_page_scores", "quest_append_score", "quest_topk_pages",
                  "quest_topk_pages_forced", "quest_sparse_decode", "quest_sparse_decode_plan",
                  "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused",
-                 "quest_decode_step"):
+                 "quest_topk_sparse_decode_plan", "quest_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     if L.quest_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libquest ABI {L.quest_abi_version()} != binding ABI {ABI_VERSION}")
@@ -335,6 +337,17 @@ def quest_topk_sparse_decode_fused(L: QuestLayout, batch: int, max_k: int) -> bo
     if st < 0:
         _raise("quest_topk_sparse_decode_fused", st)
     return st == 1
+
+
+def quest_topk_sparse_decode_plan(L: QuestLayout, batch: int, max_k: int):
+    """The plan of quest_topk_sparse_decode: whether it runs the fused kernel,
+    and its splits per selection row and pages per split."""
+    fu, ns, pps = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = load().quest_topk_sparse_decode_plan(ctypes.byref(L), int(batch), int(max_k),
+                                              ctypes.byref(fu), ctypes.byref(ns),
+                                              ctypes.byref(pps))
+    _raise("quest_topk_sparse_decode_plan", st)
+    return {"fused": bool(fu.value), "num_splits": ns.value, "pages_per_split": pps.value}
 
 
 def quest_decode_step(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq,

@@ -24,3 +24,17 @@ def gpu_lib():
         pytest.fail("gpu test selected but no GPU is visible")
     quest.load()
     return quest
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """How many selection rows differed from the oracle's only by near-tied
+    pages (each such request's output was checked against the oracle's
+    attention over the GPU's own selection)."""
+    parity = sys.modules.get("parity")
+    if parity is None or not parity.FLAGGED["requests_checked"]:
+        return
+    f = parity.FLAGGED
+    terminalreporter.write_line(
+        f"quest parity: {f['requests_checked']} request outputs checked against the oracle; "
+        f"{f['rows']} near-tie flagged selection rows in {f['requests']} requests, each "
+        f"checked against the oracle's attention over the GPU's own selection")

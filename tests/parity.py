@@ -142,14 +142,15 @@ class Layer:
         return quest.alloc_decode_buffers(self.L, self.w.batch, max_k, self.device)
 
     # ----- oracle side -------------------------------------------------------
-    def oracle_request(self, q, r, reduce="max", sm_scale=None, per_q_head=False):
+    def oracle_request(self, q, r, reduce="max", sm_scale=None, per_q_head=False, n_sink=0,
+                       n_recent=0):
         sm = workloads.default_sm_scale(self.w) if sm_scale is None else sm_scale
         qr = np.ascontiguousarray(to_oracle(q[r]))
         ctx = int(self.ctx[r])
         budget = int(self.budgets()[r])
         return oracle.decode_request(self.shape, qr, self.host[0], self.host[1],
                                      self.pt_host[r], ctx, budget, sm, reduce,
-                                     per_q_head=per_q_head)
+                                     n_sink=n_sink, n_recent=n_recent, per_q_head=per_q_head)
 
 
 # ----- comparisons -----------------------------------------------------------
@@ -211,6 +212,44 @@ def compare_selection(gpu_sel_row, gpu_nsel, ref_sel, ref_scores_row, rel=1e-5):
             assert abs(sa - sb) <= rel * max(abs(sa), abs(sb)), \
                 f"page {b} selected instead of {a}: scores {sb!r} vs {sa!r} are not a near-tie"
     return "flagged"
+
+
+# Rows whose selection differed from the oracle's only by near-tied pages,
+# over the test session; each such request's output is checked against the
+# oracle's attention over the GPU's own selection (check_request_output).
+FLAGGED = {"rows": 0, "requests": 0, "requests_checked": 0}
+
+
+def check_request_output(lay: "Layer", q, r, sel_r, nsel_r, out_r, ref, what, n_sink=0,
+                         n_recent=0, per_q_head=False, sm_scale=None):
+    """Selections of request r against the oracle's (exact, or only near-tie
+    differences), then its output: against the oracle's decode when every row
+    matched, else against the oracle's attention over the GPU's own
+    selection.  Returns the number of flagged rows."""
+    rows = len(ref["sel"])
+    flags = [compare_selection(sel_r[x], int(nsel_r[x]), ref["sel"][x], ref["scores"][x])
+             for x in range(rows)]
+    n_flag = flags.count("flagged")
+    FLAGGED["requests_checked"] += 1
+    if n_flag == 0:
+        check_out(out_r, ref["out"], lay.w.torch_dtype, what)
+        return 0
+    FLAGGED["rows"] += n_flag
+    FLAGGED["requests"] += 1
+    sm = workloads.default_sm_scale(lay.w) if sm_scale is None else sm_scale
+    qr = np.ascontiguousarray(to_oracle(q[r]))
+    gpu_sel = [np.asarray(sel_r[x][:int(nsel_r[x])], np.int32) for x in range(rows)]
+    ctx = int(lay.ctx[r])
+    if per_q_head:
+        want = oracle.request_attend_heads(lay.shape, qr, lay.host[0], lay.host[1],
+                                           lay.pt_host[r], ctx, gpu_sel, sm)
+    else:
+        want = oracle.request_attend(lay.shape, qr, lay.host[0], lay.host[1], lay.pt_host[r],
+                                     ctx, gpu_sel, sm)
+    check_out(out_r, want, lay.w.torch_dtype, f"{what} (flagged rows {n_flag}: the oracle's "
+              f"attention over the GPU selection)")
+    log(f"{what}: {n_flag} flagged row(s), output checked over the GPU selection")
+    return n_flag
 
 
 def check_out(got, ref, dtype, what="output"):

@@ -274,8 +274,9 @@ def test_topk_sparse_decode_rejections(lib):
 
 def test_topk_sparse_decode_fused_rule(lib):
     """One kernel for bf16 rows of at most 8192 pages, D 64 or (D 128, P 16),
-    each row split into at most 256 / rows parts (whole rounds of 32 pages at
-    P 16, D 128) of at most 256 pages; two kernels otherwise."""
+    each row split into at most min(256 / rows, the decode plan's splits)
+    parts (whole rounds of 32 pages at P 16, D 128) of at most 256 pages; two
+    kernels otherwise."""
     bench = layout(num_pool_pages=8 * 8009, max_pages_per_seq=8009)
     assert quest.quest_topk_sparse_decode_fused(bench, 8, 256)          # 32 rows x 8 splits
     assert quest.quest_topk_sparse_decode_fused(bench, 9, 256)          # 36 rows x 4 splits of 64
@@ -291,9 +292,57 @@ def test_topk_sparse_decode_fused_rule(lib):
     assert quest.quest_topk_sparse_decode_fused(layout(max_pages_per_seq=8192), 1, 16)
     assert not quest.quest_topk_sparse_decode_fused(layout(), 0, 16)
     big = layout(num_kv_heads=1, num_q_heads=8, num_pool_pages=9000, max_pages_per_seq=8000)
-    assert quest.quest_topk_sparse_decode_fused(big, 1, 8000)           # 250 splits of 32
-    assert not quest.quest_topk_sparse_decode_fused(big, 1, 100000)     # 256 splits of 416
+    assert quest.quest_topk_sparse_decode_fused(big, 1, 8000)           # 32 splits of 256
+    assert quest.quest_topk_sparse_decode_plan(big, 1, 8000) == {
+        "fused": True, "num_splits": 32, "pages_per_split": 256}
+    assert not quest.quest_topk_sparse_decode_fused(big, 1, 8193)       # 32 splits of 288
+    assert not quest.quest_topk_sparse_decode_fused(big, 1, 100000)
     assert lib.quest_topk_sparse_decode_fused(ctypes.byref(layout()), 1, 0) == ERR_SHAPE
+    # one request of 4 KV heads with 2048 pages kept: 32 splits (the decode
+    # plan's, whose partials the workspace holds) of two rounds each
+    one = layout(num_pool_pages=4000, max_pages_per_seq=4000)
+    assert quest.quest_topk_sparse_decode_plan(one, 1, 2048) == {
+        "fused": True, "num_splits": 32, "pages_per_split": 64}
+    p = quest.quest_topk_sparse_decode_plan(bench, 8, 256)
+    assert p == {"fused": True, "num_splits": 8, "pages_per_split": 32}
+    assert quest.quest_topk_sparse_decode_plan(bench, 64, 128) == {
+        "fused": True, "num_splits": 1, "pages_per_split": 128}
+    two = quest.quest_topk_sparse_decode_plan(layout(page_size=32), 1, 16)
+    assert not two["fused"]
+    assert two == dict(fused=False, **quest.quest_sparse_decode_plan(layout(page_size=32), 1, 16))
+    assert lib.quest_topk_sparse_decode_plan(ctypes.byref(layout()), 1, 16, None, None,
+                                             None) == ERR_NULL
+
+
+def test_fused_plan_fits_the_workspace():
+    """Over every row count the fused kernel takes (1..256) and selection
+    sizes up to 8192 pages, the fused plan never has more splits than the
+    decode plan the workspace is sized for, covers max_k with no empty split,
+    and uses whole rounds; so its partials always fit
+    quest_sparse_decode_workspace_bytes."""
+    per_round = {(16, 128): 32, (8, 64): 64, (16, 64): 32, (32, 64): 16, (64, 64): 8}
+    ks = sorted(set(list(range(1, 600)) + list(range(600, 8193, 37)) +
+                [2 ** e + d for e in range(5, 14) for d in (-1, 0, 1)]))
+    ks = [k for k in ks if 1 <= k <= 8192]
+    checked = 0
+    for (P, D), rnd in per_round.items():
+        for hkv in (1, 4):
+            for batch in sorted(set([1, 2, 3, 5, 7, 8, 9, 16, 31, 32, 33, 63, 64] +
+                                    [256 // hkv])):
+                L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8, head_dim=D, page_size=P,
+                           num_pool_pages=9000, max_pages_per_seq=8192)
+                for k in ks:
+                    f = quest.quest_topk_sparse_decode_plan(L, batch, k)
+                    if not f["fused"]:
+                        continue
+                    d = quest.quest_sparse_decode_plan(L, batch, k)
+                    assert f["num_splits"] <= d["num_splits"], (P, D, hkv, batch, k, f, d)
+                    assert batch * hkv * f["num_splits"] <= 256
+                    assert f["pages_per_split"] % rnd == 0 and f["pages_per_split"] <= 256
+                    assert (f["num_splits"] - 1) * f["pages_per_split"] < k
+                    assert f["num_splits"] * f["pages_per_split"] >= k
+                    checked += 1
+    assert checked > 10000
 
 
 def step_call(lib, L, batch=1, max_k=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, k_new=FAKE,

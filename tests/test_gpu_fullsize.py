@@ -12,7 +12,8 @@ import oracle
 from helpers import to_f64, to_oracle
 from kv_cache_decode_quest_amd import quest, workloads
 from kv_cache_decode_quest_amd.workloads import WORKLOADS, scaled
-from parity import Layer, check_kmeta, check_out, check_scores, compare_selection, log
+from parity import (Layer, check_kmeta, check_out, check_request_output, check_scores,
+                    log)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -30,12 +31,8 @@ def check_requests(lay, q, bufs, requests):
         ref = lay.oracle_request(q, r)
         check_kmeta(lay, r, ref["bounds"], km)
         check_scores(scores[r], ref["scores"], qh[r], ref["bounds"], lay.w.group)
-        flags = [compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g], ref["scores"][g])
-                 for g in range(lay.w.num_kv_heads)]
-        if "flagged" in flags:
-            flagged += 1
-        else:
-            check_out(out[r], ref["out"], lay.w.torch_dtype, f"{lay.w.name} r{r}")
+        flagged += check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref,
+                                        f"{lay.w.name} r{r}")
     return flagged
 
 
@@ -73,8 +70,11 @@ def test_full_ragged_sampled(gpu_lib):
 
 def test_full_layers48_sampled(gpu_lib):
     """The full 48-layer decode step (batch 64 x 32768, budget 2048, K outlier
-    channels x10), all 48 layers resident (about 219 GB); layers 0, 23 and 47
-    checked on requests 0 and 63."""
+    channels x10), all 48 layers resident (about 219 GB), every layer through
+    the sequence bench.py times (quest_append_score, then
+    quest_topk_sparse_decode: 256 selection rows, one fused work-group per
+    row attending its 128 pages in four rounds and writing the output with
+    no merge); layers 0, 23 and 47 checked on requests 0 and 63."""
     w = WORKLOADS["layers48"]
     sampled_layers, sample = (0, 23, 47), [0, 63]
     layers, results = [], {}
@@ -89,8 +89,11 @@ def test_full_layers48_sampled(gpu_lib):
     for li, lay in enumerate(layers):
         q, k_new, v_new = lay.step_inputs(0)
         bufs = lay.buffers(extra=1)
-        lay.append_score_step(q, k_new, v_new, bufs)
-        lay.attend(q, bufs)
+        if li == 0:
+            plan = quest.quest_topk_sparse_decode_plan(lay.L, w.batch, bufs.max_k)
+            assert plan == {"fused": True, "num_splits": 1, "pages_per_split": 128}, plan
+        lay.append_score_step(q, k_new, v_new, bufs, topk=False)
+        lay.select_attend(q, bufs)
         if li in sampled_layers:
             results[li] = (q, bufs)
     torch.cuda.synchronize()

@@ -13,10 +13,10 @@ import pytest
 import torch
 
 import oracle
-from helpers import to_f64, to_oracle
+from helpers import to_f64
 from kv_cache_decode_quest_amd import quest, workloads
 from kv_cache_decode_quest_amd.workloads import WORKLOADS, scaled
-from parity import SMALL, Layer, check_out, compare_selection, log, topk_rows
+from parity import SMALL, Layer, check_request_output, log, topk_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -28,6 +28,22 @@ CASES["bench128k_b4"] = scaled(WORKLOADS["bench128k"], batch=4, ctx=20000,
 CASES["rows256"] = workloads.Workload("rows256", 64, 32, 4, 128, 16, "bf16",
                                       ctx_range=(1, 1500), budget_tokens=320, steps=1,
                                       seed=91, poison=float("nan"))
+# Several rounds per split (the later rounds' page ids come from the split's
+# LDS list): 256 rows of 128 pages, one split of 4 rounds and no merge (the
+# 48-layer step's plan); 32 rows of 1024 pages, 8 splits of 4 rounds; one
+# request of 4 KV heads keeping 2048 pages, 32 splits of 2 rounds (the
+# decode plan's split count, which sizes the workspace)
+CASES["rounds4_rows256"] = workloads.Workload("rounds4_rows256", 64, 32, 4, 128, 16, "bf16",
+                                              ctx_range=(1000, 6000), budget_tokens=2048,
+                                              steps=1, seed=93, poison=float("nan"),
+                                              permute_pages=True)
+CASES["rounds4_rows32"] = workloads.Workload("rounds4_rows32", 8, 32, 4, 128, 16, "bf16",
+                                             ctx_range=(16500, 22000), budget_tokens=16384,
+                                             steps=1, seed=94)
+CASES["rounds2_batch1"] = workloads.Workload("rounds2_batch1", 1, 32, 4, 128, 16, "bf16",
+                                             ctx=40000, budget_tokens=32768, steps=1, seed=95)
+# rounds of the fused plan per split, where a case asserts it
+ROUNDS = {"rounds4_rows256": 4, "rounds4_rows32": 4, "rounds2_batch1": 2}
 # 40 requests: 160 rows, one split each
 CASES["rows160_d64"] = workloads.Workload("rows160_d64", 40, 16, 4, 64, 32, "bf16",
                                           ctx_range=(0, 3000), budget_tokens=640, steps=1,
@@ -44,10 +60,10 @@ def pages_per_round(P, D):
 
 def expect_fused(w, L, max_k):
     """The documented rule: bf16, rows of at most 8192 pages, D 64 or (D 128,
-    P 16), each row split into at most 256 / rows parts of whole rounds, of at
-    most 256 pages."""
+    P 16), each row split into at most min(256 / rows, the decode plan's
+    splits) parts of whole rounds, of at most 256 pages."""
     rows = w.batch * quest.selection_rows(L)
-    cap = max(1, 256 // rows)
+    cap = max(1, min(256 // rows, quest.quest_sparse_decode_plan(L, w.batch, max_k)["num_splits"]))
     per_round = pages_per_round(w.page_size, w.head_dim)
     pps = -(-(-(-max_k // cap)) // per_round) * per_round
     n_split = -(-max_k // pps)
@@ -86,7 +102,11 @@ def run_case(w, n_sink=0, n_recent=0, per_q_head=False):
         torch.cuda.synchronize()
         fused = quest.quest_topk_sparse_decode_fused(lay.L, w.batch, bufs.max_k)
         assert fused == expect_fused(w, lay.L, bufs.max_k)
-        log(f"{w.name} step {step}: fused kernel {fused}, max_k {bufs.max_k}")
+        plan = quest.quest_topk_sparse_decode_plan(lay.L, w.batch, bufs.max_k)
+        log(f"{w.name} step {step}: max_k {bufs.max_k}, plan {plan}")
+        if w.name in ROUNDS:
+            assert fused and plan["pages_per_split"] == \
+                ROUNDS[w.name] * pages_per_round(w.page_size, w.head_dim), plan
         assert torch.equal(fb.num_sel, bufs.num_sel)
         assert torch.equal(fb.sel_pages, bufs.sel_pages)
         two, one = to_f64(bufs.out), to_f64(fb.out)
@@ -94,16 +114,12 @@ def run_case(w, n_sink=0, n_recent=0, per_q_head=False):
             assert torch.equal(fb.out.view(torch.int16), bufs.out.view(torch.int16))
         else:
             assert np.all(one_bf16_ulp(one, two)), float(np.abs(one - two).max())
-        if n_sink or n_recent:
-            continue
-        sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+        sel, nsel = fb.sel_pages.cpu().numpy(), fb.num_sel.cpu().numpy()
         for r in range(w.batch):
-            ref = lay.oracle_request(q, r, per_q_head=per_q_head)
-            rows = len(ref["sel"])
-            flags = [compare_selection(sel[r, x], int(nsel[r, x]), ref["sel"][x],
-                                       ref["scores"][x]) for x in range(rows)]
-            if "flagged" not in flags:
-                check_out(one[r], ref["out"], w.torch_dtype, f"{w.name} fused r{r}")
+            ref = lay.oracle_request(q, r, per_q_head=per_q_head, n_sink=n_sink,
+                                     n_recent=n_recent)
+            check_request_output(lay, q, r, sel[r], nsel[r], one[r], ref,
+                                 f"{w.name} fused r{r}", per_q_head=per_q_head)
             if int(lay.ctx[r]) == 0:
                 assert np.all(one[r] == 0.0)
     return lay
@@ -137,14 +153,8 @@ def test_fused_forced_pages(gpu_lib):
     sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
     out = to_f64(bufs.out)
     for r in range(w.batch):
-        ref = oracle.decode_request(lay.shape, np.ascontiguousarray(to_oracle(q[r])), lay.host[0],
-                                    lay.host[1], lay.pt_host[r], int(lay.ctx[r]),
-                                    int(lay.budgets()[r]), workloads.default_sm_scale(w),
-                                    n_sink=1, n_recent=2)
-        flags = [compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g], ref["scores"][g])
-                 for g in range(w.num_kv_heads)]
-        if "flagged" not in flags:
-            check_out(out[r], ref["out"], torch.bfloat16, f"fused forced r{r}")
+        ref = lay.oracle_request(q, r, n_sink=1, n_recent=2)
+        check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref, f"fused forced r{r}")
 
 
 def test_fused_bench_shape_equals_two_calls(gpu_lib):

@@ -15,8 +15,8 @@ import oracle
 from helpers import to_f64, to_oracle
 from kv_cache_decode_quest_amd import quest, workloads
 from kv_cache_decode_quest_amd.workloads import WORKLOADS, scaled
-from parity import (SMALL, Layer, check_kmeta, check_out, check_pool_bytes, check_scores,
-                    compare_selection, log, topk_rows)
+from parity import (SMALL, Layer, check_kmeta, check_out, check_pool_bytes,
+                    check_request_output, check_scores, compare_selection, log, topk_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -67,16 +67,9 @@ def run_and_check(w, layer=0, reduce="max", fused=False):
             if ref["bounds"].shape[0]:
                 check_kmeta(lay, r, ref["bounds"], km)
                 check_scores(scores[r], ref["scores"], qh[r], ref["bounds"], w.group)
-            row_flag = False
-            for g in range(w.num_kv_heads):
-                outcome = compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g],
-                                            ref["scores"][g])
-                row_flag |= outcome == "flagged"
             check_out(out2[r], ref["out"], w.torch_dtype, f"{w.name} r{r} (oracle selection)")
-            if row_flag:
-                flagged += 1
-            else:
-                check_out(out[r], ref["out"], w.torch_dtype, f"{w.name} r{r}")
+            flagged += check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref,
+                                            f"{w.name} r{r}")
             if int(lay.ctx[r]) == 0:
                 assert np.all(out[r] == 0.0)
     log(f"workload {w.name}: ok, flagged rows {flagged}")
@@ -100,10 +93,24 @@ def test_group_sum_variant(gpu_lib):
     run_and_check(SMALL["layer32k_small"], reduce="sum")
 
 
+def check_store_against_oracle(lay, k_c, v_c, km):
+    """Pools equal the oracle's store of the same tokens byte for byte, and
+    every live page's metadata equals the oracle's from-scratch min/max."""
+    assert to_oracle(k_c).tobytes() == lay.host[0].tobytes(), "K pool differs from the oracle"
+    assert to_oracle(v_c).tobytes() == lay.host[1].tobytes(), "V pool differs from the oracle"
+    kmh = to_f64(km)
+    for r in range(lay.w.batch):
+        ctx = int(lay.ctx[r])
+        if ctx:
+            check_kmeta(lay, r, oracle.request_bounds(lay.shape, lay.host[0], lay.pt_host[r], ctx),
+                        kmh)
+
+
 def test_incremental_append_equals_bulk(gpu_lib):
-    """Pool and metadata after token-by-token appends equal the bulk append's."""
+    """Pool and metadata after token-by-token appends equal the bulk append's,
+    and both equal the oracle's store and from-scratch page bounds."""
     w = scaled(WORKLOADS["ragged"], batch=3, ctx_range=(20, 200), steps=0)
-    bulk = Layer(w, DEV, host=False)
+    bulk = Layer(w, DEV)
     k_c, v_c = workloads.empty_pool(w, bulk.lay, DEV)
     km = torch.full_like(bulk.kmeta, -3.0)
     k_new, v_new, cu, _ = workloads.prefill_tokens(w, bulk.lay, DEV)
@@ -126,16 +133,21 @@ def test_incremental_append_equals_bulk(gpu_lib):
         n = -(-int(bulk.ctx[r]) // w.page_size)
         phys = bulk.pt[r, :n].long()
         assert torch.equal(km[phys].view(torch.int16), bulk.kmeta[phys].view(torch.int16))
+    check_store_against_oracle(bulk, k_c, v_c, km)
 
 
-@pytest.mark.parametrize("page_size", [8, 16, 32, 64])
-def test_unaligned_and_chunked_append_match(page_size, gpu_lib):
-    """The same tokens stored three ways give identical pools and metadata:
-    one bulk append (16-byte vector path), chunks of 37 tokens that start and
-    end inside pages, and one bulk append from source tensors shifted off
-    16-byte alignment (the scalar path)."""
-    w = scaled(WORKLOADS["ragged"], batch=3, ctx_range=(200, 900), steps=0, page_size=page_size)
-    ref = Layer(w, DEV, host=False)
+@pytest.mark.parametrize("page_size,chunk,ctx_range", [
+    (8, 37, (200, 900)), (16, 37, (200, 900)), (32, 37, (200, 900)), (64, 37, (200, 900)),
+    (16, 4096, (5000, 13000))])
+def test_unaligned_and_chunked_append_match(page_size, chunk, ctx_range, gpu_lib):
+    """The same tokens stored three ways give identical pools and metadata,
+    equal to the oracle's store and from-scratch page bounds: one bulk append
+    (16-byte vector path), chunks of `chunk` tokens per request per call
+    (37: chunks that start and end inside pages; 4096: the prefill chunk
+    size, page-aligned, with a partial last chunk), and one bulk append from
+    source tensors shifted off 16-byte alignment (the scalar path)."""
+    w = scaled(WORKLOADS["ragged"], batch=3, ctx_range=ctx_range, steps=0, page_size=page_size)
+    ref = Layer(w, DEV)
     k_new, v_new, cu, _ = workloads.prefill_tokens(w, ref.lay, DEV)
     cuh = cu.cpu().tolist()
     lens = [cuh[r + 1] - cuh[r] for r in range(w.batch)]
@@ -151,10 +163,11 @@ def test_unaligned_and_chunked_append_match(page_size, gpu_lib):
             n = -(-lens[r] // w.page_size)
             phys = ref.pt[r, :n].long()
             assert torch.equal(km[phys].view(torch.int16), ref.kmeta[phys].view(torch.int16))
+        check_store_against_oracle(ref, k_c, v_c, km)
 
-    # chunks of 37 tokens per request
+    # chunks of `chunk` tokens per request
     k_c, v_c, km = fresh()
-    step = 37
+    step = chunk
     for t0 in range(0, max(lens), step):
         counts = [max(0, min(step, n - t0)) for n in lens]
         rows = [cuh[r] + t0 + i for r in range(w.batch) for i in range(counts[r])]
@@ -290,17 +303,11 @@ def test_forced_pages_decode(gpu_lib):
     sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
     out = to_f64(bufs.out)
     for r in range(w.batch):
-        ref = oracle.decode_request(lay.shape, np.ascontiguousarray(to_oracle(q[r])), lay.host[0],
-                                    lay.host[1], lay.pt_host[r], int(lay.ctx[r]),
-                                    int(lay.budgets()[r]), workloads.default_sm_scale(w),
-                                    n_sink=1, n_recent=2)
+        ref = lay.oracle_request(q, r, n_sink=1, n_recent=2)
         n = -(-int(lay.ctx[r]) // w.page_size)
-        flags = [compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g], ref["scores"][g])
-                 for g in range(w.num_kv_heads)]
         for g in range(w.num_kv_heads):
             assert {0, n - 2, n - 1} <= set(sel[r, g, :nsel[r, g]].tolist())
-        if "flagged" not in flags:
-            check_out(out[r], ref["out"], torch.bfloat16, f"forced r{r}")
+        check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref, f"forced r{r}")
 
 
 @pytest.mark.parametrize("name,fused", [("layer32k_small", False), ("layer32k_small", True),
@@ -338,10 +345,8 @@ def test_per_q_head_selection(name, fused, gpu_lib):
             tol = 2.0 * (w.head_dim + 2) * 2.0 ** -24 * np.einsum(
                 "hd,jhd->hj", np.abs(qh[r]), mag[:, kv_of, :]) + 1e-30
             assert np.all(np.abs(scores[r, :, :n] - ref["scores"]) <= tol)
-        flags = [compare_selection(sel[r, h], int(nsel[r, h]), ref["sel"][h], ref["scores"][h])
-                 for h in range(w.num_q_heads)]
-        if "flagged" not in flags:
-            check_out(out[r], ref["out"], w.torch_dtype, f"{name} per-head r{r}")
+        check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref, f"{name} per-head r{r}",
+                             per_q_head=True)
 
 
 def test_topk_empty_request(gpu_lib):
@@ -401,32 +406,39 @@ def test_split_count_invariance(gpu_lib):
 
 
 def test_full_bench_shape_sampled(gpu_lib):
-    """The benchmark's own shape (batch 8 x 128000, budget 4096), two decode
-    steps, requests 0 and 7 checked against the oracle in full."""
+    """The benchmark's own shape (batch 8 x 128000, budget 4096), requests 0
+    and 7 checked against the oracle in full after each of two decode steps:
+    step 0 through the four separate calls (append, scores, top-k, decode),
+    step 1 through exactly the sequence bench.py times (quest_append_score,
+    then quest_topk_sparse_decode: one fused top-k + decode launch of 8
+    splits per row and the merge)."""
     w = scaled(WORKLOADS["bench128k"], steps=2)
     log("full-size benchmark shape: building the cache")
-    lay = Layer(w, DEV)
+    lay = Layer(w, DEV, host_requests=[0, 7])
     log("cache built")
     for step in range(w.steps):
         q, k_new, v_new = lay.step_inputs(step)
-        lay.append_step(k_new, v_new)
-    bufs = lay.buffers()
-    lay.view(q, bufs)
-    lay.attend(q, bufs)
-    torch.cuda.synchronize()
-    km = to_f64(lay.kmeta)
-    scores = bufs.scores.cpu().numpy().astype(np.float64)
-    sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
-    out = to_f64(bufs.out)
-    qh = to_f64(q)
-    for r in (0, 7):
-        log(f"oracle request {r}")
-        ref = lay.oracle_request(q, r)
-        check_kmeta(lay, r, ref["bounds"], km)
-        check_scores(scores[r], ref["scores"], qh[r], ref["bounds"], w.group)
-        flags = [compare_selection(sel[r, g], int(nsel[r, g]), ref["sel"][g], ref["scores"][g])
-                 for g in range(w.num_kv_heads)]
-        assert ref["k"] == 256
-        if "flagged" not in flags:
-            check_out(out[r], ref["out"], torch.bfloat16, f"bench r{r}")
-        log(f"request {r}: selections {flags}")
+        bufs = lay.buffers(extra=1)
+        if step == 0:
+            lay.append_step(k_new, v_new)
+            lay.view(q, bufs)
+            lay.attend(q, bufs)
+        else:
+            lay.append_score_step(q, k_new, v_new, bufs, topk=False)
+            lay.select_attend(q, bufs)
+            plan = quest.quest_topk_sparse_decode_plan(lay.L, w.batch, bufs.max_k)
+            assert plan == {"fused": True, "num_splits": 8, "pages_per_split": 32}, plan
+        torch.cuda.synchronize()
+        km = to_f64(lay.kmeta)
+        scores = bufs.scores.cpu().numpy().astype(np.float64)
+        sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+        out = to_f64(bufs.out)
+        qh = to_f64(q)
+        for r in (0, 7):
+            log(f"step {step}: oracle request {r}")
+            ref = lay.oracle_request(q, r)
+            check_kmeta(lay, r, ref["bounds"], km)
+            check_scores(scores[r], ref["scores"], qh[r], ref["bounds"], w.group)
+            assert ref["k"] == 256
+            check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref,
+                                 f"bench step {step} r{r}")

@@ -19,7 +19,7 @@ import torch
 import oracle
 from helpers import to_f64, to_oracle
 from kv_cache_decode_quest_amd import quest, workloads
-from parity import Layer, check_kmeta, check_out, compare_selection, log
+from parity import Layer, check_kmeta, check_request_output, log
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -101,13 +101,8 @@ def test_sweep_matches_oracle(cfg, gpu_lib):
                                     n_recent=nr, per_q_head=cfg["per_q_head"])
         if ctx:
             check_kmeta(lay, r, ref["bounds"], km)
-        rows = len(ref["sel"])
-        flags = [compare_selection(sel[r, x], int(nsel[r, x]), ref["sel"][x], ref["scores"][x])
-                 for x in range(rows)]
-        if "flagged" in flags:
-            flagged += 1
-        else:
-            check_out(out[r], ref["out"], w.torch_dtype, f"{cfg['name']} r{r}")
+        flagged += check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref,
+                                        f"{cfg['name']} r{r}", per_q_head=cfg["per_q_head"])
         if ctx == 0:
             assert np.all(nsel[r] == 0) and np.all(out[r] == 0.0)
     log(f"{cfg['name']}: ok, flagged rows {flagged}")
