@@ -73,8 +73,13 @@ typedef enum {
   QUEST_ERR_UNSUPPORTED = -3, /* valid but not built: dtype, D, P, G */
   QUEST_ERR_WORKSPACE = -4,   /* workspace missing or too small */
   QUEST_ERR_ABI = -5,         /* layout.abi_version != QUEST_ABI_VERSION */
-  QUEST_ERR_HIP = -6          /* the HIP runtime rejected a launch */
+  QUEST_ERR_HIP = -6,         /* the HIP runtime rejected a launch */
+  QUEST_ERR_SCRATCH = -7      /* beyond the static scratch of quest_decode_step_noalloc */
 } quest_status;
+
+/* Bytes of the library-owned device scratch of quest_decode_step_noalloc
+ * (one copy per GPU, held until the process ends). */
+#define QUEST_STATIC_SCRATCH_BYTES (16u << 20)
 
 typedef enum { QUEST_F32 = 0, QUEST_BF16 = 1 } quest_dtype;
 
@@ -294,6 +299,32 @@ int quest_decode_step(const quest_layout *layout, int32_t batch, const void *q,
                       int32_t n_recent, float sm_scale, float *scores, int32_t *sel_pages,
                       int32_t *num_sel, void *out, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* quest_decode_step for callers that cannot allocate device memory (code
+ * under hipGraph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, the same kernels and the same results bit for
+ * bit, but the decode's split partials live in a library-owned device array
+ * of QUEST_STATIC_SCRATCH_BYTES (16 MiB) per GPU instead of a caller
+ * workspace.  The caller still passes every input and output.  The call
+ * allocates and frees nothing; on its first use on a device (the calling
+ * thread's current device, which must be the stream's) it looks up that
+ * device's copy of the array, a host call that allocates nothing.
+ * Limits: the call needs quest_sparse_decode_workspace_bytes(layout, batch,
+ * max_k) <= QUEST_STATIC_SCRATCH_BYTES, else QUEST_ERR_SCRATCH with nothing
+ * launched (at batch 8 x 4 KV heads, G 8, D 128: max_k up to 8192).
+ * Concurrency: every call on one GPU shares that GPU's array, and the array
+ * keeps the last call's partials (their contents on entry do not matter;
+ * nothing needs clearing).  Calls that may overlap on one GPU (several
+ * streams, several host threads) race on it and must be serialised by the
+ * caller.  Arguments and other errors as in quest_decode_step. */
+int quest_decode_step_noalloc(const quest_layout *layout, int32_t batch, const void *q,
+                              const void *k_new, const void *v_new, const int32_t *cu_new,
+                              const int32_t *ctx_before, int32_t max_new_per_seq,
+                              const int32_t *page_table, void *k_cache, void *v_cache,
+                              void *kmeta, int32_t group_reduce, const int32_t *ctx_lens,
+                              const int32_t *budget_tokens, int32_t max_k, int32_t n_sink,
+                              int32_t n_recent, float sm_scale, float *scores,
+                              int32_t *sel_pages, int32_t *num_sel, void *out, void *stream);
 
 /* Launch plan quest_sparse_decode uses (for reports): number of KV splits per
  * (request, selection row) and pages per split.  Never calls HIP. */

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libquest.so")
 
 SOURCES = ["append_kv.hip", "page_scores.hip", "topk_pages.hip", "sparse_decode.hip",
-           "plan.cpp", "quest_abi.cpp"]
+           "static_scratch.hip", "plan.cpp", "quest_abi.cpp"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for all device code.

@@ -78,6 +78,35 @@ int check_batch(int32_t batch, const Dims &dm) {
 
 int launched(hipError_t e) { return e == hipSuccess ? QUEST_OK : QUEST_ERR_HIP; }
 
+// Validation shared by quest_decode_step and quest_decode_step_noalloc
+// (everything but the workspace).
+int check_decode_step(const quest_layout *layout, int32_t batch, const void *q,
+                      const void *k_new, const void *v_new, const int32_t *cu_new,
+                      const int32_t *ctx_before, int32_t max_new_per_seq,
+                      const int32_t *page_table, const void *k_cache, const void *v_cache,
+                      const void *kmeta, int32_t group_reduce, const int32_t *ctx_lens,
+                      const int32_t *budget_tokens, int32_t max_k, int32_t n_sink,
+                      int32_t n_recent, float sm_scale, const float *scores,
+                      const int32_t *sel_pages, const int32_t *num_sel, const void *out,
+                      Dims &dm) {
+  int st = check_layout(layout, dm);
+  if (st != QUEST_OK) return st;
+  if ((st = check_batch(batch, dm)) != QUEST_OK) return st;
+  if (max_new_per_seq < 0 || max_k <= 0 || n_sink < 0 || n_recent < 0) return QUEST_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return QUEST_ERR_SHAPE;
+  if (group_reduce != QUEST_REDUCE_MAX && group_reduce != QUEST_REDUCE_SUM)
+    return QUEST_ERR_UNSUPPORTED;
+  if (batch == 0) return QUEST_OK;
+  if (!q || !k_new || !v_new || !cu_new || !ctx_before || !page_table || !k_cache ||
+      !v_cache || !kmeta || !ctx_lens || !budget_tokens || !scores || !sel_pages || !num_sel ||
+      !out)
+    return QUEST_ERR_NULL;
+  if (dm.dtype == QUEST_BF16 && (!aligned16(q) || !aligned16(kmeta) || !aligned16(k_cache) ||
+                                 !aligned16(v_cache)))
+    return QUEST_ERR_SHAPE;
+  return QUEST_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,6 +122,8 @@ const char *quest_status_string(int status) {
     case QUEST_ERR_WORKSPACE: return "workspace missing or too small";
     case QUEST_ERR_ABI: return "layout abi_version does not match the library";
     case QUEST_ERR_HIP: return "the HIP runtime rejected a launch";
+    case QUEST_ERR_SCRATCH:
+      return "the step needs more than the library's static scratch (QUEST_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -254,6 +285,30 @@ int quest_topk_sparse_decode(const quest_layout *layout, int32_t batch, const vo
                                             (float *)workspace, (hipStream_t)stream));
 }
 
+int quest_decode_step_noalloc(const quest_layout *layout, int32_t batch, const void *q,
+                              const void *k_new, const void *v_new, const int32_t *cu_new,
+                              const int32_t *ctx_before, int32_t max_new_per_seq,
+                              const int32_t *page_table, void *k_cache, void *v_cache,
+                              void *kmeta, int32_t group_reduce, const int32_t *ctx_lens,
+                              const int32_t *budget_tokens, int32_t max_k, int32_t n_sink,
+                              int32_t n_recent, float sm_scale, float *scores,
+                              int32_t *sel_pages, int32_t *num_sel, void *out, void *stream) {
+  Dims dm;
+  const int st = check_decode_step(layout, batch, q, k_new, v_new, cu_new, ctx_before,
+                                   max_new_per_seq, page_table, k_cache, v_cache, kmeta,
+                                   group_reduce, ctx_lens, budget_tokens, max_k, n_sink,
+                                   n_recent, sm_scale, scores, sel_pages, num_sel, out, dm);
+  if (st != QUEST_OK || batch == 0) return st;
+  if (quest::decode_workspace_bytes(dm, batch, max_k) > (size_t)QUEST_STATIC_SCRATCH_BYTES)
+    return QUEST_ERR_SCRATCH;
+  void *scratch = nullptr;
+  if (quest::static_scratch(&scratch) != hipSuccess) return QUEST_ERR_HIP;
+  return launched(quest::launch_decode_step(
+      dm, batch, q, k_new, v_new, cu_new, ctx_before, max_new_per_seq, page_table, k_cache,
+      v_cache, kmeta, group_reduce, ctx_lens, budget_tokens, max_k, n_sink, n_recent, sm_scale,
+      scores, sel_pages, num_sel, out, (float *)scratch, (hipStream_t)stream));
+}
+
 int quest_decode_step(const quest_layout *layout, int32_t batch, const void *q,
                       const void *k_new, const void *v_new, const int32_t *cu_new,
                       const int32_t *ctx_before, int32_t max_new_per_seq,
@@ -264,21 +319,11 @@ int quest_decode_step(const quest_layout *layout, int32_t batch, const void *q,
                       int32_t *num_sel, void *out, void *workspace, size_t workspace_bytes,
                       void *stream) {
   Dims dm;
-  int st = check_layout(layout, dm);
-  if (st != QUEST_OK) return st;
-  if ((st = check_batch(batch, dm)) != QUEST_OK) return st;
-  if (max_new_per_seq < 0 || max_k <= 0 || n_sink < 0 || n_recent < 0) return QUEST_ERR_SHAPE;
-  if (!std::isfinite(sm_scale)) return QUEST_ERR_SHAPE;
-  if (group_reduce != QUEST_REDUCE_MAX && group_reduce != QUEST_REDUCE_SUM)
-    return QUEST_ERR_UNSUPPORTED;
-  if (batch == 0) return QUEST_OK;
-  if (!q || !k_new || !v_new || !cu_new || !ctx_before || !page_table || !k_cache ||
-      !v_cache || !kmeta || !ctx_lens || !budget_tokens || !scores || !sel_pages || !num_sel ||
-      !out)
-    return QUEST_ERR_NULL;
-  if (dm.dtype == QUEST_BF16 && (!aligned16(q) || !aligned16(kmeta) || !aligned16(k_cache) ||
-                                 !aligned16(v_cache)))
-    return QUEST_ERR_SHAPE;
+  const int st = check_decode_step(layout, batch, q, k_new, v_new, cu_new, ctx_before,
+                                   max_new_per_seq, page_table, k_cache, v_cache, kmeta,
+                                   group_reduce, ctx_lens, budget_tokens, max_k, n_sink,
+                                   n_recent, sm_scale, scores, sel_pages, num_sel, out, dm);
+  if (st != QUEST_OK || batch == 0) return st;
   const size_t need = quest::decode_workspace_bytes(dm, batch, max_k);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
     return QUEST_ERR_WORKSPACE;

@@ -65,4 +65,8 @@ hipError_t launch_decode_step(const Dims &dm, int batch, const void *q, const vo
                               int32_t *sel_pages, int32_t *num_sel, void *out,
                               float *workspace, hipStream_t stream);
 
+// This device's copy of the library-owned scratch array of
+// QUEST_STATIC_SCRATCH_BYTES (the current device's; looked up on first use).
+hipError_t static_scratch(void **ptr);
+
 }  // namespace quest

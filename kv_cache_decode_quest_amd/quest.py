@@ -21,13 +21,15 @@ ABI_VERSION = 1
 QUEST_F32, QUEST_BF16 = 0, 1
 REDUCE = {"max": 0, "sum": 1}
 QUEST_SELECT_PER_KV_HEAD, QUEST_SELECT_PER_Q_HEAD = 0, 1
+QUEST_ERR_SCRATCH = -7
+STATIC_SCRATCH_BYTES = 16 << 20     # QUEST_STATIC_SCRATCH_BYTES
 
 # exported symbols declared in include/quest.h
 EXPORTS = ("quest_abi_version", "quest_status_string", "quest_append_kv", "quest_page_scores",
            "quest_append_score", "quest_topk_pages", "quest_topk_pages_forced",
            "quest_sparse_decode_workspace_bytes", "quest_sparse_decode", "quest_sparse_decode_plan",
            "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused",
-           "quest_topk_sparse_decode_plan", "quest_decode_step")
+           "quest_topk_sparse_decode_plan", "quest_decode_step", "quest_decode_step_noalloc")
 
 
 class QuestError(RuntimeError):
@@ -84,10 +86,12 @@ def load(path: str = LIB_PATH):
     L.quest_topk_sparse_decode_plan.argtypes = [lp, i32, i32, ip, ip, ip]
     L.quest_decode_step.argtypes = [lp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp,
                                     i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    L.quest_decode_step_noalloc.argtypes = [lp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32,
+                                            vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp]
     for name in ("quest_append_kv", "quest_page_scores", "quest_append_score", "quest_topk_pages",
                  "quest_topk_pages_forced", "quest_sparse_decode", "quest_sparse_decode_plan",
                  "quest_topk_sparse_decode", "quest_topk_sparse_decode_fused",
-                 "quest_topk_sparse_decode_plan", "quest_decode_step"):
+                 "quest_topk_sparse_decode_plan", "quest_decode_step", "quest_decode_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     if L.quest_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libquest ABI {L.quest_abi_version()} != binding ABI {ABI_VERSION}")
@@ -388,6 +392,46 @@ def quest_decode_step(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before, max_n
                                   _ptr(scores), _ptr(sel_pages), _ptr(num_sel), _ptr(out),
                                   _ptr(workspace), nbytes, _stream(dev))
     _raise("quest_decode_step", st)
+
+
+def quest_decode_step_noalloc(L: QuestLayout, q, k_new, v_new, cu_new, ctx_before,
+                              max_new_per_seq, page_table, k_cache, v_cache, kmeta, ctx_lens,
+                              budget_tokens, max_k, sm_scale, scores, sel_pages, num_sel, out,
+                              group_reduce="max", n_sink=0, n_recent=0):
+    """quest_decode_step with the split partials in the library's static
+    device scratch (QUEST_STATIC_SCRATCH_BYTES per GPU) instead of a caller
+    workspace: for callers that cannot allocate.  Calls that may overlap on
+    one GPU race on that scratch."""
+    dt, dev = _layout_dtype(L), q.device
+    batch = ctx_before.shape[0]
+    kshape, vshape, mshape = _pool_shapes(L)
+    rows = selection_rows(L)
+    _check(q, "q", dt, (batch, L.num_q_heads, L.head_dim), dev)
+    _check(k_cache, "k_cache", dt, kshape, dev)
+    _check(v_cache, "v_cache", dt, vshape, dev)
+    _check(kmeta, "kmeta", dt, mshape, dev)
+    T = k_new.shape[0]
+    _check(k_new, "k_new", dt, (T, L.num_kv_heads, L.head_dim), dev)
+    _check(v_new, "v_new", dt, (T, L.num_kv_heads, L.head_dim), dev)
+    _check(cu_new, "cu_new", torch.int32, (batch + 1,), dev)
+    _check(ctx_before, "ctx_before", torch.int32, (batch,), dev)
+    _check(ctx_lens, "ctx_lens", torch.int32, (batch,), dev)
+    _check(page_table, "page_table", torch.int32, (batch, L.max_pages_per_seq), dev)
+    _check(budget_tokens, "budget_tokens", torch.int32, (batch,), dev)
+    _check(scores, "scores", torch.float32, (batch, rows, L.max_pages_per_seq), dev)
+    _check(sel_pages, "sel_pages", torch.int32, (batch, rows, max_k), dev)
+    _check(num_sel, "num_sel", torch.int32, (batch, rows), dev)
+    _check(out, "out", dt, (batch, L.num_q_heads, L.head_dim), dev)
+    if T == 0:                       # nothing to store: the append reads at most row 0 of
+        k_new = v_new = q            # k_new / v_new (clamped loads), which q's storage covers
+    with torch.cuda.device(dev):     # the scratch copy of the stream's device
+        st = load().quest_decode_step_noalloc(
+            ctypes.byref(L), batch, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_new),
+            _ptr(ctx_before), int(max_new_per_seq), _ptr(page_table), _ptr(k_cache),
+            _ptr(v_cache), _ptr(kmeta), REDUCE[group_reduce], _ptr(ctx_lens),
+            _ptr(budget_tokens), int(max_k), int(n_sink), int(n_recent), float(sm_scale),
+            _ptr(scores), _ptr(sel_pages), _ptr(num_sel), _ptr(out), _stream(dev))
+    _raise("quest_decode_step_noalloc", st)
 
 
 @dataclass

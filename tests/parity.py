@@ -76,11 +76,10 @@ class Layer:
     def step_inputs(self, step):
         return workloads.step_tokens(self.w, self.device, self.layer, step)
 
-    def append_step(self, k_new, v_new):
-        B = self.w.batch
-        cu = torch.arange(B + 1, dtype=torch.int32, device=self.device)
-        quest.quest_append_kv(self.L, k_new, v_new, cu, self.ctx, 1, self.pt, self.k_cache,
-                              self.v_cache, self.kmeta)
+    def host_append(self, k_new, v_new):
+        """The oracle's store of one new token per request into the host
+        mirror, at each request's current length (the GPU side is the
+        caller's); the lengths then grow by one."""
         if self.host is not None:
             kn, vn = to_oracle(k_new), to_oracle(v_new)
             ctx = self.ctx.cpu().numpy()
@@ -90,6 +89,13 @@ class Layer:
                                     self.pt_host[r], self.host[0], self.host[1])
         self.ctx = self.ctx + 1
 
+    def append_step(self, k_new, v_new):
+        B = self.w.batch
+        cu = torch.arange(B + 1, dtype=torch.int32, device=self.device)
+        quest.quest_append_kv(self.L, k_new, v_new, cu, self.ctx, 1, self.pt, self.k_cache,
+                              self.v_cache, self.kmeta)
+        self.host_append(k_new, v_new)
+
     def append_score_step(self, q, k_new, v_new, bufs, reduce="max", topk=True):
         """One token per request through the fused quest_append_score (and the
         same store on the host), then (topk) the top-k."""
@@ -97,14 +103,7 @@ class Layer:
         cu = torch.arange(B + 1, dtype=torch.int32, device=self.device)
         quest.quest_append_score(self.L, q, k_new, v_new, cu, self.ctx, 1, self.pt, self.k_cache,
                                  self.v_cache, self.kmeta, bufs.scores, reduce)
-        if self.host is not None:
-            kn, vn = to_oracle(k_new), to_oracle(v_new)
-            ctx = self.ctx.cpu().numpy()
-            for r in self.host_requests:
-                oracle.store_tokens(self.shape, np.ascontiguousarray(kn[r:r + 1]),
-                                    np.ascontiguousarray(vn[r:r + 1]), int(ctx[r]),
-                                    self.pt_host[r], self.host[0], self.host[1])
-        self.ctx = self.ctx + 1
+        self.host_append(k_new, v_new)
         if topk:
             quest.quest_topk_pages(self.L, bufs.scores, self.ctx, self.budgets(), bufs.max_k,
                                    bufs.sel_pages, bufs.num_sel)

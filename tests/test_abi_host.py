@@ -371,3 +371,41 @@ def test_decode_step_rejections(lib):
     assert step_call(lib, layout(page_size=48)) == ERR_UNSUPPORTED
     assert step_call(lib, layout(abi_version=2)) == ERR_ABI
     assert step_call(lib, L, batch=0, q=None, k_new=None, ctx_lens=None, ws=None) == OK
+
+
+def noalloc_call(lib, L, batch=1, max_k=16, q=FAKE, scale=0.1, reduce=0):
+    return lib.quest_decode_step_noalloc(ctypes.byref(L), batch, q, FAKE, FAKE, FAKE, FAKE, 1,
+                                         FAKE, FAKE, FAKE, FAKE, reduce, FAKE, FAKE, max_k, 0, 0,
+                                         scale, FAKE, FAKE, FAKE, FAKE, None)
+
+
+def test_decode_step_noalloc_rejections(lib):
+    """The no-allocation step validates like quest_decode_step and refuses,
+    before any HIP call, a step whose split partials exceed the library's
+    static scratch (QUEST_ERR_SCRATCH); batch 0 is a no-op."""
+    ERR_SCRATCH = quest.QUEST_ERR_SCRATCH
+    L = layout()
+    assert noalloc_call(lib, L, q=None) == ERR_NULL
+    assert noalloc_call(lib, L, max_k=0) == ERR_SHAPE
+    assert noalloc_call(lib, L, scale=float("nan")) == ERR_SHAPE
+    assert noalloc_call(lib, L, reduce=5) == ERR_UNSUPPORTED
+    assert noalloc_call(lib, L, q=ctypes.c_void_p(0x100002)) == ERR_SHAPE
+    assert noalloc_call(lib, layout(abi_version=3)) == ERR_ABI
+    assert noalloc_call(lib, L, batch=0, q=None) == OK
+    assert quest.status_string(ERR_SCRATCH) != "unknown status"
+    # 1100 requests x 4 KV heads: 4400 rows of one split, 8 heads x 130
+    # floats each = 18.3 MB of partials, beyond 16 MiB
+    need = lib.quest_sparse_decode_workspace_bytes(ctypes.byref(L), 1100, 16)
+    assert need > quest.STATIC_SCRATCH_BYTES
+    assert noalloc_call(lib, L, batch=1100) == ERR_SCRATCH
+    # fp32 at G 16, D 128: 32 rows x 64 one-page splits x 16 heads x 130 floats
+    Lf = layout(dtype=0, num_q_heads=64)
+    assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(Lf), 8, 64) > \
+        quest.STATIC_SCRATCH_BYTES
+    assert noalloc_call(lib, Lf, batch=8, max_k=64) == ERR_SCRATCH
+    # the measured shapes fit: batch 8 x 128000 (budget 4096), the 48-layer
+    # step's layer, the ragged batch, every page of batch 8 x 128000
+    for batch, max_k, P in [(8, 256, 16), (64, 128, 16), (32, 409, 32), (8, 8008, 16)]:
+        Lm = layout(page_size=P, num_pool_pages=70000, max_pages_per_seq=8192)
+        assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(Lm), batch, max_k) <= \
+            quest.STATIC_SCRATCH_BYTES, (batch, max_k, P)
