@@ -47,7 +47,7 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from kv_cache_decode_quest_amd import quest, workloads  # noqa: E402
+from kv_cache_decode_quest_amd import probe, quest, workloads  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "sparse decode tokens/s + achieved HBM GB/s (% peak), batch 8 x 128k ctx"
@@ -517,10 +517,84 @@ def traffic_from_pmc(fetch_csv, write_csv, copy_bytes):
             "copy_bytes": copy_bytes, "source_hash": source_hash(SCORE_SOURCES)}
 
 
-def cpu_baseline(w, layer_inputs, steps_inputs, n_req, n_steps):
-    """The fp64 oracle doing the same per-request decode work on the host."""
+def stream_probe(copies, n_launch):
+    """A plain contiguous read of each metadata copy (the bytes the scoring
+    kernel scans, plus the unused pool pages), launched back to back over the
+    copies between one event pair, like the scoring kernel's roofline loop."""
+    sink = torch.zeros(4, dtype=torch.int32, device=copies[0].device)
+    R = len(copies)
+    nbytes = copies[0].numel() * copies[0].element_size()
+    for i in range(R):
+        probe.stream_read(copies[i], sink)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n_launch):
+        probe.stream_read(copies[i % R], sink)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) / n_launch * 1e3
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"what": "contiguous 16-byte-load read of one metadata copy per launch, copies in "
+                    "rotation, launches back to back", "bytes": nbytes, "us": us, "gbps": gbps,
+            "frac_of_peak": gbps / PEAK_HBM_GBPS}
+
+
+def gather_probe(w, layers, sels, nsels, evict, dev):
+    """A plain read of exactly the K and V pages one step selects (4 KB
+    chunks at scattered offsets), once per resident copy with that copy's
+    selection, the cache evicted before each launch."""
+    P, D, Hkv = w.page_size, w.head_dim, w.num_kv_heads
+    es = 2 if w.dtype == "bf16" else 4
+    chunk = P * D * es
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    pt = layers[0].pt.to(torch.int64)
+    runs = []
+    for c, lay in enumerate(layers):
+        sel, nsel = sels[c].to(torch.int64), nsels[c]
+        live = torch.arange(sel.shape[-1], device=dev)[None, None, :] < nsel[:, :, None]
+        rr, gg, ii = torch.nonzero(live, as_tuple=True)
+        phys = pt[rr, sel[rr, gg, ii]]
+        offs = ((phys * Hkv + gg) * (chunk // 16)).contiguous()
+        runs.append((lay, offs))
+    probe.gather_read(runs[0][0].k_cache, runs[0][0].v_cache, runs[0][1], chunk, sink)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in runs]
+    torch.cuda.synchronize()
+    for i, (lay, offs) in enumerate(runs):
+        evict()
+        ev[i][0].record()
+        probe.gather_read(lay.k_cache, lay.v_cache, offs, chunk, sink)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = sum(e[0].elapsed_time(e[1]) for e in ev) / len(runs) * 1e3
+    nbytes = int(runs[0][1].numel()) * 2 * chunk
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"what": "read of the K and V pages of one step's selection (4 KB chunks per page "
+                    "and KV head), cache evicted before each launch", "bytes": nbytes, "us": us,
+            "gbps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, layer_inputs, steps_inputs, n_req, n_steps, single_steps):
+    """The fp64 oracle doing the same per-request decode work on the host:
+    per request and step, store the new token, refresh its page's bounds,
+    then scores, top-k and attention.  Timed twice on successive decode
+    steps: single-threaded (`single_steps` steps of every request), then with
+    one host thread per request (the oracle is plain C with no shared state;
+    its ctypes calls release the interpreter lock, and requests own disjoint
+    pages) for the next `n_steps` steps."""
     import numpy as np
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
 
     def host(t):
         t = t.detach().cpu().contiguous()
@@ -544,12 +618,12 @@ def cpu_baseline(w, layer_inputs, steps_inputs, n_req, n_steps):
                             pt[r], kh, vh)
         bounds[r] = oracle.request_bounds(s, kh, pt[r], int(ctx0[r]))
     sm = workloads.default_sm_scale(w)
-    log("cpu baseline: timing")
-    t0 = time.perf_counter()
-    done = 0
-    for st in range(n_steps):
-        q, kn1, vn1 = (host(x) for x in steps_inputs[st])
-        for r in range(n_req):
+    total = single_steps + n_steps
+    step_host = [tuple(host(x) for x in steps_inputs[st]) for st in range(total)]
+
+    def request_steps(r, steps):
+        for st in steps:
+            q, kn1, vn1 = step_host[st]
             pos = int(ctx0[r]) + st
             oracle.store_tokens(s, np.ascontiguousarray(kn1[r:r + 1]),
                                 np.ascontiguousarray(vn1[r:r + 1]), pos, pt[r], kh, vh)
@@ -561,21 +635,32 @@ def cpu_baseline(w, layer_inputs, steps_inputs, n_req, n_steps):
             budget = int(workloads.budget_tokens(w, torch.tensor([ctx], dtype=torch.int32))[0])
             oracle.decode_request(s, np.ascontiguousarray(q[r]), kh, vh, pt[r], ctx, budget, sm,
                                   bounds=np.ascontiguousarray(bounds[r]))
-            done += 1
+        return len(steps)
+
+    log(f"cpu baseline: single thread, {single_steps} steps x {n_req} requests")
+    t0 = time.perf_counter()
+    done1 = 0
+    for st in range(single_steps):
+        for r in range(n_req):
+            done1 += request_steps(r, [st])
+    dt1 = time.perf_counter() - t0
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(avail, n_req))
+    log(f"cpu baseline: {threads} threads, {n_steps} steps x {n_req} requests")
+    later = list(range(single_steps, total))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        done = sum(ex.map(lambda r: request_steps(r, later), range(n_req)))
     dt = time.perf_counter() - t0
-    cpu = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    cpu = cpu_model()
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_steps} decode steps x {n_req} of {w.batch} requests of the same "
                       f"workload (store, page-bounds refresh, scores, top-k, attention per "
-                      f"request-step), fp64, single thread; {dt:.1f} s on {cpu}",
-            "seconds": dt}
+                      f"request-step), fp64, one host thread per request ({threads} threads of "
+                      f"{avail} available); {dt:.1f} s on {cpu}",
+            "seconds": dt, "cpu_model": cpu, "cores_available": avail,
+            "single_thread": {"value": done1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "steps": single_steps, "seconds": dt1}}
 
 
 def main():
@@ -590,7 +675,10 @@ def main():
                     help="skip one timed step of each other single-layer workload")
     ap.add_argument("--config-steps", type=int, default=4)
     ap.add_argument("--cpu-requests", type=int, default=8)
-    ap.add_argument("--cpu-steps", type=int, default=24)
+    ap.add_argument("--cpu-steps", type=int, default=32,
+                    help="decode steps of the threaded CPU-oracle run")
+    ap.add_argument("--cpu-single-steps", type=int, default=8,
+                    help="decode steps of the single-threaded CPU-oracle run")
     ap.add_argument("--resident-layers", type=int, default=8,
                     help="copies of the layer the timed steps rotate over")
     ap.add_argument("--no-dense", action="store_true",
@@ -606,6 +694,8 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=4096,
                     help="chunk size of the prefill append leg (0 to skip)")
     ap.add_argument("--roofline-copies", type=int, default=8)
+    ap.add_argument("--extra-replays", type=int, default=4,
+                    help="timed replays after the first, for the median per-step time")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain copy of this size (counter calibration)")
     ap.add_argument("--traffic-from-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
@@ -636,13 +726,16 @@ def main():
         print("bench.py times single-layer workloads", file=sys.stderr)
         sys.exit(2)
     K, W = args.steps, args.warmup
-    cap = max(K, W, 1)
+    # the CPU-oracle baseline runs its own successive decode steps on a host
+    # copy of the same cache: the page table has room for them too
+    cpu_total = 0 if args.no_cpu_baseline else args.cpu_single_steps + args.cpu_steps
+    cap = max(K, W, cpu_total, 1)
     log(f"workload {w.name}: batch {w.batch}, ctx {workloads.context_lengths(w).tolist()[:4]}..,"
         f" building the cache")
     layer = BenchLayer(w, cap, dev)
     torch.cuda.synchronize()
     log("cache built; drawing step inputs")
-    inputs = make_steps(w, max(K, W), dev)
+    inputs = make_steps(w, cap, dev)
     ctx_b = [(layer.ctx0 + s).to(torch.int32) for s in range(cap)]
     ctx_a = [(layer.ctx0 + s + 1).to(torch.int32) for s in range(cap)]
     budgets = [workloads.budget_tokens(w, c).to(dev) for c in ctx_a]
@@ -714,6 +807,17 @@ def main():
     total_s = ev[0].elapsed_time(ev[1]) / 1e3
     same.append(same_as_eager())
     value = w.batch * K / total_s
+    # the same replay a few more times (cache evicted before each), for the
+    # spread of the per-step time; `value` is the first timed replay alone
+    replay_ms = [total_s / K * 1e3]
+    for _ in range(args.extra_replays):
+        evict()
+        ev[0].record()
+        graph.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        replay_ms.append(ev[0].elapsed_time(ev[1]) / K)
+    same.append(same_as_eager())
 
     meta_b, kv_b = 0, 0
     for s in range(K):
@@ -721,6 +825,8 @@ def main():
         meta_b += m
         kv_b += kv
     gbps = (meta_b + kv_b) / total_s / 1e9
+    n_g = min(NL, K)
+    gather = gather_probe(w, layers[:n_g], sels[:n_g], nsels[:n_g], evict, dev)
     del graph, step_bufs, per_copy, layers
     torch.cuda.empty_cache()
 
@@ -735,8 +841,10 @@ def main():
         run_step(layer, bufs, s, inputs[s], ctx_b[s], ctx_a[s], budgets[s], sm)
         ev_step[s][1].record()
     torch.cuda.synchronize()
-    eager_ms = sum(e[0].elapsed_time(e[1]) for e in ev_step) / K
+    eager_each = sorted(e[0].elapsed_time(e[1]) for e in ev_step)
+    eager_ms = sum(eager_each) / K
     eager = {"tokens_per_s": w.batch / (eager_ms / 1e3), "ms_per_step": eager_ms,
+             "ms_per_step_median": eager_each[K // 2],
              "note": "one copy of the layer, steps launched one at a time from Python, "
                      "a 2 GiB read sweep before each step, one event pair per step"}
     # 2. per-kernel breakdown: the same steps again, an event between kernels
@@ -782,6 +890,7 @@ def main():
     score_bytes = int(n_last.sum()) * w.num_kv_heads * 2 * w.head_dim * \
         (2 if w.dtype == "bf16" else 4)
     score_gbps = score_bytes / (score_us * 1e-6) / 1e9
+    stream = stream_probe(copies, n_launch)
     traffic = measured_traffic()
     if args.calibrate_copy_mib:
         src = torch.ones(args.calibrate_copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
@@ -839,7 +948,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, (layer.lay,) + layer.prefill, inputs,
-                           min(args.cpu_requests, w.batch), min(args.cpu_steps, K))
+                           min(args.cpu_requests, w.batch), args.cpu_steps, args.cpu_single_steps)
 
     result = {
         "metric": METRIC,
@@ -870,9 +979,15 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": score_bytes,
                      "avg_launch_us": score_us, "launches": n_launch,
-                     "metadata_copies": R},
+                     "metadata_copies": R,
+                     "frac_of_stream_probe": score_gbps / stream["gbps"]},
+        "ms_per_step_median": sorted(replay_ms)[len(replay_ms) // 2],
+        "replays_ms_per_step": replay_ms,
+        "hbm_probe": {"stream_read": stream, "gather_read": gather},
         "kernels_us_event_bracketed": {k: sum(v) / K * 1e3 for k, v in phase_ms.items()},
         "topk_decode": {"selected_kv_gbps": decode_gbps, "plan": plan,
+                        "combined_plan": quest.quest_topk_sparse_decode_plan(layer.L, w.batch,
+                                                                             max_k),
                         "one_kernel": quest.quest_topk_sparse_decode_fused(layer.L, w.batch,
                                                                            max_k)},
         "launch": {"hip_graph": True, "resident_layer_copies": NL,

@@ -14,13 +14,14 @@ from kv_cache_decode_quest_amd import quest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "quest.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "quest_probe.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ABI = 0, -1, -2, -3, -4, -5
 FAKE = ctypes.c_void_p(0x100000)          # aligned, never dereferenced on the host
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(quest_\w+)\s*\(", text)))
 
@@ -409,3 +410,25 @@ def test_decode_step_noalloc_rejections(lib):
         Lm = layout(page_size=P, num_pool_pages=70000, max_pages_per_seq=8192)
         assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(Lm), batch, max_k) <= \
             quest.STATIC_SCRATCH_BYTES, (batch, max_k, P)
+
+
+def test_probe_library_exports_and_rejections():
+    """The measurement library (HBM read probes, include/quest_probe.h) loads,
+    exports what its header declares, and rejects bad arguments before any
+    launch."""
+    from kv_cache_decode_quest_amd import probe
+    L = probe.load()
+    names = declared_functions(PROBE_HEADER)
+    assert sorted(probe.EXPORTS) == names
+    for name in names:
+        assert hasattr(L, name)
+    sink = ctypes.c_void_p(0x200000)
+    assert L.quest_probe_stream_read(None, 1024, 4, 0, sink, None) == -1
+    assert L.quest_probe_stream_read(FAKE, 1000, 4, 0, sink, None) == -2
+    assert L.quest_probe_stream_read(ctypes.c_void_p(0x100008), 1024, 4, 0, sink, None) == -2
+    assert L.quest_probe_stream_read(FAKE, 1024, 0, 0, sink, None) == -2
+    assert L.quest_probe_stream_read(FAKE, 0, 4, 0, sink, None) == 0
+    assert L.quest_probe_gather_read(FAKE, FAKE, None, 4, 4096, 4, 0, sink, None) == -1
+    assert L.quest_probe_gather_read(FAKE, FAKE, FAKE, 4, 1000, 4, 0, sink, None) == -3
+    assert L.quest_probe_gather_read(FAKE, FAKE, FAKE, -1, 4096, 4, 0, sink, None) == -2
+    assert L.quest_probe_gather_read(FAKE, FAKE, FAKE, 0, 4096, 4, 0, sink, None) == 0
