@@ -9,15 +9,13 @@ namespace quest {
 
 namespace {
 
-// Work-groups the plan aims for: four per resident slot (two work-groups per
-// CU at the decode's LDS size), so rows of very different selection sizes
-// (a ragged batch: every row's grid is sized by the largest) still spread
-// over the CUs; and at most kPlanSplits splits per bf16 row, so long rows
-// take several rounds per split instead of multiplying the partials the
-// merge reads (a dense 8008-page row: 32 splits of 8 rounds).  Measured on
-// the ragged batch (32 requests, page 32, 10% budgets): 134 us per step
-// against 162 us at 1024 work-groups; the dense reference unchanged.
+// fp32: work-groups the plan aims for (the fp32 kernel walks its pages one at
+// a time, so its splits start at one page and the grid sets how many).
 constexpr long kTargetWorkGroups = 2048;
+// bf16: at most kPlanSplits splits per row, so long rows take several rounds
+// per split instead of multiplying the partials the merge reads (a dense
+// 8008-page row: 32 splits of 8 rounds); otherwise one round per split, the
+// unit the live-split decode spreads over its work-groups.
 constexpr long kPlanSplits = 32;
 
 // Shapes whose 16-wave decode fits the 128 registers a 1024-thread
@@ -29,21 +27,34 @@ bool fused_shape(int P, int D) { return D == 64 || (D == 128 && P == 16); }
 DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
   DecodePlan p{1, max_k > 0 ? max_k : 1};
   if (batch <= 0 || max_k <= 0) return p;
-  // A round: the bf16 kernel's waves take pages_per_wave pages each at once;
-  // the fp32 kernel walks its pages one at a time (each a chain of loads and
-  // barriers), so its splits start at one page.
-  const long per_round = dm.dtype == 1 ? (long)kDecodeWaves * pages_per_wave(dm.P, dm.D) : 1;
-  const long rows = (long)batch * dm.R;
-  long want_splits = std::max(1L, (kTargetWorkGroups + rows - 1) / rows);
-  if (dm.dtype == 1) want_splits = std::min(want_splits, kPlanSplits);
-  long rounds = 1;
-  while ((max_k + per_round * rounds - 1) / (per_round * rounds) >
-         std::min((long)kMaxSplits, want_splits) && per_round * rounds < max_k)
-    ++rounds;
-  const long pps = per_round * rounds;
+  long pps;
+  if (dm.dtype == 1) {
+    // A round: the bf16 kernel's waves take pages_per_wave pages each at
+    // once.  One round per split, or as many as keep the splits within
+    // kPlanSplits.
+    const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
+    const long one_round = (max_k + per_round - 1) / per_round;
+    pps = per_round * ((one_round + kPlanSplits - 1) / kPlanSplits);
+  } else {
+    // fp32: one page per split, more only past the grid the plan aims for
+    // (or kMaxSplits per row).
+    const long rows = (long)batch * dm.R;
+    const long want = std::min((long)kMaxSplits,
+                               std::max(1L, (kTargetWorkGroups + rows - 1) / rows));
+    pps = (max_k + want - 1) / want;
+  }
   p.pages_per_split = (int)pps;
   p.n_split = (int)((max_k + pps - 1) / pps);
   return p;
+}
+
+bool decode_live(const Dims &dm, int batch) {
+  return dm.dtype == 1 && batch > 0 && (long)batch * dm.R <= kLiveRows;
+}
+
+int decode_grid(const Dims &dm, int batch, int max_k) {
+  const long splits = (long)batch * dm.R * decode_plan(dm, batch, max_k).n_split;
+  return (int)(decode_live(dm, batch) ? std::min(splits, (long)kLiveGrid) : splits);
 }
 
 size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k) {

@@ -51,6 +51,19 @@ constexpr long kFusedMaxWorkGroups = 256;
 // give n_split >= 1.
 DecodePlan decode_plan(const Dims &dm, int batch, int max_k);
 
+// The bf16 standalone decode runs only the splits that hold selected pages
+// ("live" splits: ceil(count / pages_per_split) of each row): every
+// work-group lists them from the rows' selection counts in LDS and takes
+// every kLiveGrid-th one.  Used while the rows' list fits (kLiveRows rows).
+// kLiveGrid is one work-group on each of an MI355X's 256 CUs: the 8-wave
+// decode needs about 200 registers per lane (two waves per SIMD), so one
+// work-group is resident per CU and the whole grid runs at once.
+constexpr int kLiveRows = 1024;
+constexpr int kLiveGrid = 256;
+bool decode_live(const Dims &dm, int batch);
+// Work-groups of the standalone decode launch.
+int decode_grid(const Dims &dm, int batch, int max_k);
+
 // Bytes of split partials the decode (standalone or fused) writes: the
 // caller's workspace must hold this many.
 size_t decode_workspace_bytes(const Dims &dm, int batch, int max_k);

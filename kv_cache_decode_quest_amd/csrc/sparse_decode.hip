@@ -462,6 +462,64 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
       [&] { return min(num_sel[row], max_k); }, partial);
 }
 
+// The live-split form of the bf16 decode: the grid (kLiveGrid work-groups)
+// takes only the splits that hold selected pages.  Every work-group counts
+// each row's live splits from the selection counts, scans them into LDS
+// (units_end[x] = live splits of rows 0..x), and attends live splits b, b +
+// grid, b + 2 grid, ... mapped back to (row, split) by a binary search over
+// the scan.  Dead splits are never visited and write no partial; the merge
+// reads only the live ones.  A ragged batch, whose grid in the per-(row,
+// split) form is sized by its longest row, then spreads the real work evenly.
+template <int D, int P, bool kPack>
+__global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
+    int rows, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k,
+    int n_split, int pps, float scale2, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
+    const int32_t *__restrict__ sel_pages, const int32_t *__restrict__ num_sel,
+    float *__restrict__ partial) {
+  __shared__ uint32_t units_end[kLiveRows];
+  __shared__ uint32_t wave_total[kDecodeWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto units_of = [&](int x) -> uint32_t {
+    const int k = min(num_sel[x], max_k);
+    return k > 0 ? (uint32_t)((k + pps - 1) / pps) : 0u;
+  };
+  // inclusive scan of the rows' live splits: thread t owns rows 2t and 2t+1
+  static_assert(2 * kDecodeWaves * 64 >= kLiveRows, "two rows per thread");
+  const int x0 = 2 * threadIdx.x;
+  const uint32_t u0 = x0 < rows ? units_of(x0) : 0u;
+  const uint32_t u1 = x0 + 1 < rows ? units_of(x0 + 1) : 0u;
+  const uint32_t incl = wave_incl_sum(u0 + u1);
+  if (lane == 63) wave_total[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < kDecodeWaves; ++w) before += w < wave ? wave_total[w] : 0u;
+  if (x0 < rows) units_end[x0] = before + incl - u1;
+  if (x0 + 1 < rows) units_end[x0 + 1] = before + incl;
+  __syncthreads();
+  const uint32_t total = units_end[rows - 1];
+  for (uint32_t u = blockIdx.x; u < total; u += gridDim.x) {
+    // the row holding live split u: the first x with units_end[x] > u
+    int lo = 0, hi = rows - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (units_end[mid] > u) hi = mid;
+      else lo = mid + 1;
+    }
+    const int row = lo;
+    const int split = (int)(u - (row > 0 ? units_end[row - 1] : 0u));
+    // the previous split's work-group merge has finished reading its LDS
+    if (u != blockIdx.x) __syncthreads();
+    const int32_t *sel = sel_pages + (int64_t)row * max_k;
+    decode_split<D, P, kPack, kDecodeWaves>(
+        row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
+        v_cache, page_table, [&](int r) { return ctx_lens[r]; }, [&](int i) { return sel[i]; },
+        [&] { return min(num_sel[row], max_k); }, partial);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Fused top-k + decode (bf16).  Every work-group of a row runs the row's
 // selection itself (1024 threads, the row's scores read from global memory),
@@ -651,15 +709,20 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
 // ---------------------------------------------------------------------------
 // merge: out[r][h] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
 // One work-group per (request, q head), one thread per channel.  Splits are
-// taken 16 at a time with all of their loads issued together (the max and
-// sum are the same address across the work-group), merged online.
+// taken 32 at a time with all of their loads issued together (the max and
+// sum are the same address across the work-group), merged online: a bf16
+// row has at most 32 splits, so its merge is one round trip to memory.
 // ---------------------------------------------------------------------------
-constexpr int kMergeChunk = 16;
+constexpr int kMergeChunk = 32;
 
-// Every split writes a partial (an empty one has max -inf and sum 0), so the
-// merge reads all n_split of them without waiting for the selection count.
+// A row's partials are its first ceil(count / pps) splits (the live ones;
+// the per-(row, split) kernels also write empty partials, max -inf and sum
+// 0, past them, while the live-split kernel writes nothing there).  The
+// partials are loaded for all n_split splits at once, without waiting for
+// the count, and the splits past the live ones are masked.
 template <typename T>
-__global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_split,
+__global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_split, int pps,
+                                                    int max_k, const int32_t *__restrict__ num_sel,
                                                     const float *__restrict__ partial,
                                                     T *__restrict__ out, int xcd_rows) {
   // r * Hq + h
@@ -668,16 +731,24 @@ __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_s
   const int r = hq / Hq, h = hq - r * Hq;
   const int g = h / G, hl = h - g * G;
   const int row = r * R + g;
-  const int live = n_split;
+  const int cnt = min(num_sel[row], max_k);
+  const int live = cnt > 0 ? min(n_split, (cnt + pps - 1) / pps) : 0;
   const int64_t stride = (int64_t)G * (D + 2);
-  const float *base = partial + (int64_t)row * n_split * stride + (int64_t)hl * (D + 2);
+  // A zero the compiler cannot see through, added to the base address: the
+  // statistics loads below then stay vector loads into vector registers (as
+  // uniform loads, 32 splits' statistics and addresses overflow the scalar
+  // registers).
+  int lane0;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(lane0));
+  const float *base =
+      partial + (int64_t)row * n_split * stride + (int64_t)hl * (D + 2) + lane0;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float M = -__builtin_huge_valf(), L = 0.f, a = 0.f;
-    for (int s0 = 0; s0 < live; s0 += kMergeChunk) {
+    for (int s0 = 0; s0 < n_split; s0 += kMergeChunk) {
       float mv[kMergeChunk], lv[kMergeChunk], av[kMergeChunk];
 #pragma unroll
       for (int u = 0; u < kMergeChunk; ++u) {
-        const float *p = base + (s0 + u < live ? s0 + u : s0) * stride;
+        const float *p = base + (s0 + u < n_split ? s0 + u : s0) * stride;
         mv[u] = p[D];
         lv[u] = p[D + 1];
         av[u] = p[d];
@@ -706,16 +777,18 @@ __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_s
   }
 }
 
-static hipError_t launch_merge(const Dims &dm, int batch, const DecodePlan &plan,
-                               const float *workspace, void *out, hipStream_t stream,
-                               int xcd_rows = 0) {
+static hipError_t launch_merge(const Dims &dm, int batch, const DecodePlan &plan, int max_k,
+                               const int32_t *num_sel, const float *workspace, void *out,
+                               hipStream_t stream, int xcd_rows = 0) {
   const unsigned mblocks = (unsigned)((long)batch * dm.Hq);
   if (dm.dtype == 1)
     hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, workspace, (uint16_t *)out, xcd_rows);
+                       dm.Gcols, dm.D, plan.n_split, plan.pages_per_split, max_k, num_sel,
+                       workspace, (uint16_t *)out, xcd_rows);
   else
     hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, workspace, (float *)out, xcd_rows);
+                       dm.Gcols, dm.D, plan.n_split, plan.pages_per_split, max_k, num_sel,
+                       workspace, (float *)out, xcd_rows);
   return hipGetLastError();
 }
 
@@ -727,7 +800,9 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
                          float *workspace, hipStream_t stream) {
   const DecodePlan plan = decode_plan(dm, batch, max_k);
   const float scale2 = sm_scale * kLog2e;
-  const unsigned blocks = (unsigned)((long)batch * dm.R * plan.n_split);
+  const unsigned blocks = (unsigned)decode_grid(dm, batch, max_k);
+  const bool live = decode_live(dm, batch);
+  const int rows = batch * dm.R;
   if (dm.dtype == 1) {
 #define QUEST_DECODE(DD, PP)                                                              \
   do {                                                                                    \
@@ -735,12 +810,22 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
     else QUEST_DECODE_G(DD, PP, false);                                                   \
   } while (0)
 #define QUEST_DECODE_G(DD, PP, PK)                                                        \
-  hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP, PK>), dim3(blocks), dim3(kDecodeWaves * 64), 0, stream, \
-                     dm.R, dm.Gcols, dm.Hkv, dm.gdiv, dm.pool, dm.max_pages, max_k,       \
-                     plan.n_split,                                                        \
-                     plan.pages_per_split, scale2, (const uint16_t *)q,                   \
-                     (const uint16_t *)k_cache, (const uint16_t *)v_cache, page_table,    \
-                     ctx_lens, sel_pages, num_sel, workspace)
+  do {                                                                                    \
+    if (live)                                                                             \
+      hipLaunchKernelGGL((sparse_decode_live_kernel<DD, PP, PK>), dim3(blocks),           \
+                         dim3(kDecodeWaves * 64), 0, stream, rows, dm.R, dm.Gcols, dm.Hkv, \
+                         dm.gdiv, dm.pool, dm.max_pages, max_k, plan.n_split,             \
+                         plan.pages_per_split, scale2, (const uint16_t *)q,               \
+                         (const uint16_t *)k_cache, (const uint16_t *)v_cache,            \
+                         page_table, ctx_lens, sel_pages, num_sel, workspace);            \
+    else                                                                                  \
+      hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP, PK>), dim3(blocks),           \
+                         dim3(kDecodeWaves * 64), 0, stream, dm.R, dm.Gcols, dm.Hkv,      \
+                         dm.gdiv, dm.pool, dm.max_pages, max_k, plan.n_split,             \
+                         plan.pages_per_split, scale2, (const uint16_t *)q,               \
+                         (const uint16_t *)k_cache, (const uint16_t *)v_cache,            \
+                         page_table, ctx_lens, sel_pages, num_sel, workspace);            \
+  } while (0)
     if (dm.D == 128 && dm.P == 16) QUEST_DECODE(128, 16);
     else if (dm.D == 128 && dm.P == 32) QUEST_DECODE(128, 32);
     else if (dm.D == 128 && dm.P == 64) QUEST_DECODE(128, 64);
@@ -763,7 +848,7 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_merge(dm, batch, plan, workspace, out, stream);
+  return launch_merge(dm, batch, plan, max_k, num_sel, workspace, out, stream);
 }
 
 hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const void *k_cache,
@@ -812,7 +897,7 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
 #undef QUEST_FUSED_G
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.n_split == 1) return err;
-  return launch_merge(dm, batch, plan, workspace, out, stream, xcd_rows);
+  return launch_merge(dm, batch, plan, max_k, num_sel, workspace, out, stream, xcd_rows);
 }
 
 hipError_t launch_decode_step(const Dims &dm, int batch, const void *q, const void *k_new,

@@ -442,3 +442,43 @@ def test_full_bench_shape_sampled(gpu_lib):
             assert ref["k"] == 256
             check_request_output(lay, q, r, sel[r], nsel[r], out[r], ref,
                                  f"bench step {step} r{r}")
+
+
+def test_live_splits_ignore_stale_partials(gpu_lib):
+    """The decode writes partials only for the splits that hold selected
+    pages, and the merge reads only those: with the workspace filled with NaN,
+    or holding a larger previous call's partials, a call with few (and no)
+    selected pages per row still matches the oracle's attention over its
+    selection; a request with no token outputs zeros."""
+    w = workloads.Workload("live_splits", 5, 32, 4, 128, 32, "bf16",
+                           ctx_list=(0, 40, 700, 2000, 3100), budget_tokens=4000, steps=1,
+                           seed=97, permute_pages=True, poison=float("nan"))
+    lay = Layer(w, DEV)
+    q, _, _ = lay.step_inputs(0)
+    max_k = 125
+    plan = quest.quest_sparse_decode_plan(lay.L, w.batch, max_k)
+    assert plan["num_splits"] > 4, plan
+    bufs = lay.buffers(max_k=max_k)
+    quest.quest_page_scores(lay.L, q, lay.kmeta, lay.pt, lay.ctx, bufs.scores)
+    sm = workloads.default_sm_scale(w)
+    outs = []
+    for budget, fill in ((4000, None), (64, None), (32, float("nan")), (1000, float("nan"))):
+        bud = torch.full((w.batch,), budget, dtype=torch.int32, device=DEV)
+        quest.quest_topk_pages(lay.L, bufs.scores, lay.ctx, bud, max_k, bufs.sel_pages,
+                               bufs.num_sel)
+        if fill is not None:
+            bufs.workspace.fill_(fill)
+        lay.attend(q, bufs)
+        torch.cuda.synchronize()
+        out = to_f64(bufs.out)
+        sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+        assert np.isfinite(out).all(), budget
+        assert np.all(out[0] == 0.0) and np.all(nsel[0] == 0)
+        for r in range(1, w.batch):
+            gpu_sel = [np.asarray(sel[r, g, :nsel[r, g]], np.int32) for g in range(w.num_kv_heads)]
+            want = oracle.request_attend(lay.shape, np.ascontiguousarray(to_oracle(q[r])),
+                                         lay.host[0], lay.host[1], lay.pt_host[r],
+                                         int(lay.ctx[r]), gpu_sel, sm)
+            check_out(out[r], want, torch.bfloat16, f"live splits budget {budget} r{r}")
+        outs.append(out)
+    log(f"live splits: plan {plan}")
