@@ -2,12 +2,13 @@
  * quest.h -- C ABI of libquest.so: Quest query-aware sparse decode attention
  * over a paged KV cache, for AMD Instinct MI355X (gfx950).
  *
- * The method.  Quest (Tang et al., "Quest: Query-Aware Sparsity for Efficient
- * Long-Context LLM Inference", ICML 2024) keeps, per KV page, the elementwise
- * minimum and maximum of the page's keys.  At each decode step the current
- * query gives every page an upper bound on q.k over that min/max box, the
- * best pages within a token budget are selected per KV head, and attention
- * runs over those pages only.
+ * The method.  The pages name Quest, its persistent page metadata and the
+ * two hooks it uses, but never write its arithmetic; this library computes
+ * the reading stated here and in each entry point below: per KV page, the
+ * elementwise minimum and maximum of the page's keys; at each decode step
+ * the current query gives every page an upper bound on q.k over that min/max
+ * box, the best pages within a token budget are selected per KV head, and
+ * attention runs over those pages only.
  *
  * Where the pages put it.  The Sparse-vLLM skill page "add-sparse-method"
  * (Placement Rules 2-4, Decision Rules) places persistent per-page metadata in
@@ -191,7 +192,10 @@ int quest_append_score(const quest_layout *layout, int32_t batch, const void *q,
                        const int32_t *page_table, void *k_cache, void *v_cache,
                        void *kmeta, int32_t group_reduce, float *scores, void *stream);
 
-/* build_decode_view, part 2: k_r = min(max_k, clamp(floor(budget_tokens[r] /
+/* build_decode_view, part 2 (Sparse-vLLM "add-sparse-method", Placement
+ * Rules 4: the decode view is built from the current layer's q; SparseEngine
+ * digest, Method key points: Quest's query-relevant page selection):
+ * k_r = min(max_k, clamp(floor(budget_tokens[r] /
  * P), 1, n_r)) pages per (request, selection row), n_r = ceil(ctx_lens[r]/P);
  * k_r = 0 when ctx_lens[r] == 0.  The k_r pages with the largest scores are
  * selected; equal scores go to the lower logical page (-0.0 equals +0.0).

@@ -3,6 +3,8 @@
 // call, so the C ABI can size workspaces and report plans without a GPU.
 #include "quest_plan.h"
 
+#include <stdint.h>
+
 #include <algorithm>
 
 namespace quest {
@@ -77,7 +79,9 @@ DecodePlan fused_plan(const Dims &dm, int batch, int max_k) {
   long pps = (max_k + cap - 1) / cap;
   pps = (pps + per_round - 1) / per_round * per_round;
   DecodePlan p;
-  p.pages_per_split = (int)pps;
+  // a split this long is never fused (more than kMaxFusedPages); the clamp
+  // only keeps the reported size from wrapping when max_k nears INT32_MAX
+  p.pages_per_split = (int)std::min(pps, (long)INT32_MAX);
   p.n_split = (int)((max_k + pps - 1) / pps);
   return p;
 }

@@ -16,11 +16,12 @@
  *    Method key points: Quest registers query-relevant page selection; the
  *    cache manager owns KV representation, physical layout, position mapping
  *    and metadata; the attention view hands explicit KV to the backend.
- *  - The Quest method itself (Tang et al., "Quest: Query-Aware Sparsity for
- *    Efficient Long-Context LLM Inference", ICML 2024): per page the
- *    elementwise min and max of its keys; per page the upper bound
- *    sum_d max(q_d*min_d, q_d*max_d) of q.k over any key inside that box; the
- *    top-k pages by that bound within a token budget; attention over them.
+ *  - The reading of Quest's arithmetic that this oracle and the library both
+ *    follow (the pages name the method, its page metadata and its hooks, but
+ *    never write its formulas): per page the elementwise min and max of its
+ *    keys; per page the upper bound sum_d max(q_d*min_d, q_d*max_d) of q.k
+ *    over any key inside that box; the top-k pages by that bound within a
+ *    token budget; attention over them.
  *
  * Every step is written as its definition, in fp64, with loops in the order a
  * reader checks by eye.  Inputs are upcast exactly (bf16 and fp32 values are

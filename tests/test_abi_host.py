@@ -286,6 +286,8 @@ def test_topk_sparse_decode_fused_rule(lib):
     assert not quest.quest_topk_sparse_decode_fused(bench, 65, 128)     # 260 rows
     assert quest.quest_topk_sparse_decode_fused(layout(selection=1), 8, 256)   # 256 q-head rows
     assert not quest.quest_topk_sparse_decode_fused(layout(selection=1), 8, 257)  # 288 pages
+    # a split past INT32_MAX pages (256 rows, max_k near INT32_MAX) is not fused
+    assert not quest.quest_topk_sparse_decode_fused(layout(selection=1), 8, 2 ** 31 - 1)
     assert not quest.quest_topk_sparse_decode_fused(layout(page_size=32), 1, 16)
     assert not quest.quest_topk_sparse_decode_fused(layout(page_size=8), 1, 16)
     assert quest.quest_topk_sparse_decode_fused(layout(head_dim=64, page_size=64), 1, 16)
