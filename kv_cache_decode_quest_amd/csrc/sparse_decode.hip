@@ -90,28 +90,61 @@ struct PageRegs {
   uint2 v[TT][NT];
 };
 
-// K (token-major): lane (col, grp) takes token tt*16 + col, channels
-// c*32 + 8*grp .. +7 -- its A operand of S = K q^T.
+// Which token a row of a 16-token tile holds.  Pages of 32 and 64 tokens are
+// attended in pairs of tiles (32 tokens): in a pair's first tile, matrix row i
+// holds the pair's token 8*(i/4) + i%4, in its second tile token
+// 8*(i/4) + 4 + i%4.  The four logits lane (col, grp) then gets from each
+// tile of the pair (rows 4*grp .. +3) are the pair's tokens 8*grp .. 8*grp + 7
+// in order: the 8 consecutive tokens of one channel that the lane loads as 16
+// contiguous bytes of the dim-major V page, and the K slots of one
+// v_mfma_f32_16x16x32_bf16 of O^T += V^T P^T.  Pages of 16 tokens (one tile)
+// keep row i = token i.
+template <int TT>
+__device__ __forceinline__ int k_row_token(int tt, int row) {
+  return TT >= 2 ? 32 * (tt >> 1) + 8 * (row >> 2) + 4 * (tt & 1) + (row & 3) : tt * 16 + row;
+}
+// The first of the four tokens lane slot group `tok0` = 4*grp holds in tile tt
+// (the logits of S and the V values of the same lane both follow it).
+template <int TT>
+__device__ __forceinline__ int lane_token0(int tt, int tok0) {
+  return TT >= 2 ? 32 * (tt >> 1) + 2 * tok0 + 4 * (tt & 1) : tt * 16 + tok0;
+}
+
+// K (token-major): lane (col, grp) takes the token of row col of tile tt,
+// channels c*32 + 8*grp .. +7 -- its A operand of S = K q^T.
 template <int D, int P>
 __device__ __forceinline__ void load_k(PageRegs<D, P> &pr, const uint16_t *__restrict__ kp,
                                        int col, int grp) {
+  constexpr int TT = PageRegs<D, P>::TT;
 #pragma unroll
-  for (int tt = 0; tt < PageRegs<D, P>::TT; ++tt)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int c = 0; c < PageRegs<D, P>::KC; ++c)
-      pr.k[tt][c] = *(const uint4 *)(kp + (tt * 16 + col) * D + c * 32 + grp * 8);
+      pr.k[tt][c] = *(const uint4 *)(kp + k_row_token<TT>(tt, col) * D + c * 32 + grp * 8);
 }
 
-// V (dim-major): lane (col, grp) takes channel nt*16 + col, tokens
-// tt*16 + 4*grp .. +3 -- its A operand of O^T = V^T P^T.
+// V (dim-major): lane (col, grp) takes channel nt*16 + col: one tile, tokens
+// 4*grp .. +3 (8 bytes); a pair of tiles, the pair's tokens 8*grp .. +7 (16
+// bytes, the first four for the pair's first tile) -- its A operand of
+// O^T = V^T P^T.
 template <int D, int P>
 __device__ __forceinline__ void load_v(PageRegs<D, P> &pr, const uint16_t *__restrict__ vp,
                                        int col, int grp) {
+  constexpr int TT = PageRegs<D, P>::TT;
+  if constexpr (TT >= 2) {
 #pragma unroll
-  for (int tt = 0; tt < PageRegs<D, P>::TT; ++tt)
+    for (int pp = 0; pp < TT / 2; ++pp)
+#pragma unroll
+      for (int nt = 0; nt < PageRegs<D, P>::NT; ++nt) {
+        const uint4 w = *(const uint4 *)(vp + (nt * 16 + col) * P + pp * 32 + grp * 8);
+        pr.v[2 * pp][nt] = make_uint2(w.x, w.y);
+        pr.v[2 * pp + 1][nt] = make_uint2(w.z, w.w);
+      }
+  } else {
 #pragma unroll
     for (int nt = 0; nt < PageRegs<D, P>::NT; ++nt)
-      pr.v[tt][nt] = *(const uint2 *)(vp + (nt * 16 + col) * P + tt * 16 + grp * 4);
+      pr.v[0][nt] = *(const uint2 *)(vp + (nt * 16 + col) * P + grp * 4);
+  }
 }
 
 // 8-token pages: a 16-token tile holds page a in tokens 0..7 and page b in
@@ -150,8 +183,10 @@ __device__ __forceinline__ void load_v_half(PageRegs<D, 16> &pr, const uint16_t 
 // lane col - 8 feeds the hi weights: one matrix-core step per tile instead of
 // two, and accumulator columns h and h + 8 add up to head h.
 //
-// Validity: token tt*16 + tok0 + e of the lane takes part iff it is below
-// lim[u]; full[u] (uniform) says every token of tile-page u does.
+// Validity: token lane_token0(tt, tok0) + e of the lane takes part iff it is
+// below lim[u]; full[u] (uniform) says every token of tile-page u does.
+// Pages of two or more tiles multiply P.V a pair of tiles (32 tokens) at a
+// time on v_mfma_f32_16x16x32_bf16 (see k_row_token).
 template <int D, int P, int NPG, bool kPack>
 __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
                                              const bool *full, int tok0, const bf16x8 *qop,
@@ -184,7 +219,7 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s[u][tt][e] = tt * 16 + tok0 + e < lim[u] ? c4[e] * scale2 : kNegInf;
+          s[u][tt][e] = lane_token0<PR::TT>(tt, tok0) + e < lim[u] ? c4[e] * scale2 : kNegInf;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) pmax = fmaxf(pmax, s[u][tt][e]);
@@ -232,7 +267,7 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
     if (!full[u]) {
 #pragma unroll
       for (int tt = 0; tt < PR::TT; ++tt) {
-        const int t0 = tt * 16 + tok0;
+        const int t0 = lane_token0<PR::TT>(tt, tok0);
         const uint32_t mx = (t0 + 0 < lim[u] ? 0x0000ffffu : 0u) |
                             (t0 + 1 < lim[u] ? 0xffff0000u : 0u);
         const uint32_t my = (t0 + 2 < lim[u] ? 0x0000ffffu : 0u) |
@@ -244,17 +279,42 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
         }
       }
     }
+    if constexpr (PR::TT >= 2) {
+      // a pair of tiles per product: K slots 8*grp + j are the pair's tokens
+      // 8*grp + j for both operands (tile 2pp gives j < 4, tile 2pp+1 j >= 4)
+      auto pair = [](s16x4 a, s16x4 b) {
+        return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, a).x,
+                                                     __builtin_bit_cast(uint2, a).y,
+                                                     __builtin_bit_cast(uint2, b).x,
+                                                     __builtin_bit_cast(uint2, b).y));
+      };
 #pragma unroll
-    for (int tt = 0; tt < PR::TT; ++tt) {
+      for (int pp = 0; pp < PR::TT / 2; ++pp) {
+        const bf16x8 whi = pair(phi[u][2 * pp], phi[u][2 * pp + 1]);
+        const bf16x8 wlo = pair(plo[u][2 * pp], plo[u][2 * pp + 1]);
+#pragma unroll
+        for (int nt = 0; nt < PR::NT; ++nt) {
+          const uint2 v0 = pg[u].v[2 * pp][nt], v1 = pg[u].v[2 * pp + 1][nt];
+          const bf16x8 vv = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          if constexpr (kPack) {
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, col < 8 ? whi : wlo, acc[nt],
+                                                              0, 0, 0);
+          } else {
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, whi, acc[nt], 0, 0, 0);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, wlo, acc[nt], 0, 0, 0);
+          }
+        }
+      }
+    } else {
 #pragma unroll
       for (int nt = 0; nt < PR::NT; ++nt) {
-        const s16x4 vv = __builtin_bit_cast(s16x4, pg[u].v[tt][nt]);
+        const s16x4 vv = __builtin_bit_cast(s16x4, pg[u].v[0][nt]);
         if constexpr (kPack) {
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, col < 8 ? phi[u][tt] : plo[u][tt],
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, col < 8 ? phi[u][0] : plo[u][0],
                                                               acc[nt], 0, 0, 0);
         } else {
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, phi[u][tt], acc[nt], 0, 0, 0);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, plo[u][tt], acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, phi[u][0], acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, plo[u][0], acc[nt], 0, 0, 0);
         }
       }
     }
