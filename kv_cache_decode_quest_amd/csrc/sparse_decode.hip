@@ -328,8 +328,12 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
 // max_k; ctx_of(r) request r's length.  Writes the split's partial (acc, m,
 // l) per head, or, with final_out (a row of one split), the row's output
 // acc / l in bf16 directly — what the merge would compute from that single
-// partial, bit for bit.
-template <int D, int P, bool kPack, int kWaves, typename Ids, typename Count, typename CtxOf>
+// partial, bit for bit.  kAhead (splits of several rounds): the next round's
+// page ids and page-table entries are looked up right after the current
+// round's K/V loads are issued, so each later round starts its K/V loads at
+// once; results are the same bit for bit.
+template <int D, int P, bool kPack, int kWaves, bool kAhead, typename Ids, typename Count,
+          typename CtxOf>
 __device__ __forceinline__ void decode_split(
     int row, int split, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages,
     int max_k, int n_split, int pps, float scale2, const uint16_t *__restrict__ q,
@@ -410,23 +414,36 @@ __device__ __forceinline__ void decode_split(
   float m = -__builtin_huge_valf();     // running max of head `col` (base-2 logits)
   float l = 0.f;                        // running sum of head `col`
 
+  // The physical page and valid-token count of selected position i with
+  // logical id j (slots past the split, or with an id outside the request,
+  // re-read the split's first page, a cache hit, with no valid token).
+  auto lookup = [&](int i, int j, int64_t &ph_out, int &valid_out) {
+    const bool live = i < last && j >= 0 && j < n;
+    const int jj = live ? j : ((jfirst >= 0 && jfirst < n) ? jfirst : 0);
+    const int64_t ph = pt[jj];
+    const bool ok = ph >= 0 && ph < pool;
+    ph_out = ok ? ph : 0;
+    valid_out = (live && ok) ? min(P, ctx - j * P) : 0;
+  };
+  int64_t next_phys[PPW];
+  int next_valid[PPW];
   // Each round, wave w takes PPW consecutive selected pages.
   for (int base = first; base < last; base += kRound) {
     const int p0 = base + wave * PPW;
     int64_t phys[PPW];
     int valid[PPW];
+    if (!kAhead || base == first) {
 #pragma unroll
-    for (int u = 0; u < PPW; ++u) {
-      const int i = p0 + u;
-      const int j = (base == first) ? sel0[u] : ids(i < last ? i : last - 1);
-      // slots past the split, or with an id outside the request, re-read the
-      // split's first page (a cache hit) with no valid token
-      const bool live = i < last && j >= 0 && j < n;
-      const int jj = live ? j : ((jfirst >= 0 && jfirst < n) ? jfirst : 0);
-      const int64_t ph = pt[jj];
-      const bool ok = ph >= 0 && ph < pool;
-      phys[u] = ok ? ph : 0;
-      valid[u] = (live && ok) ? min(P, ctx - j * P) : 0;
+      for (int u = 0; u < PPW; ++u) {
+        const int i = p0 + u;
+        lookup(i, (base == first) ? sel0[u] : ids(i < last ? i : last - 1), phys[u], valid[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < PPW; ++u) {
+        phys[u] = next_phys[u];
+        valid[u] = next_valid[u];
+      }
     }
     // per update group: all K, then all V (the logits need only the K loads)
     constexpr int UPG = kPagesPerUpdate < NV ? kPagesPerUpdate : NV;
@@ -448,6 +465,15 @@ __device__ __forceinline__ void decode_split(
     }
     // keep every load of the round ahead of the first wait on any of them
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kAhead) {
+      // the next round's lookups (unconditional, clamped; unused after the
+      // last round), in flight while this round's pages arrive
+#pragma unroll
+      for (int u = 0; u < PPW; ++u) {
+        const int i = p0 + kRound + u;
+        lookup(i, ids(i < last ? i : last - 1), next_phys[u], next_valid[u]);
+      }
+    }
     // validity per tile page: this lane's tokens 4*grp .. +3 lie in page
     // 2v + (grp >> 1) of a half tile, as slots 4*(grp & 1) .. +3
     int lim[NV];
@@ -506,7 +532,7 @@ __device__ __forceinline__ void decode_split(
   }
 }
 
-template <int D, int P, bool kPack>
+template <int D, int P, bool kPack, bool kAhead>
 __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
     int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k, int n_split,
     int pps, float scale2, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
@@ -516,7 +542,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
   const int split = blockIdx.x % n_split;
   const int row = blockIdx.x / n_split;
   const int32_t *sel = sel_pages + (int64_t)row * max_k;
-  decode_split<D, P, kPack, kDecodeWaves>(
+  decode_split<D, P, kPack, kDecodeWaves, kAhead>(
       row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
       v_cache, page_table, [&](int r) { return ctx_lens[r]; }, [&](int i) { return sel[i]; },
       [&] { return min(num_sel[row], max_k); }, partial);
@@ -573,7 +599,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
     // the previous split's work-group merge has finished reading its LDS
     if (u != blockIdx.x) __syncthreads();
     const int32_t *sel = sel_pages + (int64_t)row * max_k;
-    decode_split<D, P, kPack, kDecodeWaves>(
+    decode_split<D, P, kPack, kDecodeWaves, false>(
         row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
         v_cache, page_table, [&](int r) { return ctx_lens[r]; }, [&](int i) { return sel[i]; },
         [&] { return min(num_sel[row], max_k); }, partial);
@@ -595,7 +621,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 2 * kDecodeWaves;
 static_assert(kFusedWaves * kWave == kTopkThreads, "the fused kernel runs the 1024-thread selection");
-template <int D, int P, bool kPack>
+template <int D, int P, bool kPack, bool kAhead>
 __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
     int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k, int n_split,
     int pps, int n_sink, int n_recent, float scale2, const uint16_t *__restrict__ q,
@@ -642,7 +668,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_mfma_kernel(
   else select_row<true, false>(sh, s, sv, span, n, k, 0, 0, emit);
   __syncthreads();
   // any index is clamped into the list
-  decode_split<D, P, kPack, kFusedWaves>(
+  decode_split<D, P, kPack, kFusedWaves, kAhead>(
       row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
       v_cache, page_table, [&](int) { return ctx; },
       [&](int i) {
@@ -863,6 +889,9 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   const unsigned blocks = (unsigned)decode_grid(dm, batch, max_k);
   const bool live = decode_live(dm, batch);
   const int rows = batch * dm.R;
+  // splits of several rounds look the next round's pages up ahead
+  const bool ahead =
+      dm.dtype == 1 && plan.pages_per_split > kDecodeWaves * pages_per_wave(dm.P, dm.D);
   if (dm.dtype == 1) {
 #define QUEST_DECODE(DD, PP)                                                              \
   do {                                                                                    \
@@ -878,8 +907,15 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
                          plan.pages_per_split, scale2, (const uint16_t *)q,               \
                          (const uint16_t *)k_cache, (const uint16_t *)v_cache,            \
                          page_table, ctx_lens, sel_pages, num_sel, workspace);            \
+    else if (ahead)                                                                       \
+      hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP, PK, true>), dim3(blocks),     \
+                         dim3(kDecodeWaves * 64), 0, stream, dm.R, dm.Gcols, dm.Hkv,      \
+                         dm.gdiv, dm.pool, dm.max_pages, max_k, plan.n_split,             \
+                         plan.pages_per_split, scale2, (const uint16_t *)q,               \
+                         (const uint16_t *)k_cache, (const uint16_t *)v_cache,            \
+                         page_table, ctx_lens, sel_pages, num_sel, workspace);            \
     else                                                                                  \
-      hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP, PK>), dim3(blocks),           \
+      hipLaunchKernelGGL((sparse_decode_mfma_kernel<DD, PP, PK, false>), dim3(blocks),    \
                          dim3(kDecodeWaves * 64), 0, stream, dm.R, dm.Gcols, dm.Hkv,      \
                          dm.gdiv, dm.pool, dm.max_pages, max_k, plan.n_split,             \
                          plan.pages_per_split, scale2, (const uint16_t *)q,               \
@@ -935,18 +971,27 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
   // XCD-major keeps the splits of a row, and the merge of its heads, on one
   // XCD, where the score row and the partials stay in that XCD's L2.
   const int xcd_rows = xcd_placement(blocks, plan.n_split, mblocks);
+  // splits of several rounds look the next round's pages up ahead (a round:
+  // 16 waves of half the 8-wave kernel's pages)
+  const bool ahead = plan.pages_per_split > kDecodeWaves * pages_per_wave(dm.P, dm.D);
 #define QUEST_FUSED(DD, PP)                                                               \
   do {                                                                                    \
     if (dm.Gcols <= 8) QUEST_FUSED_G(DD, PP, true);                                       \
     else QUEST_FUSED_G(DD, PP, false);                                                    \
   } while (0)
 #define QUEST_FUSED_G(DD, PP, PK)                                                         \
-  hipLaunchKernelGGL((topk_decode_mfma_kernel<DD, PP, PK>), dim3(blocks), dim3(kTopkThreads), \
-                     0, stream, dm.R, dm.Gcols, dm.Hkv, dm.gdiv, dm.pool, dm.max_pages,    \
-                     max_k, plan.n_split, plan.pages_per_split, n_sink, n_recent, scale2,  \
-                     (const uint16_t *)q, (const uint16_t *)k_cache,                      \
-                     (const uint16_t *)v_cache, page_table, ctx_lens, scores,             \
-                     budget_tokens, sel_pages, num_sel, workspace, (uint16_t *)out, xcd_rows)
+  do {                                                                                    \
+    if (ahead) QUEST_FUSED_A(DD, PP, PK, true);                                           \
+    else QUEST_FUSED_A(DD, PP, PK, false);                                                \
+  } while (0)
+#define QUEST_FUSED_A(DD, PP, PK, AH)                                                     \
+  hipLaunchKernelGGL((topk_decode_mfma_kernel<DD, PP, PK, AH>), dim3(blocks),             \
+                     dim3(kTopkThreads), 0, stream, dm.R, dm.Gcols, dm.Hkv, dm.gdiv,      \
+                     dm.pool, dm.max_pages, max_k, plan.n_split, plan.pages_per_split,    \
+                     n_sink, n_recent, scale2, (const uint16_t *)q,                       \
+                     (const uint16_t *)k_cache, (const uint16_t *)v_cache, page_table,    \
+                     ctx_lens, scores, budget_tokens, sel_pages, num_sel, workspace,      \
+                     (uint16_t *)out, xcd_rows)
   if (dm.D == 128 && dm.P == 16) QUEST_FUSED(128, 16);
   else if (dm.D == 64 && dm.P == 8) QUEST_FUSED(64, 8);
   else if (dm.D == 64 && dm.P == 16) QUEST_FUSED(64, 16);
@@ -955,6 +1000,7 @@ hipError_t launch_topk_decode(const Dims &dm, int batch, const void *q, const vo
   else return hipErrorInvalidValue;
 #undef QUEST_FUSED
 #undef QUEST_FUSED_G
+#undef QUEST_FUSED_A
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.n_split == 1) return err;
   return launch_merge(dm, batch, plan, max_k, num_sel, workspace, out, stream, xcd_rows);
