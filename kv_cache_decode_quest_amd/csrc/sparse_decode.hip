@@ -552,10 +552,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
 // takes only the splits that hold selected pages.  Every work-group counts
 // each row's live splits from the selection counts, scans them into LDS
 // (units_end[x] = live splits of rows 0..x), and attends live splits b, b +
-// grid, b + 2 grid, ... mapped back to (row, split) by a binary search over
-// the scan.  Dead splits are never visited and write no partial; the merge
-// reads only the live ones.  A ragged batch, whose grid in the per-(row,
-// split) form is sized by its longest row, then spreads the real work evenly.
+// A, b + 2 A, ... mapped back to (row, split) by a binary search over the
+// scan.  Dead splits are never visited and write no partial; the merge reads
+// only the live ones.  A ragged batch, whose grid in the per-(row, split)
+// form is sized by its longest row, then spreads the real work evenly.
+// A is the number of work-groups that take part: with U live splits and a
+// grid of N, every one of A = ceil(U / ceil(U / N)) work-groups attends
+// ceil(U / N) splits (the last one fewer) and the others exit.  The splits
+// stream at the HBM rate while every work-group has one in flight, so equal
+// shares keep the chip busy to the end; with all N taking part, the last
+// round of splits would run on a fraction of the CUs (U = 1376, N = 256:
+// 96 work-groups for the last 11 us of a 78 us launch).
 template <int D, int P, bool kPack>
 __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
     int rows, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k,
@@ -586,7 +593,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
   if (x0 + 1 < rows) units_end[x0 + 1] = before + incl;
   __syncthreads();
   const uint32_t total = units_end[rows - 1];
-  for (uint32_t u = blockIdx.x; u < total; u += gridDim.x) {
+  const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
+  const uint32_t active = per > 0 ? (total + per - 1) / per : 0u;
+  for (uint32_t u = blockIdx.x; u < total && blockIdx.x < active; u += active) {
     // the row holding live split u: the first x with units_end[x] > u
     int lo = 0, hi = rows - 1;
     while (lo < hi) {
