@@ -468,13 +468,14 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "page_scores_bench128k_traffic.jso
 COPY_KERNEL = "copy"    # the runtime's buffer-copy kernel: the known-size calibration
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM traffic of the scoring kernel from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source (else None)."""
+    summary, if it was taken on this workload and on the current kernel
+    source (else None)."""
     if not os.path.exists(TRAFFIC_JSON):
         return None
     rec = json.load(open(TRAFFIC_JSON))
-    if rec.get("source_hash") != source_hash(SCORE_SOURCES):
+    if rec.get("workload") != workload or rec.get("source_hash") != source_hash(SCORE_SOURCES):
         return None
     return rec.get("bytes_per_launch")
 
@@ -895,7 +896,7 @@ def main():
         (2 if w.dtype == "bf16" else 4)
     score_gbps = score_bytes / (score_us * 1e-6) / 1e9
     stream = stream_probe(copies, n_launch)
-    traffic = measured_traffic()
+    traffic = measured_traffic(w.name)
     if args.calibrate_copy_mib:
         src = torch.ones(args.calibrate_copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

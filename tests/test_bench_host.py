@@ -65,16 +65,19 @@ def test_traffic_from_pmc_scales_by_the_copy(tmp_path):
 
 
 def test_traffic_reported_only_for_the_current_source(tmp_path, monkeypatch):
-    rec = {"bytes_per_launch": 123.0, "source_hash": bench.source_hash(bench.SCORE_SOURCES)}
+    rec = {"bytes_per_launch": 123.0, "workload": "bench128k",
+           "source_hash": bench.source_hash(bench.SCORE_SOURCES)}
     path = tmp_path / "traffic.json"
     path.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(path))
-    assert bench.measured_traffic() == 123.0
+    assert bench.measured_traffic("bench128k") == 123.0
+    # a record of another workload's launches says nothing about this one's
+    assert bench.measured_traffic("ragged") is None
     rec["source_hash"] = "0" * 16
     path.write_text(json.dumps(rec))
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic("bench128k") is None
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "missing.json"))
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic("bench128k") is None
 
 
 def test_committed_traffic_record_is_consistent():
