@@ -53,8 +53,10 @@ DecodePlan decode_plan(const Dims &dm, int batch, int max_k);
 
 // The bf16 standalone decode runs only the splits that hold selected pages
 // ("live" splits: ceil(count / pages_per_split) of each row): every
-// work-group lists them from the rows' selection counts in LDS and takes
-// every kLiveGrid-th one.  Used while the rows' list fits (kLiveRows rows).
+// work-group lists them from the rows' selection counts in LDS; with U live
+// splits the first A = ceil(U / ceil(U / kLiveGrid)) work-groups take equal
+// shares (work-group b: splits b, b + A, b + 2A, ...) and the rest exit.
+// Used while the rows' list fits (kLiveRows rows).
 // kLiveGrid is one work-group on each of an MI355X's 256 CUs: the 8-wave
 // decode needs about 200 registers per lane (two waves per SIMD), so one
 // work-group is resident per CU and the whole grid runs at once.
