@@ -780,9 +780,21 @@ def main():
         m = s // NL
         run_step(layers[s % NL], step_bufs[s], s, inputs[s], ctx_b[m], ctx_a[m], budgets[m], sm)
 
+    def restore_all():
+        # Every copy's touched metadata rows back to their state before the
+        # first step.  Re-storing a token at its position rewrites the same
+        # K/V, but a page's min/max only restarts at slot 0: a pass that
+        # starts mid-page would otherwise see bounds that already hold the
+        # later steps' tokens, and score that page differently.  With this,
+        # every pass over the K steps (the eager one and each replay) sees
+        # the same state step by step.
+        for c in layers:
+            c.kmeta[touched] = saved
+
     log(f"warm-up: {W} steps, then one eager pass over the {K} steps")
     for s in range(W):
         rot_step(s % K)
+    restore_all()
     for s in range(K):
         rot_step(s)
     torch.cuda.synchronize()
@@ -792,6 +804,7 @@ def main():
     with torch.cuda.graph(graph):
         for s in range(K):
             rot_step(s)
+    restore_all()
     graph.replay()
     torch.cuda.synchronize()
     def same_as_eager():
@@ -801,6 +814,7 @@ def main():
     same = [same_as_eager()]
     log(f"timed: {K} steps replayed")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    restore_all()
     evict()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -816,6 +830,7 @@ def main():
     # spread of the per-step time; `value` is the first timed replay alone
     replay_ms = [total_s / K * 1e3]
     for _ in range(args.extra_replays):
+        restore_all()
         evict()
         ev[0].record()
         graph.replay()
