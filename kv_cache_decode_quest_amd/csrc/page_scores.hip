@@ -199,21 +199,25 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
 
 constexpr int kMaxGroup = 16;       // q heads per KV head the layout allows
 
-// fp32 path: one thread per page, the group's q in LDS.  Each term takes the
+// fp32 path: one thread per page, the group's q in LDS, padded with zero
+// rows to kG heads (the power of two at or above G) so the loop over heads
+// has no branch (a padded head's sum is never read).  Each term takes the
 // product on the side the sign of q selects; rounding is monotonic, so this
-// is the larger of the two rounded products.
+// is the larger of the two rounded products.  Every head sums over d in
+// order.
 // With cu_new non-null the request length is ctx_before + its new tokens
 // (the fused path, after a separate append launch), else ctx_lens.
+template <int kG>
 __global__ __launch_bounds__(256) void page_scores_valu_kernel(
     int Hkv, int G, int per_head, int D, int64_t pool, int P, int max_pages, int reduce,
     const float *__restrict__ q, const float *__restrict__ kmeta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
     const int32_t *__restrict__ cu_new, const int32_t *__restrict__ ctx_before,
     float *__restrict__ scores) {
-  extern __shared__ float q_lds[];     // [G][D]
+  extern __shared__ __align__(16) float q_lds[];     // [kG][D]
   const int g = blockIdx.y, r = blockIdx.z;
   const float *qg = q + ((int64_t)r * Hkv * G + (int64_t)g * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_lds[i] = qg[i];
+  for (int i = threadIdx.x; i < kG * D; i += blockDim.x) q_lds[i] = i < G * D ? qg[i] : 0.f;
   __syncthreads();
   const int ctx = cu_new ? ctx_before[r] + max(cu_new[r + 1] - cu_new[r], 0) : ctx_lens[r];
   const int n = pages_in(ctx, P, max_pages);
@@ -223,15 +227,42 @@ __global__ __launch_bounds__(256) void page_scores_valu_kernel(
   if (phys < 0 || phys >= pool) return;
   const float *lo = kmeta + (phys * Hkv + g) * 2 * D;
   const float *hi = lo + D;
-  // each metadata element is read once; every head sums over d in order
-  float u[kMaxGroup];
+  float u[kG];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) u[h] = 0.f;
-  for (int d = 0; d < D; ++d) {
-    const float a = lo[d], b = hi[d];
+  for (int h = 0; h < kG; ++h) u[h] = 0.f;
+  if ((((uintptr_t)kmeta) & 15u) == 0) {
+    // 16 channels of min and of max in flight at once (D is 64 or 128, a
+    // multiple of 16, and rows of 2D floats keep 16-byte alignment); q read
+    // 4 channels of a head at a time
+    for (int d0 = 0; d0 < D; d0 += 16) {
+      float4 la[4], ha[4];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < G) {
+      for (int i = 0; i < 4; ++i) {
+        la[i] = *(const float4 *)(lo + d0 + 4 * i);
+        ha[i] = *(const float4 *)(hi + d0 + 4 * i);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 qv[kG];
+#pragma unroll
+        for (int h = 0; h < kG; ++h) qv[h] = *(const float4 *)&q_lds[h * D + d0 + 4 * i];
+        const float a[4] = {la[i].x, la[i].y, la[i].z, la[i].w};
+        const float b[4] = {ha[i].x, ha[i].y, ha[i].z, ha[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int h = 0; h < kG; ++h) {
+            const float qd = e == 0 ? qv[h].x : (e == 1 ? qv[h].y : (e == 2 ? qv[h].z : qv[h].w));
+            u[h] += qd >= 0.f ? qd * b[e] : qd * a[e];
+          }
+        }
+      }
+    }
+  } else {
+    for (int d = 0; d < D; ++d) {
+      const float a = lo[d], b = hi[d];
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
         const float qd = q_lds[h * D + d];
         u[h] += qd >= 0.f ? qd * b : qd * a;
       }
@@ -239,7 +270,7 @@ __global__ __launch_bounds__(256) void page_scores_valu_kernel(
   }
   float v = reduce == 0 ? -__builtin_huge_valf() : 0.f;
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
+  for (int h = 0; h < kG; ++h) {
     if (h < G) {
       if (per_head) scores[((int64_t)(r * Hkv + g) * G + h) * max_pages + j] = u[h];
       v = reduce == 0 ? fmaxf(v, u[h]) : v + u[h];
@@ -269,12 +300,18 @@ static hipError_t launch_scores(const Dims &dm, int batch, const void *q, void *
 #undef QUEST_SCORES
   } else {
     dim3 grid((unsigned)((dm.max_pages + 255) / 256), (unsigned)dm.Hkv, (unsigned)batch);
-    hipLaunchKernelGGL(page_scores_valu_kernel, grid, dim3(256),
-                       (size_t)dm.G * dm.D * sizeof(float), stream, dm.Hkv, dm.G,
-                       (int)dm.per_head(), dm.D,
-                       dm.pool, dm.P, dm.max_pages, reduce, (const float *)q,
-                       (const float *)kmeta, page_table, ctx_lens,
-                       fused ? fa.cu_new : nullptr, fused ? fa.ctx_before : nullptr, scores);
+#define QUEST_SCORES32(KG)                                                                  \
+  hipLaunchKernelGGL(page_scores_valu_kernel<KG>, grid, dim3(256),                          \
+                     (size_t)(KG) * dm.D * sizeof(float), stream, dm.Hkv, dm.G,             \
+                     (int)dm.per_head(), dm.D, dm.pool, dm.P, dm.max_pages, reduce,         \
+                     (const float *)q, (const float *)kmeta, page_table, ctx_lens,          \
+                     fused ? fa.cu_new : nullptr, fused ? fa.ctx_before : nullptr, scores)
+    if (dm.G <= 1) QUEST_SCORES32(1);
+    else if (dm.G <= 2) QUEST_SCORES32(2);
+    else if (dm.G <= 4) QUEST_SCORES32(4);
+    else if (dm.G <= 8) QUEST_SCORES32(8);
+    else QUEST_SCORES32(kMaxGroup);
+#undef QUEST_SCORES32
   }
   return hipGetLastError();
 }
