@@ -201,10 +201,11 @@ constexpr int kMaxGroup = 16;       // q heads per KV head the layout allows
 
 // fp32 path: one thread per page, the group's q in LDS, padded with zero
 // rows to kG heads (the power of two at or above G) so the loop over heads
-// has no branch (a padded head's sum is never read).  Each term takes the
-// product on the side the sign of q selects; rounding is monotonic, so this
-// is the larger of the two rounded products.  Every head sums over d in
-// order.
+// has no branch (a padded head's sum is never read).  Each term is the
+// product on the side the sign of q selects (q * max for q >= 0, else
+// q * min), the larger of the two exact products, so the choice itself
+// rounds nothing; the compiler fuses it into the fp32 add (one rounding per
+// term).  Every head sums over d in order.
 // With cu_new non-null the request length is ctx_before + its new tokens
 // (the fused path, after a separate append launch), else ctx_lens.
 template <int kG>
