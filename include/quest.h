@@ -18,7 +18,7 @@
  * Inference Engine", Method key points) registers Quest's query-relevant page
  * selection as a lifecycle hook, lets each method's cache manager own KV
  * representation, physical layout, position mapping and metadata, and hands
- * the backend an explicit-KV attention view.  The four entry points below are
+ * the backend an explicit-KV attention view.  The entry points map onto
  * those steps:
  *     quest_append_kv      on_kv_stored: KV store + fused min/max refresh
  *     quest_page_scores    build_decode_view, part 1: per-page bounds from q
@@ -31,8 +31,9 @@
  * Conventions shared by every entry point
  *  - All buffers are device memory owned by the caller (the cache manager
  *    role).  The library allocates nothing, keeps no pointer after a call
- *    returns and holds no state between calls.  The layout struct is read
- *    during the call only.
+ *    returns and holds no state between calls (the one exception is the
+ *    library-owned scratch array of quest_decode_step_noalloc, described
+ *    there).  The layout struct is read during the call only.
  *  - Every call is asynchronous: it validates its arguments on the host,
  *    enqueues kernels on `stream` (a hipStream_t passed as void*, NULL for the
  *    null stream) and returns.  It never synchronises, allocates or copies
@@ -170,8 +171,9 @@ int quest_append_kv(const quest_layout *layout, int32_t batch,
  *   scores[r][g][j] = max_h U[h][j]   (group_reduce MAX) or sum_h (SUM).
  * With per-q-head selection there is no reduction: scores[r][h][j] = U[h][j]
  * for every q head h (group_reduce is still validated but has no effect).
- * Products of bf16 values are exact in fp32; sums are fp32 in an unspecified
- * order.  Entries j >= ceil(ctx/P) are not written. */
+ * Products of bf16 values are exact in fp32 (fp32 inputs: each product is
+ * fused into its fp32 add); sums are fp32 in an unspecified order.  Entries
+ * j >= ceil(ctx/P) are not written. */
 int quest_page_scores(const quest_layout *layout, int32_t batch,
                       const void *q, const void *kmeta,
                       const int32_t *page_table, const int32_t *ctx_lens,
