@@ -317,7 +317,8 @@ int quest_decode_step(const quest_layout *layout, int32_t batch, const void *q,
  * device's copy of the array, a host call that allocates nothing.
  * Limits: the call needs quest_sparse_decode_workspace_bytes(layout, batch,
  * max_k) <= QUEST_STATIC_SCRATCH_BYTES, else QUEST_ERR_SCRATCH with nothing
- * launched (at batch 8 x 4 KV heads, G 8, D 128: max_k up to 8192).
+ * launched (at 4 KV heads, G 8, D 128: any max_k up to batch 126, whose
+ * rows take at most 8 splits each).
  * Concurrency: every call on one GPU shares that GPU's array, and the array
  * keeps the last call's partials (their contents on entry do not matter;
  * nothing needs clearing).  Calls that may overlap on one GPU (several

@@ -14,11 +14,18 @@ namespace {
 // fp32: work-groups the plan aims for (the fp32 kernel walks its pages one at
 // a time, so its splits start at one page and the grid sets how many).
 constexpr long kTargetWorkGroups = 2048;
-// bf16: at most kPlanSplits splits per row, so long rows take several rounds
-// per split instead of multiplying the partials the merge reads (a dense
-// 8008-page row: 32 splits of 8 rounds); otherwise one round per split, the
-// unit the live-split decode spreads over its work-groups.
-constexpr long kPlanSplits = 32;
+// bf16: at most kPlanSplits splits per row, or as many as give every CU a
+// split when the batch has fewer than kLiveGrid / kPlanSplits rows, so long
+// rows take several rounds per split instead of multiplying the work-group
+// merges and the partials the merge kernel reads (a dense 8008-page row of
+// batch 8: 8 splits of 32 rounds; the ragged batch's longest rows, 383
+// pages of 32 tokens: 8 splits of 3 rounds); otherwise one round per split,
+// the unit the live-split decode spreads over its work-groups.  Measured on
+// the ragged batch, at most 4 / 6 / 8 / 12 / 32 splits per row: 130.3 /
+// 111.3 / 108.4 / 110.5 / 116.8 us per step; rows of up to 8 rounds (batch 8
+// x 128000 at a 4096-token budget, the 48-layer step, the 32k layer) keep
+// one round per split.
+constexpr long kPlanSplits = 8;
 
 // Shapes whose 16-wave decode fits the 128 registers a 1024-thread
 // work-group leaves each lane (the others spill, and stay two launches).
@@ -32,11 +39,14 @@ DecodePlan decode_plan(const Dims &dm, int batch, int max_k) {
   long pps;
   if (dm.dtype == 1) {
     // A round: the bf16 kernel's waves take pages_per_wave pages each at
-    // once.  One round per split, or as many as keep the splits within
-    // kPlanSplits.
+    // once.  One round per split, or as many as keep the splits within the
+    // cap.
     const long per_round = (long)kDecodeWaves * pages_per_wave(dm.P, dm.D);
     const long one_round = (max_k + per_round - 1) / per_round;
-    pps = per_round * ((one_round + kPlanSplits - 1) / kPlanSplits);
+    const long rows = (long)batch * dm.R;
+    const long cap = std::max(kPlanSplits,
+                              std::min((long)kMaxSplits, (kLiveGrid + rows - 1) / rows));
+    pps = per_round * ((one_round + cap - 1) / cap);
   } else {
     // fp32: one page per split, more only past the grid the plan aims for
     // (or kMaxSplits per row).

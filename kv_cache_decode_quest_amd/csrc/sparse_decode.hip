@@ -562,8 +562,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_mfma_kernel(
 // stream at the HBM rate while every work-group has one in flight, so equal
 // shares keep the chip busy to the end; with all N taking part, the last
 // round of splits would run on a fraction of the CUs (U = 1376, N = 256:
-// 96 work-groups for the last 11 us of a 78 us launch).
-template <int D, int P, bool kPack>
+// 96 work-groups for the last 11 us of a 78 us launch).  kAhead: splits of
+// several rounds look each next round's pages up ahead, as in decode_split.
+template <int D, int P, bool kPack, bool kAhead>
 __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
     int rows, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages, int max_k,
     int n_split, int pps, float scale2, const uint16_t *__restrict__ q,
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
     // the previous split's work-group merge has finished reading its LDS
     if (u != blockIdx.x) __syncthreads();
     const int32_t *sel = sel_pages + (int64_t)row * max_k;
-    decode_split<D, P, kPack, kDecodeWaves, false>(
+    decode_split<D, P, kPack, kDecodeWaves, kAhead>(
         row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
         v_cache, page_table, [&](int r) { return ctx_lens[r]; }, [&](int i) { return sel[i]; },
         [&] { return min(num_sel[row], max_k); }, partial);
@@ -909,8 +910,15 @@ hipError_t launch_decode(const Dims &dm, int batch, const void *q,
   } while (0)
 #define QUEST_DECODE_G(DD, PP, PK)                                                        \
   do {                                                                                    \
-    if (live)                                                                             \
-      hipLaunchKernelGGL((sparse_decode_live_kernel<DD, PP, PK>), dim3(blocks),           \
+    if (live && ahead)                                                                    \
+      hipLaunchKernelGGL((sparse_decode_live_kernel<DD, PP, PK, true>), dim3(blocks),     \
+                         dim3(kDecodeWaves * 64), 0, stream, rows, dm.R, dm.Gcols, dm.Hkv, \
+                         dm.gdiv, dm.pool, dm.max_pages, max_k, plan.n_split,             \
+                         plan.pages_per_split, scale2, (const uint16_t *)q,               \
+                         (const uint16_t *)k_cache, (const uint16_t *)v_cache,            \
+                         page_table, ctx_lens, sel_pages, num_sel, workspace);            \
+    else if (live)                                                                        \
+      hipLaunchKernelGGL((sparse_decode_live_kernel<DD, PP, PK, false>), dim3(blocks),    \
                          dim3(kDecodeWaves * 64), 0, stream, rows, dm.R, dm.Gcols, dm.Hkv, \
                          dm.gdiv, dm.pool, dm.max_pages, max_k, plan.n_split,             \
                          plan.pages_per_split, scale2, (const uint16_t *)q,               \

@@ -213,17 +213,20 @@ def test_plan_covers_every_page():
 def test_plan_shapes_of_the_workloads():
     """The plan at the measured shapes: one round per split (8 waves x 4 pages
     at page 16, x 2 at page 32), or as many rounds as keep a bf16 row within
-    32 splits."""
+    8 splits, or within as many as give each of 256 CUs a split when the
+    batch has fewer than 32 rows."""
     def plan(batch, hkv, max_k, page_size):
         L = layout(num_kv_heads=hkv, num_q_heads=hkv * 8, page_size=page_size, dtype=1)
         p = quest.quest_sparse_decode_plan(L, batch, max_k)
         return p["num_splits"], p["pages_per_split"]
     assert plan(8, 4, 256, 16) == (8, 32)        # batch 8 x 128000, budget 4096: one round each
-    assert plan(8, 4, 8008, 16) == (32, 256)     # every page (the dense reference): 8 rounds
-    assert plan(32, 4, 383, 32) == (24, 16)      # the ragged batch: rounds of 16 pages
+    assert plan(8, 4, 8008, 16) == (8, 1024)     # every page (the dense reference): 32 rounds
+    assert plan(32, 4, 383, 32) == (8, 48)       # the ragged batch: 3 rounds of 16 pages
     assert plan(64, 4, 128, 16) == (4, 32)       # 256 rows of 128 pages
     for batch, max_k in [(1, 60000), (2, 9000), (8, 8008)]:
-        assert plan(batch, 4, max_k, 16)[0] <= 32
+        assert plan(batch, 4, max_k, 16)[0] <= max(8, -(-256 // (batch * 4)))
+    assert plan(1, 4, 60000, 16) == (63, 960)     # 4 rows: 63 splits each, so 252 in all
+    assert plan(1, 1, 8000, 16) == (250, 32)      # one row: one round per split
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -296,17 +299,18 @@ def test_topk_sparse_decode_fused_rule(lib):
     assert quest.quest_topk_sparse_decode_fused(layout(max_pages_per_seq=8192), 1, 16)
     assert not quest.quest_topk_sparse_decode_fused(layout(), 0, 16)
     big = layout(num_kv_heads=1, num_q_heads=8, num_pool_pages=9000, max_pages_per_seq=8000)
-    assert quest.quest_topk_sparse_decode_fused(big, 1, 8000)           # 32 splits of 256
+    assert quest.quest_topk_sparse_decode_fused(big, 1, 8000)           # 250 splits of 32
     assert quest.quest_topk_sparse_decode_plan(big, 1, 8000) == {
-        "fused": True, "num_splits": 32, "pages_per_split": 256}
-    assert not quest.quest_topk_sparse_decode_fused(big, 1, 8193)       # 32 splits of 288
-    assert not quest.quest_topk_sparse_decode_fused(big, 1, 100000)
+        "fused": True, "num_splits": 250, "pages_per_split": 32}
+    assert quest.quest_topk_sparse_decode_plan(big, 1, 8193) == {       # 129 splits of 64
+        "fused": True, "num_splits": 129, "pages_per_split": 64}
+    assert not quest.quest_topk_sparse_decode_fused(big, 1, 100000)     # 241 splits of 416
     assert lib.quest_topk_sparse_decode_fused(ctypes.byref(layout()), 1, 0) == ERR_SHAPE
-    # one request of 4 KV heads with 2048 pages kept: 32 splits (the decode
-    # plan's, whose partials the workspace holds) of two rounds each
+    # one request of 4 KV heads with 2048 pages kept: 64 splits each (the
+    # decode plan's, whose partials the workspace holds), one round each
     one = layout(num_pool_pages=4000, max_pages_per_seq=4000)
     assert quest.quest_topk_sparse_decode_plan(one, 1, 2048) == {
-        "fused": True, "num_splits": 32, "pages_per_split": 64}
+        "fused": True, "num_splits": 64, "pages_per_split": 32}
     p = quest.quest_topk_sparse_decode_plan(bench, 8, 256)
     assert p == {"fused": True, "num_splits": 8, "pages_per_split": 32}
     assert quest.quest_topk_sparse_decode_plan(bench, 64, 128) == {

@@ -30,9 +30,9 @@ CASES["rows256"] = workloads.Workload("rows256", 64, 32, 4, 128, 16, "bf16",
                                       seed=91, poison=float("nan"))
 # Several rounds per split (the later rounds' page ids come from the split's
 # LDS list): 256 rows of 128 pages, one split of 4 rounds and no merge (the
-# 48-layer step's plan); 32 rows of 1024 pages, 8 splits of 4 rounds; one
-# request of 4 KV heads keeping 2048 pages, 32 splits of 2 rounds (the
-# decode plan's split count, which sizes the workspace)
+# 48-layer step's plan); 32 rows of 1024 pages, 8 splits of 4 rounds; and
+# one request of 4 KV heads keeping 2048 pages, 64 one-round splits per row
+# (the decode plan's split count, which sizes the workspace)
 CASES["rounds4_rows256"] = workloads.Workload("rounds4_rows256", 64, 32, 4, 128, 16, "bf16",
                                               ctx_range=(1000, 6000), budget_tokens=2048,
                                               steps=1, seed=93, poison=float("nan"),
@@ -40,10 +40,10 @@ CASES["rounds4_rows256"] = workloads.Workload("rounds4_rows256", 64, 32, 4, 128,
 CASES["rounds4_rows32"] = workloads.Workload("rounds4_rows32", 8, 32, 4, 128, 16, "bf16",
                                              ctx_range=(16500, 22000), budget_tokens=16384,
                                              steps=1, seed=94)
-CASES["rounds2_batch1"] = workloads.Workload("rounds2_batch1", 1, 32, 4, 128, 16, "bf16",
+CASES["batch1_long"] = workloads.Workload("batch1_long", 1, 32, 4, 128, 16, "bf16",
                                              ctx=40000, budget_tokens=32768, steps=1, seed=95)
 # rounds of the fused plan per split, where a case asserts it
-ROUNDS = {"rounds4_rows256": 4, "rounds4_rows32": 4, "rounds2_batch1": 2}
+ROUNDS = {"rounds4_rows256": 4, "rounds4_rows32": 4, "batch1_long": 1}
 # 40 requests: 160 rows, one split each
 CASES["rows160_d64"] = workloads.Workload("rows160_d64", 40, 16, 4, 64, 32, "bf16",
                                           ctx_range=(0, 3000), budget_tokens=640, steps=1,
