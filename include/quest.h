@@ -44,7 +44,7 @@
  *    failure reported by HIP returns QUEST_ERR_HIP.  Nothing is printed, no
  *    exception crosses the ABI, the library never aborts.
  *  - batch == 0 is valid and launches nothing.  Size limits (QUEST_ERR_SHAPE
- *    beyond them): 0 <= batch <= 65535, batch * num_q_heads <= 2^22,
+ *    beyond them): 0 <= batch <= 65535, batch * num_q_heads <= 2^19,
  *    max_pages_per_seq * page_size <= INT32_MAX and max_pages_per_seq *
  *    num_kv_heads < 2^30 (every launch grid stays within 2^32 work-items).
  *  - Device-side preconditions, not checked on the host (the data lives on the

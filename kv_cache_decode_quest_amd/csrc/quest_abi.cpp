@@ -67,12 +67,14 @@ int check_layout(const quest_layout *L, Dims &dm) {
 }
 
 // batch <= 65535 (grid y of the scoring, top-k and append kernels) and
-// batch * Hq <= 2^22, which keeps the decode (at most about max(rows, 1024)
-// work-groups of 512 threads) and merge (batch * Hq work-groups of 128)
-// grids under 2^32 work-items.
+// batch * Hq <= 2^19, which keeps every other grid under 2^32 work-items:
+// the bf16 decode launches at most 8 splits per row once a batch has more
+// than 1024 selection rows (at most 256 work-groups below that), so at most
+// 2^19 x 8 work-groups of 512 threads; the fp32 decode at most rows + 2048
+// work-groups of 256; the merge batch * Hq work-groups of 128.
 int check_batch(int32_t batch, const Dims &dm) {
   if (batch < 0 || batch > 65535) return QUEST_ERR_SHAPE;
-  if ((int64_t)batch * dm.Hq > ((int64_t)1 << 22)) return QUEST_ERR_SHAPE;
+  if ((int64_t)batch * dm.Hq > ((int64_t)1 << 19)) return QUEST_ERR_SHAPE;
   return QUEST_OK;
 }
 

@@ -807,7 +807,9 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
 // One work-group per (request, q head), one thread per channel.  Splits are
 // taken 32 at a time with all of their loads issued together (the max and
 // sum are the same address across the work-group), merged online: a bf16
-// row has at most 32 splits, so its merge is one round trip to memory.
+// row has at most 8 splits once the batch has 32 selection rows or more, so
+// its merge is one round trip to memory; a batch of fewer rows gives each
+// row up to ceil(256 / rows) splits, 32 per round trip.
 // ---------------------------------------------------------------------------
 constexpr int kMergeChunk = 32;
 

@@ -227,6 +227,18 @@ int main(void) {
     if (pst == QUEST_OK) {
       CHECK(pps >= 1 && ns >= 1 && ns <= 256, "plan bounds");
       CHECK((int64_t)ns * pps >= max_k && (int64_t)(ns - 1) * pps < max_k, "plan covers max_k");
+      if (batch > 0) {
+        /* the decode's grid (rows x splits work-groups, 512 threads for bf16
+         * and 256 for fp32; the live-split form launches fewer) and the
+         * merge's (one 128-thread work-group per q head) stay within 2^32
+         * work-items */
+        const int64_t rows = (int64_t)batch * (S.selection == QUEST_SELECT_PER_Q_HEAD
+                                                   ? S.num_q_heads : S.num_kv_heads);
+        const int64_t threads = S.dtype == QUEST_BF16 ? 512 : 256;
+        CHECK(rows * ns * threads < ((int64_t)1 << 32), "decode grid within 2^32 work-items");
+        CHECK((int64_t)batch * S.num_q_heads * 128 < ((int64_t)1 << 32),
+              "merge grid within 2^32 work-items");
+      }
       if (fu) {
         CHECK(fns <= ns, "fused plan within the workspace's splits");
         CHECK((int64_t)fns * fpps >= max_k && (int64_t)(fns - 1) * fpps < max_k,

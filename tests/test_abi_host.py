@@ -130,10 +130,11 @@ def test_batch_bounds_and_empty_batch(lib):
     L = layout()
     assert scores_call(lib, L, batch=-1) == ERR_SHAPE
     assert scores_call(lib, L, batch=70000) == ERR_SHAPE
-    # batch * Hq <= 2^22 keeps the decode and merge grids within 2^32 work-items
+    # batch * Hq <= 2^19 keeps the decode and merge grids within 2^32 work-items
     wide = layout(num_q_heads=1024, num_kv_heads=64)
-    assert decode_call(lib, wide, batch=4097) == ERR_SHAPE
-    assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(wide), 4097, 8) == 0
+    assert decode_call(lib, wide, batch=513) == ERR_SHAPE
+    assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(wide), 513, 8) == 0
+    assert lib.quest_sparse_decode_workspace_bytes(ctypes.byref(wide), 512, 8) > 0
     # max_pages_per_seq * Hkv < 2^30 keeps the scoring grid within 2^32 work-items
     assert scores_call(lib, layout(max_pages_per_seq=1 << 28, num_pool_pages=1 << 28)) == ERR_SHAPE
     # batch 0: nothing to do, no pointer needed, nothing launched
