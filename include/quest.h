@@ -49,9 +49,12 @@
  *    num_kv_heads < 2^30 (every launch grid stays within 2^32 work-items).
  *  - Device-side preconditions, not checked on the host (the data lives on the
  *    device): page-table entries of live pages lie in [0, num_pool_pages);
- *    ctx_lens[r] <= max_pages_per_seq * page_size; budgets >= 0.  Kernels skip
- *    any page id outside the pool and any index outside a row instead of
- *    touching memory out of bounds; results for such inputs are unspecified.
+ *    ctx_lens[r] <= max_pages_per_seq * page_size; budgets >= 0.  No kernel
+ *    touches memory outside the pool for a live page whose id lies outside
+ *    [0, num_pool_pages): such a page scores -inf, is never stored to and
+ *    contributes no token to the attention.  Kernels clamp every other index
+ *    into its row; results for inputs that break the other preconditions are
+ *    unspecified.
  *  - Numbers: q, K, V, the page metadata and the output share one element type
  *    (fp32, or bf16 with round-to-nearest-even on every bf16 write).  Scores,
  *    softmax statistics and accumulators are fp32.
@@ -172,8 +175,9 @@ int quest_append_kv(const quest_layout *layout, int32_t batch,
  * With per-q-head selection there is no reduction: scores[r][h][j] = U[h][j]
  * for every q head h (group_reduce is still validated but has no effect).
  * Products of bf16 values are exact in fp32 (fp32 inputs: each product is
- * fused into its fp32 add); sums are fp32 in an unspecified order.  Entries
- * j >= ceil(ctx/P) are not written. */
+ * fused into its fp32 add); sums are fp32 in an unspecified order.  A page
+ * whose page-table entry lies outside [0, num_pool_pages) scores -inf.
+ * Entries j >= ceil(ctx/P) are not written. */
 int quest_page_scores(const quest_layout *layout, int32_t batch,
                       const void *q, const void *kmeta,
                       const int32_t *page_table, const int32_t *ctx_lens,

@@ -94,8 +94,8 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
                             max_pages;
 
   // Metadata row of this lane's page in each of the wave's tiles; pages past
-  // the request (or with an id outside the pool) read physical page 0 and are
-  // never written back.
+  // the request read physical page 0 and are never written back, and a page
+  // whose id lies outside the pool reads physical page 0 and scores -inf.
   int page[kScoreTilesPerWave];
   int64_t row[kScoreTilesPerWave];
 #pragma unroll
@@ -144,10 +144,12 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
     }
   }
 
+  bool in_pool[kScoreTilesPerWave];
 #pragma unroll
   for (int t = 0; t < kScoreTilesPerWave; ++t) {
     const int64_t phys = row[t];
-    const bool ok = page[t] < n && phys >= 0 && phys < pool;
+    in_pool[t] = phys >= 0 && phys < pool;
+    const bool ok = page[t] < n && in_pool[t];
     row[t] = (ok ? phys * Hkv + g : (int64_t)g) * (2 * D);
   }
 
@@ -180,7 +182,9 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
     if (per_head) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (4 * grp + i < G && page[t] < n) out[(int64_t)(4 * grp + i) * max_pages + page[t]] = acc[i];
+        if (4 * grp + i < G && page[t] < n)
+          out[(int64_t)(4 * grp + i) * max_pages + page[t]] =
+              in_pool[t] ? acc[i] : -__builtin_huge_valf();
       continue;
     }
     // combine the group
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
     v = reduce == 0 ? fmaxf(v, o16) : v + o16;
     const float o32 = __shfl_xor(v, 32, kWave);
     v = reduce == 0 ? fmaxf(v, o32) : v + o32;
-    if (grp == 0 && page[t] < n) out[page[t]] = v;
+    if (grp == 0 && page[t] < n) out[page[t]] = in_pool[t] ? v : -__builtin_huge_valf();
   }
 }
 
@@ -225,7 +229,15 @@ __global__ __launch_bounds__(256) void page_scores_valu_kernel(
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
   const int64_t phys = page_table[(int64_t)r * max_pages + j];
-  if (phys < 0 || phys >= pool) return;
+  if (phys < 0 || phys >= pool) {                     // outside the pool: -inf
+    if (per_head) {
+      for (int h = 0; h < G; ++h)
+        scores[((int64_t)(r * Hkv + g) * G + h) * max_pages + j] = -__builtin_huge_valf();
+    } else {
+      scores[((int64_t)r * Hkv + g) * max_pages + j] = -__builtin_huge_valf();
+    }
+    return;
+  }
   const float *lo = kmeta + (phys * Hkv + g) * 2 * D;
   const float *hi = lo + D;
   float u[kG];
