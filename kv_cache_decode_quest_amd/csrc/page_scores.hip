@@ -78,9 +78,12 @@ __global__ __launch_bounds__(256) void page_scores_mfma_kernel(
   const int r = blockIdx.y;
   int ctx, row0 = 0, p0 = 0, n_new = 0;
   if constexpr (kAppend) {
-    row0 = fa.cu_new[r];
-    n_new = fa.cu_new[r + 1] - row0;
+    // ctx_before read first: the compiler then issues the three length
+    // loads together (one scalar round trip instead of two in a row)
     p0 = fa.ctx_before[r];
+    row0 = fa.cu_new[r];
+    const int row1 = fa.cu_new[r + 1];
+    n_new = row1 - row0;
     ctx = p0 + (n_new > 0 ? n_new : 0);
   } else {
     ctx = ctx_lens[r];
