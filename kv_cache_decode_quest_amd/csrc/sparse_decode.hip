@@ -579,15 +579,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
   __shared__ uint32_t units_end[kLiveRows];
   __shared__ uint32_t wave_total[kDecodeWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  auto units_of = [&](int x) -> uint32_t {
-    const int k = min(num_sel[x], max_k);
+  auto units_of = [&](int count) -> uint32_t {
+    const int k = min(count, max_k);
     return k > 0 ? (uint32_t)((k + pps - 1) / pps) : 0u;
   };
   // inclusive scan of the rows' live splits: thread t owns rows 2t and 2t+1
+  // (both counts read at once from indices clamped into the rows, then
+  // masked: loads under the row test were drained one after the other)
   static_assert(2 * kDecodeWaves * 64 >= kLiveRows, "two rows per thread");
   const int x0 = 2 * threadIdx.x;
-  const uint32_t u0 = x0 < rows ? units_of(x0) : 0u;
-  const uint32_t u1 = x0 + 1 < rows ? units_of(x0 + 1) : 0u;
+  const int c0 = num_sel[min(x0, rows - 1)];
+  const int c1 = num_sel[min(x0 + 1, rows - 1)];
+  const uint32_t u0 = x0 < rows ? units_of(c0) : 0u;
+  const uint32_t u1 = x0 + 1 < rows ? units_of(c1) : 0u;
   const uint32_t incl = wave_incl_sum(u0 + u1);
   if (lane == 63) wave_total[wave] = incl;
   __syncthreads();
