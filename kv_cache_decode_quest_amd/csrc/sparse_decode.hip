@@ -813,11 +813,15 @@ __global__ __launch_bounds__(256) void sparse_decode_valu_kernel(
 // ---------------------------------------------------------------------------
 // merge: out[r][h] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
 // One work-group per (request, q head), one thread per channel.  Splits are
-// taken 32 at a time with all of their loads issued together (the max and
-// sum are the same address across the work-group), merged online: a bf16
-// row has at most 8 splits once the batch has 32 selection rows or more, so
-// its merge is one round trip to memory; a batch of fewer rows gives each
-// row up to ceil(256 / rows) splits, 32 per round trip.
+// taken kChunk at a time with all of their loads issued together (the max
+// and sum are the same address across the work-group), merged online.  A
+// bf16 row has at most 8 splits once the batch has 32 selection rows or
+// more, so its merge is one round trip to memory; a batch of fewer rows
+// gives each row up to ceil(256 / rows) splits, 32 per round trip.  kChunk
+// is the fewest of 8, 16 and 32 that holds the row's splits: the slots of a
+// chunk past n_split re-load the chunk's first split and the wave still
+// waits for them (a chunk of 32 for 8 splits cost 1.3 us per step at batch
+// 8 x 128000 and 2.8 us on the ragged batch).
 // ---------------------------------------------------------------------------
 constexpr int kMergeChunk = 32;
 
@@ -826,7 +830,7 @@ constexpr int kMergeChunk = 32;
 // 0, past them, while the live-split kernel writes nothing there).  The
 // partials are loaded for all n_split splits at once, without waiting for
 // the count, and the splits past the live ones are masked.
-template <typename T>
+template <typename T, int kChunk>
 __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_split, int pps,
                                                     int max_k, const int32_t *__restrict__ num_sel,
                                                     const float *__restrict__ partial,
@@ -850,10 +854,10 @@ __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_s
       partial + (int64_t)row * n_split * stride + (int64_t)hl * (D + 2) + lane0;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float M = -__builtin_huge_valf(), L = 0.f, a = 0.f;
-    for (int s0 = 0; s0 < n_split; s0 += kMergeChunk) {
-      float mv[kMergeChunk], lv[kMergeChunk], av[kMergeChunk];
+    for (int s0 = 0; s0 < n_split; s0 += kChunk) {
+      float mv[kChunk], lv[kChunk], av[kChunk];
 #pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u) {
+      for (int u = 0; u < kChunk; ++u) {
         const float *p = base + (s0 + u < n_split ? s0 + u : s0) * stride;
         mv[u] = p[D];
         lv[u] = p[D + 1];
@@ -861,14 +865,14 @@ __global__ __launch_bounds__(128) void merge_kernel(int R, int G, int D, int n_s
       }
       float cm = M;
 #pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u)
+      for (int u = 0; u < kChunk; ++u)
         if (s0 + u < live) cm = fmaxf(cm, mv[u]);
       if (cm == -__builtin_huge_valf()) continue;  // nothing but empty splits so far
       const float f0 = (M == -__builtin_huge_valf()) ? 0.f : exp2_fast(M - cm);
       a *= f0;
       L *= f0;
 #pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u) {
+      for (int u = 0; u < kChunk; ++u) {
         // an empty split (max -inf) leaves its accumulator unwritten: select,
         // never multiply it by a zero weight
         if (s0 + u < live && mv[u] != -__builtin_huge_valf()) {
@@ -887,14 +891,22 @@ static hipError_t launch_merge(const Dims &dm, int batch, const DecodePlan &plan
                                const int32_t *num_sel, const float *workspace, void *out,
                                hipStream_t stream, int xcd_stride = 0) {
   const unsigned mblocks = (unsigned)((long)batch * dm.Hq);
-  if (dm.dtype == 1)
-    hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, plan.pages_per_split, max_k, num_sel,
-                       workspace, (uint16_t *)out, xcd_stride);
-  else
-    hipLaunchKernelGGL(merge_kernel<float>, dim3(mblocks), dim3(128), 0, stream, dm.R,
-                       dm.Gcols, dm.D, plan.n_split, plan.pages_per_split, max_k, num_sel,
-                       workspace, (float *)out, xcd_stride);
+  // splits per round trip: the fewest of 8, 16, 32 that hold the row's
+  // splits (slots past n_split would re-load the first one)
+#define QUEST_MERGE(TT, CH)                                                               \
+  hipLaunchKernelGGL((merge_kernel<TT, CH>), dim3(mblocks), dim3(128), 0, stream, dm.R,    \
+                     dm.Gcols, dm.D, plan.n_split, plan.pages_per_split, max_k, num_sel,  \
+                     workspace, (TT *)out, xcd_stride)
+#define QUEST_MERGE_T(TT)                                                                 \
+  do {                                                                                    \
+    if (plan.n_split <= 8) QUEST_MERGE(TT, 8);                                            \
+    else if (plan.n_split <= 16) QUEST_MERGE(TT, 16);                                     \
+    else QUEST_MERGE(TT, kMergeChunk);                                                    \
+  } while (0)
+  if (dm.dtype == 1) QUEST_MERGE_T(uint16_t);
+  else QUEST_MERGE_T(float);
+#undef QUEST_MERGE_T
+#undef QUEST_MERGE
   return hipGetLastError();
 }
 
