@@ -385,21 +385,33 @@ def test_deterministic_and_budget_covering_all_is_dense(gpu_lib):
         check_out(to_f64(outs[0][r]), dense, torch.bfloat16, "dense")
 
 
-def test_split_count_invariance(gpu_lib):
-    """Changing max_k changes the split plan; outputs stay within tolerance."""
-    w = scaled(WORKLOADS["layer32k"], batch=2, ctx=8000, budget_tokens=1024, steps=1)
-    lay = Layer(w, DEV, host=False)
+@pytest.mark.parametrize("budget,max_ks", [(1024, (64, 200, 501)), (8000, (501, 520, 1100))])
+def test_split_count_invariance(budget, max_ks, gpu_lib):
+    """Changing max_k changes the split plan (2, 7, 16, 17 and 18 splits per
+    row, so the merge's round trips hold 8, 16 or 32 splits, with and without
+    empty ones): the selections stay the same and every plan's outputs meet
+    the oracle."""
+    w = scaled(WORKLOADS["layer32k"], batch=2, ctx=8000, budget_tokens=budget, steps=1)
+    lay = Layer(w, DEV)
     q, k_new, v_new = lay.step_inputs(0)
     lay.append_step(k_new, v_new)
+    refs = [lay.oracle_request(q, r) for r in range(w.batch)]
+    k = budget // w.page_size
     results = []
-    for max_k in (64, 200, 501):
+    for max_k in max_ks:
         bufs = lay.buffers(max_k=max_k)
         plan = quest.quest_sparse_decode_plan(lay.L, w.batch, max_k)
+        log(f"split invariance: budget {budget}, max_k {max_k}, plan {plan}")
         lay.view(q, bufs)
         lay.attend(q, bufs)
         torch.cuda.synchronize()
-        results.append((plan, to_f64(bufs.out), bufs.sel_pages[:, :, :64].cpu()))
-    assert len({p["num_splits"] for p, _, _ in results}) > 1
+        sel, nsel, out = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy(), to_f64(bufs.out)
+        assert (nsel == k).all()
+        for r in range(w.batch):
+            check_request_output(lay, q, r, sel[r], nsel[r], out[r], refs[r],
+                                 f"split invariance max_k {max_k} r{r}")
+        results.append((plan, out, bufs.sel_pages[:, :, :k].cpu()))
+    assert len({p["num_splits"] for p, _, _ in results}) == len(max_ks)
     for _, out, sel in results[1:]:
         assert torch.equal(sel, results[0][2])
         check_out(out, results[0][1], torch.bfloat16, "split invariance")
