@@ -336,8 +336,8 @@ __device__ __forceinline__ void attend_round(PageRegs<D, P> *pg, const int *lim,
 // page ids and page-table entries are looked up right after the current
 // round's K/V loads are issued, so each later round starts its K/V loads at
 // once; results are the same bit for bit.
-template <int D, int P, bool kPack, int kWaves, bool kAhead, typename Ids, typename Count,
-          typename CtxOf>
+template <int D, int P, bool kPack, int kWaves, bool kAhead, bool kNonEmpty = false,
+          typename Ids, typename Count, typename CtxOf>
 __device__ __forceinline__ void decode_split(
     int row, int split, int R, int G, int Hkv, int gdiv, int64_t pool, int max_pages,
     int max_k, int n_split, int pps, float scale2, const uint16_t *__restrict__ q,
@@ -381,7 +381,10 @@ __device__ __forceinline__ void decode_split(
   const int jfirst = ids(first < max_k ? first : max_k - 1);
   const int nsel = count();
   const int ctx = ctx_of(r);
-  if (first >= nsel) {                             // no page in this split:
+  // (kNonEmpty: the caller only passes splits that hold pages, so the count
+  // is not waited for here and its load goes out with the page ids'; 0.45 us
+  // per step on the ragged batch, one scalar round trip per split)
+  if (!kNonEmpty && first >= nsel) {               // no page in this split:
     if (final_out) {                                // a row with no page outputs zeros
       for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x)
         Elem<uint16_t>::store(final_out, (int64_t)row * G * D + idx, 0.f);
@@ -616,8 +619,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_live_kernel(
     const int split = (int)(u - (row > 0 ? units_end[row - 1] : 0u));
     // the previous split's work-group merge has finished reading its LDS
     if (u != blockIdx.x) __syncthreads();
+    // a live split is one of the row's first ceil(count / pps), so its first
+    // position is below the count: decode_split skips its empty-split test
     const int32_t *sel = sel_pages + (int64_t)row * max_k;
-    decode_split<D, P, kPack, kDecodeWaves, kAhead>(
+    decode_split<D, P, kPack, kDecodeWaves, kAhead, true>(
         row, split, R, G, Hkv, gdiv, pool, max_pages, max_k, n_split, pps, scale2, q, k_cache,
         v_cache, page_table, [&](int r) { return ctx_lens[r]; }, [&](int i) { return sel[i]; },
         [&] { return min(num_sel[row], max_k); }, partial);
