@@ -20,8 +20,9 @@ replay; a HIP event pair brackets the timed replay.  value = batch * K /
 replay time.  Also reported: the same steps launched eagerly one at a time,
 the cache evicted before each by an untimed 2 GiB read sweep (each step then
 pays its own dispatch latency); a per-kernel breakdown; the dominant kernel's
-roofline (its launch time over 8 copies of the metadata, and the committed
-counter record of its HBM traffic); the dense decode over every page, the
+roofline (its average over 128 back-to-back launches cycling through 8
+copies of the metadata, and the committed counter record of its HBM
+traffic); the dense decode over every page, the
 per-q-head selection, the SUM / forced-page / page-size variants and the
 prefill-chunk append, each timed like the eager steps; the 48-layer batch-64
 step; one step each of the other single-layer workloads (the tiny fp32
@@ -713,6 +714,10 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=4096,
                     help="chunk size of the prefill append leg (0 to skip)")
     ap.add_argument("--roofline-copies", type=int, default=8)
+    ap.add_argument("--roofline-launches", type=int, default=128,
+                    help="back-to-back launches the dominant kernel's average is taken over "
+                         "(rounded down to a multiple of the copies); independent of --steps, "
+                         "so a short run does not weigh the first launch from an idle GPU more")
     ap.add_argument("--extra-replays", type=int, default=4,
                     help="timed replays after the first, for the median per-step time")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -904,7 +909,7 @@ def main():
     restore()
     copies = [layer.kmeta.clone() for _ in range(R)]
     q0, k0, v0 = inputs[0]
-    n_launch = max(R, (K // R) * R)
+    n_launch = max(R, (args.roofline_launches // R) * R)
 
     def fused(i):
         quest.quest_append_score(layer.L, q0, k0, v0, layer.cu1, ctx_b[0], 1, layer.pt,

@@ -13,8 +13,14 @@
 // handful of barrier-separated phases, each short; wave-level scans and
 // reductions use the DPP network and ballots, not LDS round trips, and
 // cross-wave sums read one LDS word per lane.
-//  1. min and max key: every key shares the bits above the highest bit where
-//     they differ;
+//  1. the range the threshold key lies in: up to the largest key, from the
+//     least key or, where that is larger, the least of the threads' largest
+//     keys (every thread holding a key at least that large, at least
+//     kTopkThreads keys reach it, so for k <= kTopkThreads the threshold
+//     does too); every key in the range shares the bits above the highest
+//     bit where its ends differ.  The second bound keeps low outliers (a
+//     partly filled last page, pages outside the pool at -inf) from widening
+//     the first histogram's buckets;
 //  2. refinement: an (up to) 11-bit histogram of the keys matching the known
 //     prefix, on the next bits, gives the bucket holding the k-th largest key
 //     and the count kept above it; repeated until the bucket holds at most 64
@@ -55,7 +61,7 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 
 struct TopkShared {
   uint32_t hist[kBins];
-  uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves];
+  uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves], wave_c[kTopkWaves];
   uint32_t cand_key[kWave];
   int32_t cand_idx[kWave];
   uint32_t cnt_gt[kTopkWaves], cnt_eq[kTopkWaves];   // per-wave output counts
@@ -81,22 +87,29 @@ __device__ __forceinline__ uint32_t sum_of_earlier_waves(const uint32_t *vals, i
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
 }
 
-// min and max of vals_lo[w] / vals_hi[w] over all waves, the same way.
-__device__ __forceinline__ void minmax_over_waves(const uint32_t *vals_lo,
-                                                  const uint32_t *vals_hi, uint32_t &lo,
-                                                  uint32_t &hi) {
+// min of vals_lo[w] and vals_c[w], max of vals_hi[w] over all waves, the
+// same way.
+__device__ __forceinline__ void range_over_waves(const uint32_t *vals_lo,
+                                                 const uint32_t *vals_hi,
+                                                 const uint32_t *vals_c, uint32_t &lo,
+                                                 uint32_t &hi, uint32_t &c) {
   const int lane = lane_id() & (kTopkWaves - 1);
-  uint32_t a = vals_lo[lane], b = vals_hi[lane];
+  uint32_t a = vals_lo[lane], b = vals_hi[lane], f = vals_c[lane];
   a = min(a, dpp_row<kRowShr1>(a, a));
-  a = min(a, dpp_row<kRowShr2>(a, a));
-  a = min(a, dpp_row<kRowShr4>(a, a));
-  a = min(a, dpp_row<kRowShr8>(a, a));
   b = max(b, dpp_row<kRowShr1>(b, b));
+  f = min(f, dpp_row<kRowShr1>(f, f));
+  a = min(a, dpp_row<kRowShr2>(a, a));
   b = max(b, dpp_row<kRowShr2>(b, b));
+  f = min(f, dpp_row<kRowShr2>(f, f));
+  a = min(a, dpp_row<kRowShr4>(a, a));
   b = max(b, dpp_row<kRowShr4>(b, b));
+  f = min(f, dpp_row<kRowShr4>(f, f));
+  a = min(a, dpp_row<kRowShr8>(a, a));
   b = max(b, dpp_row<kRowShr8>(b, b));
+  f = min(f, dpp_row<kRowShr8>(f, f));
   lo = (uint32_t)__builtin_amdgcn_readlane((int)a, 15);
   hi = (uint32_t)__builtin_amdgcn_readlane((int)b, 15);
+  c = (uint32_t)__builtin_amdgcn_readlane((int)f, 15);
 }
 
 // The bucket (of `bins` <= kBins) holding the krem-th largest counted key,
@@ -208,7 +221,7 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
   }
   auto valid = [&](int i) { const int j = slot_page(i); return j >= 0 && in_row(j); };
 
-  // 1. min and max key
+  // 1. min and max key, and the least of the threads' largest keys
   uint32_t lo = 0xffffffffu, hi = 0u;
   if constexpr (kRegs) {
     // slots outside the range hold key 0, which never raises hi
@@ -224,29 +237,35 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
       hi = max(hi, x);
     }
   }
+  uint32_t top = hi;                                  // 0 for a thread holding no key
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
+  top = wave_min_u32(top);
   if (lane == 0) {
     sh.wave_a[wave] = lo;
     sh.wave_b[wave] = hi;
+    sh.wave_c[wave] = top;
   }
 #pragma unroll
   for (int e = 0; e < kBinsPerLane; ++e) sh.hist[kBinsPerLane * tid + e] = 0;
   if (tid == 0) sh.cand_count = 0;
   __syncthreads();
-  minmax_over_waves(sh.wave_a, sh.wave_b, lo, hi);
+  range_over_waves(sh.wave_a, sh.wave_b, sh.wave_c, lo, hi, top);
 
   uint32_t thresh, krem = (uint32_t)kk;
   if (lo == hi) {                                     // every key equal: the lowest kk pages
     for (int i = tid; i < kk; i += kTopkThreads) emit(a + i, a + i);
     return;
   }
-  // 2. refine the threshold key, 11 bits at a time
-  const int hb = 31 - __builtin_clz(lo ^ hi);
-  int lowbit = hb + 1;                                // bits >= lowbit are known
+  // With top > 0 every thread holds a key >= top, so at least kTopkThreads
+  // keys reach it, and for kk <= kTopkThreads so does the threshold key.
+  const uint32_t floor_key = kk <= kTopkThreads ? max(lo, top) : lo;
+  // 2. refine the threshold key, 11 bits at a time.  floor_key == hi: at
+  // least kk keys equal hi, which is then the threshold key.
+  int lowbit = floor_key == hi ? 0 : 32 - __builtin_clz(floor_key ^ hi);   // bits >= lowbit known
   uint32_t prefix = (uint32_t)(((uint64_t)hi >> lowbit) << lowbit);
-  uint32_t count;
-  for (bool first_pass = true;; first_pass = false) {
+  uint32_t count = 0;
+  for (bool first_pass = true; lowbit > 0; first_pass = false) {
     const int w = lowbit < kDigitBits ? lowbit : kDigitBits;
     const int shift = lowbit - w;
     const uint32_t bmask = (1u << w) - 1u;

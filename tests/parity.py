@@ -328,4 +328,12 @@ def topk_rows(n_max, gen):
     rows.append(thr[torch.randperm(n_max, generator=gen)])
     rows.append(torch.randn(n_max, generator=gen) * 1e30)                    # wide range
     rows.append(torch.randn(n_max, generator=gen) * 1e-3 + 100.0)            # narrow range
+    low = torch.randn(n_max, generator=gen) + 30.0                          # low outliers
+    low[torch.randperm(n_max, generator=gen)[: max(1, n_max // 500)]] = float("-inf")
+    low[torch.randint(0, n_max, (2,), generator=gen)] = -1e30
+    rows.append(low)
+    top = torch.full((n_max,), 2.0)                      # most keys tied at the maximum
+    top[torch.randperm(n_max, generator=gen)[: n_max // 8]] = \
+        torch.randn(n_max // 8, generator=gen) - 4.0
+    rows.append(top)
     return rows

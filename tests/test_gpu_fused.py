@@ -233,3 +233,80 @@ def test_fused_selection_on_constructed_rows(n_max, P, D, max_k, forced, gpu_lib
     assert torch.equal(one.sel_pages, two.sel_pages)
     a, c = to_f64(one.out), to_f64(two.out)
     assert np.all(one_bf16_ulp(a, c)), float(np.abs(a - c).max())
+
+
+def range_floor_rows(n_max, gen):
+    """Four score rows per request: low outliers (-inf and -1e30 among normal
+    scores), most keys tied at the row's maximum, one -inf among normal
+    scores, and plain normal scores."""
+    low = torch.randn(n_max, generator=gen) + 30.0
+    low[torch.randperm(n_max, generator=gen)[: n_max // 400]] = float("-inf")
+    low[torch.randint(0, n_max, (3,), generator=gen)] = -1e30
+    top = torch.full((n_max,), 2.0)
+    top[torch.randperm(n_max, generator=gen)[: n_max // 8]] = \
+        torch.randn(n_max // 8, generator=gen) - 4.0
+    one = torch.randn(n_max, generator=gen)
+    one[int(torch.randint(0, n_max, (1,), generator=gen))] = float("-inf")
+    return [low, top, one, torch.randn(n_max, generator=gen)]
+
+
+@pytest.mark.parametrize("n_max,fused", [(8008, True), (10000, False)])
+def test_selection_range_floor(n_max, fused, gpu_lib):
+    """Rows of at least 1024 pages keeping at most 1024 (every selection
+    thread then holds a key, and the threshold's range starts at the least
+    of the threads' largest keys, which leaves low outliers out of the first
+    histogram), at k = 1, 64, 256, 1000, 1024 and 1025 (one past that bound,
+    where the range starts at the least key again), with the row filling the
+    table stride or ending in the last wave's span: the top-k kernel's
+    selection, and the fused kernel's where the shape allows it, equal the
+    oracle's; the fused outputs equal the two-call path's within one bf16
+    step."""
+    P, D, Hkv, G = 16, 128, 4, 8
+    ks = (1, 64, 256, 1000, 1024, 1025)
+    ns = (n_max, 7800)
+    gen = torch.Generator().manual_seed(9100 + n_max)
+    B = len(ks) * len(ns)
+    rows = [r for _ in range(B) for r in range_floor_rows(n_max, gen)]
+    scores = torch.stack(rows).reshape(B, Hkv, n_max).contiguous().to(DEV)
+    ctx = torch.tensor([ns[b % 2] * P - (b % 3) for b in range(B)], dtype=torch.int32,
+                       device=DEV)
+    bud = torch.tensor([ks[b // 2] * P + (b % 5) for b in range(B)], dtype=torch.int32,
+                       device=DEV)
+    max_k = max(ks)
+    pool = n_max                                   # every request reads the same pages
+    L = quest.make_layout(G * Hkv, Hkv, D, P, torch.bfloat16, pool, n_max)
+    assert quest.quest_topk_sparse_decode_fused(L, B, max_k) == fused
+    two = quest.alloc_decode_buffers(L, B, max_k, DEV)
+    quest.quest_topk_pages(L, scores, ctx, bud, max_k, two.sel_pages, two.num_sel)
+    log(f"range floor n_max {n_max}: {B} requests x {Hkv} heads, k {ks}")
+    outs = [two]
+    if fused:
+        pt = torch.arange(pool, dtype=torch.int32, device=DEV).repeat(B, 1).contiguous()
+        g = torch.Generator(device=DEV).manual_seed(9200 + n_max)
+        k_cache = torch.randn((pool, Hkv, P, D), generator=g, device=DEV).to(torch.bfloat16)
+        v_cache = torch.randn((pool, Hkv, D, P), generator=g, device=DEV).to(torch.bfloat16)
+        q = torch.randn((B, G * Hkv, D), generator=g, device=DEV).to(torch.bfloat16)
+        sm = D ** -0.5
+        one = quest.alloc_decode_buffers(L, B, max_k, DEV)
+        one.sel_pages.fill_(12345)
+        quest.quest_sparse_decode(L, q, k_cache, v_cache, pt, ctx, two.sel_pages, two.num_sel,
+                                  max_k, sm, two.out, two.workspace)
+        quest.quest_topk_sparse_decode(L, q, k_cache, v_cache, pt, ctx, scores, bud, max_k, sm,
+                                       one.sel_pages, one.num_sel, one.out, one.workspace)
+        outs.append(one)
+    torch.cuda.synchronize()
+    s64 = scores.cpu().double().numpy()
+    for bufs in outs:
+        sel, nsel = bufs.sel_pages.cpu().numpy(), bufs.num_sel.cpu().numpy()
+        for b in range(B):
+            n = -(-int(ctx[b]) // P)
+            k = min(oracle.pages_for_budget(int(bud[b]), int(ctx[b]), P), max_k)
+            assert k == ks[b // 2]
+            for h in range(Hkv):
+                want = oracle.select(np.ascontiguousarray(s64[b, h, :n]), k)
+                assert nsel[b, h] == k, (b, h)
+                assert np.array_equal(sel[b, h, :k], want), (b, h, n, k)
+                assert np.all(sel[b, h, k:] == -1)
+    if fused:
+        a, c = to_f64(outs[1].out), to_f64(outs[0].out)
+        assert np.all(one_bf16_ulp(a, c)), float(np.abs(a - c).max())
