@@ -399,11 +399,33 @@ def prefill_chunk_append(layer, chunk, n_calls, evict, dev):
     elem = 2 if w.dtype == "bf16" else 4
     tokens = B * chunk * len(calls)
     nbytes = tokens * H * D * elem * 4 + (tokens // P) * H * 2 * D * elem
+    # a plain device copy of the call's new K and V (the bytes it reads, and
+    # about the bytes it writes), timed the same way: what moving these bytes
+    # costs on this chip without any paging or metadata
+    src = torch.cat([calls[0][0].reshape(-1), calls[0][1].reshape(-1)])
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
+    torch.cuda.synchronize()
+    for e in evc:
+        evict()
+        e[0].record()
+        dst.copy_(src)
+        e[1].record()
+    torch.cuda.synchronize()
+    copy_s = sum(e[0].elapsed_time(e[1]) for e in evc) / 1e3
+    copy_bytes = 2 * src.numel() * src.element_size()
+    del src, dst
     return {"what": f"quest_append_kv of one {chunk}-token chunk per request ({B} requests) "
                     "per call, cache evicted before each call",
             "chunk_tokens": chunk, "calls": len(calls), "us_per_call": total_s / len(calls) * 1e6,
             "tokens_per_s": tokens / total_s, "bytes_per_call": nbytes / len(calls),
-            "hbm_gbps": nbytes / total_s / 1e9, "hbm_frac_peak": nbytes / total_s / 1e9 / PEAK_HBM_GBPS}
+            "hbm_gbps": nbytes / total_s / 1e9, "hbm_frac_peak": nbytes / total_s / 1e9 / PEAK_HBM_GBPS,
+            "copy_probe": {"what": "device copy of one call's new K and V, cache evicted before each",
+                           "bytes": copy_bytes, "us": copy_s / len(calls) * 1e6,
+                           "gbps": copy_bytes * len(calls) / copy_s / 1e9,
+                           "append_rate_of_copy_rate": (nbytes / total_s) /
+                                                       (copy_bytes * len(calls) / copy_s)}}
 
 
 def config_legs(names, n_steps, evict, dev, warm=2):
