@@ -14,13 +14,12 @@
 // reductions use the DPP network and ballots, not LDS round trips, and
 // cross-wave sums read one LDS word per lane.
 //  1. the range the threshold key lies in: up to the largest key, from the
-//     least key or, where that is larger, the least of the threads' largest
-//     keys (every thread holding a key at least that large, at least
-//     kTopkThreads keys reach it, so for k <= kTopkThreads the threshold
-//     does too); every key in the range shares the bits above the highest
-//     bit where its ends differ.  The second bound keeps low outliers (a
-//     partly filled last page, pages outside the pool at -inf) from widening
-//     the first histogram's buckets;
+//     least key or, where that is larger, the least of the largest keys of
+//     the threads that hold keys (each of those holds a key at least that
+//     large, so when they are k or more, so is the threshold); every key in
+//     the range shares the bits above the highest bit where its ends differ.
+//     The second bound keeps low outliers (a partly filled last page, pages
+//     outside the pool at -inf) from widening the first histogram's buckets;
 //  2. refinement: an (up to) 11-bit histogram of the keys matching the known
 //     prefix, on the next bits, gives the bucket holding the k-th largest key
 //     and the count kept above it; repeated until the bucket holds at most 64
@@ -61,7 +60,7 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 
 struct TopkShared {
   uint32_t hist[kBins];
-  uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves], wave_c[kTopkWaves];
+  uint32_t wave_a[kTopkWaves], wave_b[kTopkWaves], wave_c[kTopkWaves], wave_d[kTopkWaves];
   uint32_t cand_key[kWave];
   int32_t cand_idx[kWave];
   uint32_t cnt_gt[kTopkWaves], cnt_eq[kTopkWaves];   // per-wave output counts
@@ -221,14 +220,17 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
   }
   auto valid = [&](int i) { const int j = slot_page(i); return j >= 0 && in_row(j); };
 
-  // 1. min and max key, and the least of the threads' largest keys
+  // 1. min and max key, and the least of the largest keys of the threads
+  // that hold keys, with the number of those threads
   uint32_t lo = 0xffffffffu, hi = 0u;
+  bool holds = false;
   if constexpr (kRegs) {
     // slots outside the range hold key 0, which never raises hi
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       lo = min(lo, valid(i) ? u[i] : 0xffffffffu);
       hi = max(hi, u[i]);
+      holds = holds || valid(i);
     }
   } else {
     for (int j = a + tid; j < b; j += kTopkThreads) {
@@ -236,8 +238,10 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
       lo = min(lo, x);
       hi = max(hi, x);
     }
+    holds = a + tid < b;
   }
-  uint32_t top = hi;                                  // 0 for a thread holding no key
+  uint32_t top = holds ? hi : 0xffffffffu;
+  const uint32_t holders = (uint32_t)__popcll(__ballot(holds));
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
   top = wave_min_u32(top);
@@ -245,21 +249,23 @@ __device__ __forceinline__ void select_row(TopkShared &sh, const float *__restri
     sh.wave_a[wave] = lo;
     sh.wave_b[wave] = hi;
     sh.wave_c[wave] = top;
+    sh.wave_d[wave] = holders;
   }
 #pragma unroll
   for (int e = 0; e < kBinsPerLane; ++e) sh.hist[kBinsPerLane * tid + e] = 0;
   if (tid == 0) sh.cand_count = 0;
   __syncthreads();
   range_over_waves(sh.wave_a, sh.wave_b, sh.wave_c, lo, hi, top);
+  const uint32_t n_holders = sum_of_earlier_waves(sh.wave_d, kTopkWaves);
 
   uint32_t thresh, krem = (uint32_t)kk;
   if (lo == hi) {                                     // every key equal: the lowest kk pages
     for (int i = tid; i < kk; i += kTopkThreads) emit(a + i, a + i);
     return;
   }
-  // With top > 0 every thread holds a key >= top, so at least kTopkThreads
-  // keys reach it, and for kk <= kTopkThreads so does the threshold key.
-  const uint32_t floor_key = kk <= kTopkThreads ? max(lo, top) : lo;
+  // Each of the n_holders threads holding keys holds one >= top, so for
+  // kk <= n_holders the threshold key is >= top too.
+  const uint32_t floor_key = (uint32_t)kk <= n_holders ? max(lo, top) : lo;
   // 2. refine the threshold key, 11 bits at a time.  floor_key == hi: at
   // least kk keys equal hi, which is then the threshold key.
   int lowbit = floor_key == hi ? 0 : 32 - __builtin_clz(floor_key ^ hi);   // bits >= lowbit known

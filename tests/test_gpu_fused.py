@@ -250,20 +250,21 @@ def range_floor_rows(n_max, gen):
     return [low, top, one, torch.randn(n_max, generator=gen)]
 
 
-@pytest.mark.parametrize("n_max,fused", [(8008, True), (10000, False)])
-def test_selection_range_floor(n_max, fused, gpu_lib):
-    """Rows of at least 1024 pages keeping at most 1024 (every selection
-    thread then holds a key, and the threshold's range starts at the least
-    of the threads' largest keys, which leaves low outliers out of the first
-    histogram), at k = 1, 64, 256, 1000, 1024 and 1025 (one past that bound,
-    where the range starts at the least key again), with the row filling the
-    table stride or ending in the last wave's span: the top-k kernel's
-    selection, and the fused kernel's where the shape allows it, equal the
-    oracle's; the fused outputs equal the two-call path's within one bf16
-    step."""
+@pytest.mark.parametrize("n_max,ns,ks,fused", [
+    (8008, (8008, 7800), (1, 64, 256, 1000, 1024, 1025), True),
+    (10000, (10000, 7800), (1, 64, 256, 1000, 1024, 1025), False),
+    (2049, (2049, 1500), (1, 64, 128, 500, 704, 705), True)])
+def test_selection_range_floor(n_max, ns, ks, fused, gpu_lib):
+    """The threshold's range starts at the least of the largest keys of the
+    selection threads that hold keys, when k is at most their number (which
+    leaves low outliers out of the first histogram), else at the least key.
+    Rows that fill the table stride or end inside a wave's span (at stride
+    2049, 704 threads hold pages of a full row and 512 of a 1500-page one; at
+    8008 and 10000 all 1024), k on both sides of the holders' count: the
+    top-k kernel's selection, and the fused kernel's where the shape allows
+    it, equal the oracle's; the fused outputs equal the two-call path's within
+    one bf16 step."""
     P, D, Hkv, G = 16, 128, 4, 8
-    ks = (1, 64, 256, 1000, 1024, 1025)
-    ns = (n_max, 7800)
     gen = torch.Generator().manual_seed(9100 + n_max)
     B = len(ks) * len(ns)
     rows = [r for _ in range(B) for r in range_floor_rows(n_max, gen)]
