@@ -494,3 +494,83 @@ def test_live_splits_ignore_stale_partials(gpu_lib):
             check_out(out[r], want, torch.bfloat16, f"live splits budget {budget} r{r}")
         outs.append(out)
     log(f"live splits: plan {plan}")
+
+
+@pytest.mark.parametrize("P,D", [(8, 128), (16, 128), (32, 64), (64, 128)])
+def test_append_ties_and_signed_zeros(P, D, gpu_lib):
+    """Keys drawn from {-0, +0, -1, +1}: every channel of a page is full of
+    ties, both zeros among them.  Stored four ways (one bulk append, chunks
+    of 5 tokens that start and end inside pages, one token per call, and the
+    scalar path from a source one element off 16-byte alignment), the
+    metadata equals the oracle's from-scratch bounds bit for bit, the sign
+    of zero included (a scan in position order with strict comparisons keeps
+    the first-seen of equal values), and the pools equal the oracle's store."""
+    Hq, Hkv, B = 8, 2, 3
+    lens = [3 * P + 5, 2 * P, 7]
+    gen = torch.Generator().manual_seed(4400 + P + D)
+    n_pages = [-(-n // P) for n in lens]
+    max_pages = max(n_pages) + 1
+    pool = sum(n_pages) + 3
+    ids = torch.randperm(pool, generator=gen).to(torch.int32)
+    pt = torch.zeros((B, max_pages), dtype=torch.int32)
+    o = 0
+    for r in range(B):
+        pt[r, :n_pages[r]] = ids[o:o + n_pages[r]]
+        o += n_pages[r]
+    N = sum(lens)
+    vals = torch.tensor([-0.0, 0.0, -1.0, 1.0])
+    k_new = vals[torch.randint(0, 4, (N, Hkv, D), generator=gen)].to(torch.bfloat16)
+    v_new = torch.randn((N, Hkv, D), generator=gen).to(torch.bfloat16)
+    cuh = [0] + np.cumsum(lens).tolist()
+    L = quest.make_layout(Hq, Hkv, D, P, torch.bfloat16, pool, max_pages)
+    shape = oracle.Shape(Hq, Hkv, D, P, pool, oracle.BF16)
+    kh = np.zeros((pool, Hkv, P, D), np.uint16)
+    vh = np.zeros((pool, Hkv, D, P), np.uint16)
+    pt_h = pt.numpy()
+    for r in range(B):
+        oracle.store_tokens(shape, np.ascontiguousarray(to_oracle(k_new[cuh[r]:cuh[r + 1]])),
+                            np.ascontiguousarray(to_oracle(v_new[cuh[r]:cuh[r + 1]])), 0,
+                            pt_h[r], kh, vh)
+    want = [oracle.request_bounds(shape, kh, pt_h[r], lens[r]) for r in range(B)]
+    assert any(np.any((w == 0) & np.signbit(w)) for w in want)    # -0 kept somewhere
+    assert any(np.any((w == 0) & ~np.signbit(w)) for w in want)   # and +0
+    pt_d, kn, vn = pt.to(DEV), k_new.to(DEV), v_new.to(DEV)
+
+    def fresh():
+        return (torch.zeros((pool, Hkv, P, D), dtype=torch.bfloat16, device=DEV),
+                torch.zeros((pool, Hkv, D, P), dtype=torch.bfloat16, device=DEV),
+                torch.full((pool, Hkv, 2, D), 5.0, dtype=torch.bfloat16, device=DEV))
+
+    def in_chunks(step, src_k=kn, src_v=vn):
+        k_c, v_c, km = fresh()
+        for t0 in range(0, max(lens), step):
+            counts = [max(0, min(step, n - t0)) for n in lens]
+            rows = [cuh[r] + t0 + i for r in range(B) for i in range(counts[r])]
+            sub_cu = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int32, device=DEV)
+            ctx0 = torch.tensor([min(t0, n) for n in lens], dtype=torch.int32, device=DEV)
+            idx = torch.tensor(rows, dtype=torch.int64, device=DEV)
+            quest.quest_append_kv(L, src_k[idx].contiguous(), src_v[idx].contiguous(), sub_cu,
+                                  ctx0, step, pt_d, k_c, v_c, km)
+        return k_c, v_c, km
+
+    ways = {"bulk": in_chunks(max(lens)), "chunks5": in_chunks(5), "tokens": in_chunks(1)}
+    k_buf = torch.empty(kn.numel() + 1, dtype=kn.dtype, device=DEV)
+    v_buf = torch.empty(vn.numel() + 1, dtype=vn.dtype, device=DEV)
+    k_off, v_off = k_buf[1:].view(kn.shape), v_buf[1:].view(vn.shape)
+    k_off.copy_(kn)
+    v_off.copy_(vn)
+    assert k_off.data_ptr() % 16 != 0
+    k_c, v_c, km = fresh()
+    quest.quest_append_kv(L, k_off, v_off, torch.tensor(cuh, dtype=torch.int32, device=DEV),
+                          torch.zeros(B, dtype=torch.int32, device=DEV), max(lens), pt_d, k_c,
+                          v_c, km)
+    ways["scalar"] = (k_c, v_c, km)
+    torch.cuda.synchronize()
+    for name, (k_c, v_c, km) in ways.items():
+        assert to_oracle(k_c).tobytes() == kh.tobytes(), name
+        assert to_oracle(v_c).tobytes() == vh.tobytes(), name
+        kmh = to_f64(km)
+        for r in range(B):
+            got = kmh[pt_h[r, :n_pages[r]]]
+            assert np.array_equal(got, want[r]), (name, r)
+            assert np.array_equal(np.signbit(got), np.signbit(want[r])), (name, r)
