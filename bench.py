@@ -19,7 +19,9 @@ W eager warm-up steps, one eager pass over the sequence and one untimed
 replay; a HIP event pair brackets the timed replay.  value = batch * K /
 replay time.  Also reported: the same steps launched eagerly one at a time,
 the cache evicted before each by an untimed 2 GiB read sweep (each step then
-pays its own dispatch latency); a per-kernel breakdown; the dominant kernel's
+pays its own dispatch latency); the same steps replayed on one copy without
+eviction (labelled cache-assisted); the bytes each step moves besides the
+headline ones, by item; a per-kernel breakdown; the dominant kernel's
 roofline (its average over 128 back-to-back launches cycling through 8
 copies of the metadata, and the committed counter record of its HBM
 traffic); the dense decode over every page, the
@@ -28,7 +30,8 @@ prefill-chunk append, each timed like the eager steps; the 48-layer batch-64
 step; one step each of the other single-layer workloads (the tiny fp32
 request, the 32k-context layer, the ragged batch), each on a cache of its
 own and timed like the eager steps; and the CPU oracle on a bounded sample
-of the same workload.
+of the same workload (all host threads and one), its from-scratch metadata
+build, and one layer-step of the 48-layer workload.
 
 Prints one JSON line.
 """
