@@ -136,6 +136,30 @@ def pin_bounds_contain_and_attain(dtype):
             assert np.array_equal(oracle.page_bounds(s, k_pool, pt, ctx, j), b[j])
 
 
+def pin_bounds_keep_first_seen(dtype):
+    """Among equal key values the bound keeps the one met first in position
+    order (strict comparisons), which only shows in the sign of a zero: on
+    one page, a channel whose keys are +0, -0, +0, -0 has bounds (+0, +0),
+    one whose keys are -0, +0, -0, +0 has (-0, -0), and one with +0, -0, 1,
+    -1 has min -1 and max 1."""
+    P, D, Hkv = 4, 8, 1
+    s = shape_of(Hkv, Hkv, D, P, 2, dtype)
+    pt = np.array([1], dtype=np.int32)
+    k = torch.ones((P, Hkv, D))
+    k[:, 0, 0] = torch.tensor([0.0, -0.0, 0.0, -0.0])
+    k[:, 0, 1] = torch.tensor([-0.0, 0.0, -0.0, 0.0])
+    k[:, 0, 2] = torch.tensor([0.0, -0.0, 1.0, -1.0])
+    k_tok = to_oracle(k.to(dtype))
+    v_tok = to_oracle(torch.zeros((P, Hkv, D)).to(dtype))
+    k_pool, v_pool = pool_arrays(s, 7.0)
+    store_request(s, k_tok, v_tok, pt, k_pool, v_pool)
+    b = oracle.request_bounds(s, k_pool, pt, P)[0, 0]           # [2][D]
+    assert b[0, 0] == 0 and not np.signbit(b[0, 0]) and b[1, 0] == 0 and not np.signbit(b[1, 0])
+    assert b[0, 1] == 0 and np.signbit(b[0, 1]) and b[1, 1] == 0 and np.signbit(b[1, 1])
+    assert b[0, 2] == -1.0 and b[1, 2] == 1.0
+    assert np.all(b[:, 3:] == 1.0)
+
+
 # --------------------------------------------------------------------------
 # page scores
 # --------------------------------------------------------------------------
@@ -407,7 +431,8 @@ def pin_budget_covering_all_is_dense(dtype):
 
 PINS = [
     pin_hand_example, pin_store_layout, pin_store_incremental_equals_bulk,
-    pin_bounds_contain_and_attain, pin_score_is_box_maximum, pin_score_bounds_every_key,
+    pin_bounds_contain_and_attain, pin_bounds_keep_first_seen, pin_score_is_box_maximum,
+    pin_score_bounds_every_key,
     pin_score_closed_forms, pin_group_reduce, pin_per_head_selection, pin_budget_table,
     pin_select_bruteforce, pin_select_forced,
     pin_dense_equals_sdpa, pin_sparse_equals_masked_sdpa, pin_attention_closed_forms,
@@ -445,6 +470,7 @@ MUTANTS = {
         "qsort(sel, (size_t)k, sizeof(int32_t), ascending_int);", ""),
     "bounds read stale slots": ("const int32_t last = (first + P < ctx ? first + P : ctx);",
                                 "const int32_t last = first + P;"),
+    "bounds keep the last-seen of equal values": ("if (x < lo) lo = x;", "if (x <= lo) lo = x;"),
     "min and max swapped": ("bounds_j[((int64_t)g * 2 + 0) * D + d] = lo;",
                             "bounds_j[((int64_t)g * 2 + 0) * D + d] = hi; (void)lo;"),
     "budget rounds up": ("int32_t k = budget_tokens / page_size;",
