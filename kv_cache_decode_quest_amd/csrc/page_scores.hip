@@ -213,19 +213,41 @@ constexpr int kMaxGroup = 16;       // q heads per KV head the layout allows
 // q * min), the larger of the two exact products, so the choice itself
 // rounds nothing; the compiler fuses it into the fp32 add (one rounding per
 // term).  Every head sums over d in order.
-// With cu_new non-null the request length is ctx_before + its new tokens
-// (the fused path, after a separate append launch), else ctx_lens.
+// With cu_new non-null (the fused on_kv_stored + scores path) the request
+// length is ctx_before + its new tokens, and the work-group whose pages hold
+// new tokens first stores them for its KV head and refreshes those pages'
+// min/max (the per-channel body of the standalone append, so the metadata is
+// the same bit for bit); the barrier after the q load makes the rows visible
+// to the threads that score them.  Else the length is ctx_lens.
 template <int kG>
 __global__ __launch_bounds__(256) void page_scores_valu_kernel(
     int Hkv, int G, int per_head, int D, int64_t pool, int P, int max_pages, int reduce,
-    const float *__restrict__ q, const float *__restrict__ kmeta,
+    const float *__restrict__ q, float *kmeta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ ctx_lens,
     const int32_t *__restrict__ cu_new, const int32_t *__restrict__ ctx_before,
-    float *__restrict__ scores) {
+    const float *__restrict__ k_new, const float *__restrict__ v_new, float *k_cache,
+    float *v_cache, float *__restrict__ scores) {
   extern __shared__ __align__(16) float q_lds[];     // [kG][D]
   const int g = blockIdx.y, r = blockIdx.z;
   const float *qg = q + ((int64_t)r * Hkv * G + (int64_t)g * G) * D;
   for (int i = threadIdx.x; i < kG * D; i += blockDim.x) q_lds[i] = i < G * D ? qg[i] : 0.f;
+  if (cu_new != nullptr && k_new != nullptr) {
+    const int row0 = cu_new[r], n_new = cu_new[r + 1] - row0, p0 = ctx_before[r];
+    if (n_new > 0 && p0 >= 0) {
+      const int p1 = p0 + n_new;
+      const int base = blockIdx.x * blockDim.x;
+      const int a0 = max(p0 / P, base);
+      const int a1 = min((p1 - 1) / P, base + (int)blockDim.x - 1);
+      const int32_t *ptr = page_table + (int64_t)r * max_pages;
+      for (int pg = a0; pg <= a1 && pg < max_pages; ++pg) {
+        const int64_t phys = ptr[pg];
+        if (phys < 0 || phys >= pool) continue;
+        const AppendSpan a = append_span(phys, Hkv, g, P, pg, p0, p1, row0);
+        for (int d = threadIdx.x; d < D; d += blockDim.x)
+          append_channel<float>(a, d, Hkv, D, P, k_new, v_new, k_cache, v_cache, kmeta);
+      }
+    }
+  }
   __syncthreads();
   const int ctx = cu_new ? ctx_before[r] + max(cu_new[r + 1] - cu_new[r], 0) : ctx_lens[r];
   const int n = pages_in(ctx, P, max_pages);
@@ -320,8 +342,12 @@ static hipError_t launch_scores(const Dims &dm, int batch, const void *q, void *
   hipLaunchKernelGGL(page_scores_valu_kernel<KG>, grid, dim3(256),                          \
                      (size_t)(KG) * dm.D * sizeof(float), stream, dm.Hkv, dm.G,             \
                      (int)dm.per_head(), dm.D, dm.pool, dm.P, dm.max_pages, reduce,         \
-                     (const float *)q, (const float *)kmeta, page_table, ctx_lens,          \
-                     fused ? fa.cu_new : nullptr, fused ? fa.ctx_before : nullptr, scores)
+                     (const float *)q, (float *)kmeta, page_table, ctx_lens,                \
+                     fused ? fa.cu_new : nullptr, fused ? fa.ctx_before : nullptr,           \
+                     fused ? (const float *)fa.k_new : nullptr,                             \
+                     fused ? (const float *)fa.v_new : nullptr,                             \
+                     fused ? (float *)fa.k_cache : nullptr,                                 \
+                     fused ? (float *)fa.v_cache : nullptr, scores)
     if (dm.G <= 1) QUEST_SCORES32(1);
     else if (dm.G <= 2) QUEST_SCORES32(2);
     else if (dm.G <= 4) QUEST_SCORES32(4);
@@ -346,15 +372,9 @@ hipError_t launch_append_scores(const Dims &dm, int batch, const void *q, const 
                                 const int32_t *ctx_before, int max_new,
                                 const int32_t *page_table, void *k_cache, void *v_cache,
                                 void *kmeta, int reduce, float *scores, hipStream_t stream) {
+  (void)max_new;                    // each work-group finds its own touched pages
   const FusedAppend fa{(const uint16_t *)k_new, (const uint16_t *)v_new, cu_new, ctx_before,
                        (uint16_t *)k_cache, (uint16_t *)v_cache};
-  if (dm.dtype != 1) {
-    // fp32: the append runs as its own launch, then the scores read the
-    // request lengths from cu_new / ctx_before
-    const hipError_t e = launch_append(dm, batch, k_new, v_new, cu_new, ctx_before, max_new,
-                                       page_table, k_cache, v_cache, kmeta, stream);
-    if (e != hipSuccess) return e;
-  }
   return launch_scores(dm, batch, q, kmeta, page_table, nullptr, reduce, fa, true, scores,
                        stream);
 }
