@@ -574,3 +574,81 @@ def test_append_ties_and_signed_zeros(P, D, gpu_lib):
             got = kmh[pt_h[r, :n_pages[r]]]
             assert np.array_equal(got, want[r]), (name, r)
             assert np.array_equal(np.signbit(got), np.signbit(want[r])), (name, r)
+
+
+@pytest.mark.parametrize("dtype,D,P", [(torch.bfloat16, 128, 16), (torch.bfloat16, 64, 32),
+                                       (torch.float32, 64, 16)])
+def test_append_score_several_tokens(dtype, D, P, gpu_lib):
+    """quest_append_score storing several new tokens per request in one call
+    (0, 1, 5, 17 and 40; first positions inside pages, at a page start, and
+    just before the first page of the next scoring work-group's range: 1024
+    tokens at page 16 for the matrix-core kernel's 64-page groups, 4096 for
+    the fp32 kernel's 256-page groups): pools equal the oracle's store byte
+    for byte, every live page's metadata equals the oracle's from-scratch
+    bounds, and the scores meet the oracle's within the fp32 summation
+    bound."""
+    Hq, Hkv = 8, 2
+    G = Hq // Hkv
+    span = (64 if dtype == torch.bfloat16 else 256) * P     # tokens per scoring work-group
+    before = [span - 3, 7, P, span - 10, 2 * P + 1, 0]
+    new = [5, 17, 40, 40, 0, 1]
+    B = len(before)
+    gen = torch.Generator().manual_seed(4500 + D + P)
+    n_pages = [-(-(b + n) // P) for b, n in zip(before, new)]
+    max_pages = max(n_pages) + 2
+    pool = sum(n_pages) + 5
+    ids = torch.randperm(pool, generator=gen).to(torch.int32)
+    pt = torch.zeros((B, max_pages), dtype=torch.int32)
+    o = 0
+    for r in range(B):
+        pt[r, :n_pages[r]] = ids[o:o + n_pages[r]]
+        o += n_pages[r]
+    elem = oracle.BF16 if dtype == torch.bfloat16 else oracle.F32
+    shape = oracle.Shape(Hq, Hkv, D, P, pool, elem)
+    L = quest.make_layout(Hq, Hkv, D, P, dtype, pool, max_pages)
+    pt_h = pt.numpy()
+    # prompts (bulk append) and the new tokens (one quest_append_score call)
+    k0 = torch.randn((sum(before), Hkv, D), generator=gen).to(dtype)
+    v0 = torch.randn((sum(before), Hkv, D), generator=gen).to(dtype)
+    k1 = torch.randn((sum(new), Hkv, D), generator=gen).to(dtype)
+    v1 = torch.randn((sum(new), Hkv, D), generator=gen).to(dtype)
+    q = torch.randn((B, Hq, D), generator=gen).to(dtype)
+    cu0 = [0] + np.cumsum(before).tolist()
+    cu1 = [0] + np.cumsum(new).tolist()
+    kh = np.zeros((pool, Hkv, P, D), shape.storage_dtype())
+    vh = np.zeros((pool, Hkv, D, P), shape.storage_dtype())
+    for r in range(B):
+        if before[r]:
+            oracle.store_tokens(shape, np.ascontiguousarray(to_oracle(k0[cu0[r]:cu0[r + 1]])),
+                                np.ascontiguousarray(to_oracle(v0[cu0[r]:cu0[r + 1]])), 0,
+                                pt_h[r], kh, vh)
+        if new[r]:
+            oracle.store_tokens(shape, np.ascontiguousarray(to_oracle(k1[cu1[r]:cu1[r + 1]])),
+                                np.ascontiguousarray(to_oracle(v1[cu1[r]:cu1[r + 1]])),
+                                before[r], pt_h[r], kh, vh)
+    k_c = torch.zeros((pool, Hkv, P, D), dtype=dtype, device=DEV)
+    v_c = torch.zeros((pool, Hkv, D, P), dtype=dtype, device=DEV)
+    km = torch.full((pool, Hkv, 2, D), 3.0, dtype=dtype, device=DEV)
+    pt_d = pt.to(DEV)
+    zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
+    quest.quest_append_kv(L, k0.to(DEV), v0.to(DEV), torch.tensor(cu0, dtype=torch.int32,
+                          device=DEV), zeros, max(before), pt_d, k_c, v_c, km)
+    scores = torch.full((B, Hkv, max_pages), 7.0, dtype=torch.float32, device=DEV)
+    quest.quest_append_score(L, q.to(DEV), k1.to(DEV), v1.to(DEV),
+                             torch.tensor(cu1, dtype=torch.int32, device=DEV),
+                             torch.tensor(before, dtype=torch.int32, device=DEV), max(new), pt_d,
+                             k_c, v_c, km, scores)
+    torch.cuda.synchronize()
+    assert to_oracle(k_c).tobytes() == kh.tobytes()
+    assert to_oracle(v_c).tobytes() == vh.tobytes()
+    kmh, sc = to_f64(km), scores.cpu().numpy().astype(np.float64)
+    qh = to_oracle(q)
+    for r in range(B):
+        ctx = before[r] + new[r]
+        if ctx == 0:
+            continue
+        bounds = oracle.request_bounds(shape, kh, pt_h[r], ctx)
+        got = kmh[pt_h[r, :n_pages[r]]]
+        assert np.array_equal(got, bounds), r
+        ref = oracle.request_scores(shape, np.ascontiguousarray(qh[r]), bounds)
+        check_scores(sc[r], ref, to_f64(q[r]), bounds, G)
