@@ -188,10 +188,10 @@ int quest_page_scores(const quest_layout *layout, int32_t batch,
  * max_new_per_seq, page_table, k_cache, v_cache, kmeta) then
  * quest_page_scores(layout, batch, q, kmeta, page_table, ctx_lens,
  * group_reduce, scores) with ctx_lens[r] = ctx_before[r] + (cu_new[r+1] -
- * cu_new[r]).  On bf16 it is one kernel: the scoring work-group that owns a
- * touched page stores the new tokens and refreshes the page's min/max first,
- * so the metadata is read once.  Arguments and layouts as in those two
- * calls. */
+ * cu_new[r]).  It is one kernel (bf16 and fp32): the scoring work-group that
+ * owns a touched page stores the new tokens and refreshes the page's min/max
+ * first, so the metadata is read once; max_new_per_seq is validated but the
+ * grid does not depend on it.  Arguments and layouts as in those two calls. */
 int quest_append_score(const quest_layout *layout, int32_t batch, const void *q,
                        const void *k_new, const void *v_new, const int32_t *cu_new,
                        const int32_t *ctx_before, int32_t max_new_per_seq,
